@@ -1,0 +1,45 @@
+"""Plain fp64 CPU oracle for the TurboQuant KV-cache hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant generator with the HIP library; both sides receive the same seeded
+inputs (including the Gaussian draws the method needs) from
+``kv_cache_vector_quantize_amd.inputs``, which holds none of the method's
+arithmetic.
+
+Sources (the pages describe TurboQuant, Zandieh et al., "Online Vector
+Quantization with Near-optimal Distortion Rate"):
+
+* qiita.com/okssusucha/items/81738e4261f2841d40f8 ("P1") -- sections
+  "Rotate, then quantize" and "One more stage so attention doesn't break".
+* a2a-mcp.org/blog/what-is-turboquant-ja ("P3") -- "How it works",
+  Stage 1 (random rotation, Beta((d-1)/2,(d-1)/2) law, Lloyd-Max) and
+  Stage 2 (1-bit QJL on the residual); "How to implement", item 1
+  (precomputed codebook, pre-rotated query, dots straight from indices).
+
+Every function is written in the order the pages give the steps; the
+readings taken where the pages are silent are listed in each docstring.
+All arithmetic is float64, single threaded, no blocking or fusion.
+
+Pinned by ``tests/test_oracle_*.py`` (closed forms, textbook special cases,
+invariants, brute force).  No function here is "parity unpinned".
+"""
+
+from .codebook import (beta_density, bin_mass, bin_first_moment, lloyd_max,
+                       codebook_mse)
+from .rotation import rotation_from_gaussian
+from .quantize import quantize_keys, quantize_values, residual_and_sketch
+from .packing import (pack_key_codes, unpack_key_codes, pack_signs, unpack_signs,
+                      pack_value_codes, unpack_value_codes, round_norms)
+from .attention import (query_prep, key_logits, key_logits_from_records,
+                        decode, decode_from_records, qjl_scale)
+
+__all__ = [
+    "beta_density", "bin_mass", "bin_first_moment", "lloyd_max", "codebook_mse",
+    "rotation_from_gaussian", "quantize_keys", "quantize_values",
+    "residual_and_sketch", "pack_key_codes", "unpack_key_codes", "pack_signs",
+    "unpack_signs", "pack_value_codes", "unpack_value_codes", "round_norms",
+    "query_prep", "key_logits", "key_logits_from_records", "decode",
+    "decode_from_records", "qjl_scale",
+]

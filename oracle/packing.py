@@ -1,0 +1,103 @@
+"""Canonical packed layout of quantized key and value streams.
+
+Test infrastructure (see ``oracle/__init__``).
+
+The pages only say the indices are stored compactly and that attention is
+computed straight from them (P3 "How it works", closing paragraph; "How to
+implement", item 1, which mentions uint8 indices).  The bit layout is this
+implementation's choice, fixed here so that GPU parity is byte-for-byte.
+All words are little-endian uint32; bit k of a word is (word >> k) & 1.
+
+Key stream (one record per token, coordinates along the word):
+  codes[s, t, w, p]  bit k = bit p of idx[s, t, 32*w + k]     shape [S, T, d/32, b]
+  signs[s, t, w]     bit k = sign bit of z[s, t, 32*w + k]    shape [S, T, m/32]
+Value stream (blocks of 32 tokens, tokens along the word):
+  codes[s, B, j, p]  bit k = bit p of idx[s, 32*B + k, j]     shape [S, ceil(T/32), d, b]
+  bits of tokens past T in the last block are 0.
+Norms are one value per token, [S, T], stored as float32 or as float16
+(round to nearest even).
+"""
+
+import numpy as np
+
+
+def pack_key_codes(idx, bits):
+    idx = np.asarray(idx, dtype=np.int64)
+    *lead, d = idx.shape
+    if d % 32:
+        raise ValueError("d must be a multiple of 32")
+    words = np.zeros((*lead, d // 32, bits), dtype=np.uint64)
+    for j in range(d):
+        w, k = divmod(j, 32)
+        for p in range(bits):
+            words[..., w, p] |= ((idx[..., j] >> p) & 1).astype(np.uint64) << np.uint64(k)
+    return words.astype(np.uint32)
+
+
+def unpack_key_codes(words, d):
+    words = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    *lead, nw, bits = words.shape
+    idx = np.zeros((*lead, d), dtype=np.int64)
+    for j in range(d):
+        w, k = divmod(j, 32)
+        for p in range(bits):
+            idx[..., j] |= ((words[..., w, p] >> k) & 1) << p
+    return idx
+
+
+def pack_signs(signs):
+    signs = np.asarray(signs, dtype=bool)
+    *lead, m = signs.shape
+    if m % 32:
+        raise ValueError("m must be a multiple of 32")
+    words = np.zeros((*lead, m // 32), dtype=np.uint64)
+    for i in range(m):
+        w, k = divmod(i, 32)
+        words[..., w] |= signs[..., i].astype(np.uint64) << np.uint64(k)
+    return words.astype(np.uint32)
+
+
+def unpack_signs(words, m):
+    words = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    *lead, nw = words.shape
+    out = np.zeros((*lead, m), dtype=bool)
+    for i in range(m):
+        w, k = divmod(i, 32)
+        out[..., i] = ((words[..., w] >> k) & 1) == 1
+    return out
+
+
+def pack_value_codes(idx, bits):
+    """idx: [S, T, d] -> words [S, ceil(T/32), d, bits]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    S, T, d = idx.shape
+    nb = (T + 31) // 32
+    words = np.zeros((S, nb, d, bits), dtype=np.uint64)
+    for t in range(T):
+        blk, k = divmod(t, 32)
+        for p in range(bits):
+            words[:, blk, :, p] |= ((idx[:, t, :] >> p) & 1).astype(np.uint64) << np.uint64(k)
+    return words.astype(np.uint32)
+
+
+def unpack_value_codes(words, T):
+    words = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    S, nb, d, bits = words.shape
+    idx = np.zeros((S, T, d), dtype=np.int64)
+    for t in range(T):
+        blk, k = divmod(t, 32)
+        for p in range(bits):
+            idx[:, t, :] |= ((words[:, blk, :, p] >> k) & 1) << p
+    return idx
+
+
+def round_norms(x, dtype):
+    """Round fp64 norms to the storage type ('f32' or 'f16', nearest even).
+
+    Returns the stored array (numpy float32 / float16)."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    raise ValueError(dtype)
