@@ -1,0 +1,197 @@
+/*
+ * tq.h -- C ABI of libtq.so: TurboQuant KV-cache vector quantization and
+ * decode attention from the packed codes, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Zandieh et al., "TurboQuant: Online Vector Quantization with
+ * Near-optimal Distortion Rate") as the source pages describe it:
+ *   - a data-independent random orthogonal rotation, the Q factor of a
+ *     Gaussian matrix, drawn once and cached
+ *     (a2a-mcp.org/blog/what-is-turboquant-ja, "How it works", Stage 1;
+ *      deepsignal-app.com article, QJL section);
+ *   - after rotation each coordinate of the normalised vector follows
+ *     Beta((d-1)/2,(d-1)/2) on [-1,1], so an MSE-optimal Lloyd-Max scalar
+ *     codebook can be precomputed per (head dim, bit width)
+ *     (same page, Stage 1; "How to implement", item 1;
+ *      qiita.com/okssusucha/items/81738e4261f2841d40f8, "Rotate, then quantize");
+ *   - for keys, a 1-bit quantized JL transform (random projection + sign) of
+ *     the residual left by the MSE stage makes inner products unbiased
+ *     (Stage 2; qiita page, "One more stage so attention doesn't break");
+ *   - attention logits are computed straight from the stored indices with a
+ *     query rotated once, with no pass that dequantizes the cache
+ *     (Stage 2 closing paragraph; "How to implement", item 1).
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers unless stated otherwise.  The
+ *     caller allocates and owns every buffer; the library never allocates or
+ *     frees device memory and keeps no pointer after the call returns.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
+ *     call never synchronizes.  Buffers must stay valid until the stream has
+ *     executed the work.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     bad argument returns TQ_EINVAL (nothing launched); a shape or width the
+ *     kernels were not built for returns TQ_EUNSUPPORTED; a workspace smaller
+ *     than the matching *_workspace() size returns TQ_EWORKSPACE; a failed
+ *     launch returns TQ_EHIP.  Errors raised by earlier, unrelated work on the
+ *     stream are not reported here.
+ *   - Device pointers must be 16-byte aligned.  Layouts are dense, row-major,
+ *     little-endian.  No global mutable state: calls are thread-safe.
+ *
+ * Packed layout (bit k of a uint32 word is (word >> k) & 1):
+ *   key stream   codes[s][t][d/32][bits]  bit k of word (w,p) = bit p of idx[s][t][32w+k]
+ *                signs[s][t][m/32]        bit k of word w     = [z[s][t][32w+k] >= 0]
+ *                norm[s][t]  = ||k||,  rnorm[s][t] = ||k|| * ||r||
+ *   value stream codes[s][ceil(T/32)][d][bits]
+ *                bit k of word (B,j,p) = bit p of idx[s][32B+k][j]; bits of
+ *                tokens past T are 0.        norm[s][t] = ||v||
+ *   idx = number of codebook boundaries <= the rotated, normalised coordinate.
+ *   z = S r, r = Pi x/||x|| - centroid[idx] (rotated domain, unit scale).
+ *   Norms are float32 or float16 (round to nearest even), per tq_packed.
+ *   A zero vector stores norms 0, idx 2^(bits-1) everywhere and sign bits 1.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,        /* bad argument; nothing launched */
+  TQ_EUNSUPPORTED = -2,  /* valid, but not a shape/width the kernels support */
+  TQ_EWORKSPACE = -3,    /* workspace smaller than required */
+  TQ_EHIP = -4           /* HIP launch / runtime error */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+typedef enum { TQ_KEY = 0, TQ_VALUE = 1 } tq_role;
+
+/* Data-independent tables of one stream (device memory, caller-owned). */
+typedef struct {
+  int32_t d;               /* head dimension; the hot-path kernels support 128   */
+  int32_t m;               /* sketch rows: 128 for keys, 0 for values             */
+  int32_t bits;            /* code width, 1..4                                    */
+  int32_t reserved;        /* must be 0                                           */
+  const float *rot;        /* Pi, d x d row-major; y = Pi x                       */
+  const float *sketch;     /* S, m x d row-major, iid N(0,1); NULL when m == 0    */
+  const float *centroids;  /* 2^bits ascending, unit-sphere scale                 */
+  const float *bounds;     /* 2^bits - 1 ascending decision boundaries            */
+} tq_tables;
+
+/* A packed key or value stream of nseq sequences of T tokens (caller-owned). */
+typedef struct {
+  int32_t role;            /* tq_role                                             */
+  int32_t bits;            /* must equal the tables' bits                         */
+  int32_t d;               /* must equal the tables' d                            */
+  int32_t m;               /* keys: the tables' m (> 0); values: 0                */
+  int64_t nseq;            /* sequences (batch x kv heads), >= 0                  */
+  int64_t T;               /* tokens per sequence, >= 0                           */
+  uint32_t *codes;         /* layout above                                        */
+  uint32_t *signs;         /* keys only, else NULL                                */
+  void *norm;              /* [nseq][T] of norm_dtype                             */
+  void *rnorm;             /* keys only, [nseq][T] of norm_dtype, else NULL       */
+  int32_t norm_dtype;      /* TQ_F32 or TQ_F16                                    */
+  int32_t reserved;        /* must be 0                                           */
+} tq_packed;
+
+/* Version of this ABI (TQ_ABI_VERSION of the built library). */
+int tq_abi_version(void);
+
+/* Static string for a status code; never NULL. */
+const char *tq_status_str(int status);
+
+/*
+ * tq_codebook -- Lloyd-Max codebook for Beta((d-1)/2,(d-1)/2) on [-1,1].
+ * Cites: a2a-mcp.org page, "How it works", Stage 1 (the Beta law, optimal
+ * centroids precomputed); "How to implement", item 1 (codebook per head dim
+ * and width); qiita page, "Rotate, then quantize" (Lloyd-Max per coordinate).
+ * Iterates the two Lloyd conditions (boundary = midpoint of neighbouring
+ * centroids, centroid = conditional mean of its cell) in float64 until no
+ * centroid moves by 1e-15.  Setup: run once per (d, bits).
+ *   d            3..4096
+ *   bits         1..4
+ *   centroids64  out, 2^bits doubles, or NULL
+ *   bounds64     out, 2^bits - 1 doubles, or NULL
+ *   centroids32  out, 2^bits floats (round to nearest), required
+ *   bounds32     out, 2^bits - 1 floats, required
+ */
+tq_status tq_codebook(int d, int bits, double *centroids64, double *bounds64,
+                      float *centroids32, float *bounds32, hipStream_t stream);
+
+/*
+ * tq_rotation -- Pi = Q diag(sign(diag R)) for G = Q R (Householder QR in
+ * float64), the unique QR factor with a positive diagonal.
+ * Cites: a2a-mcp.org page, "How it works", Stage 1 (QR of a Gaussian matrix);
+ * deepsignal-app.com page, QJL section (drawn once before inference, cached).
+ * Setup helper; G is an input drawn by the caller (iid N(0,1)).
+ *   d      2..128
+ *   G      in, d x d row-major doubles
+ *   rot64  out, d x d row-major doubles (also used as working storage)
+ *   rot32  out, d x d row-major floats (round to nearest), or NULL
+ */
+tq_status tq_rotation(int d, const double *G, double *rot64, float *rot32, hipStream_t stream);
+
+/*
+ * tq_quantize -- online quantization of key or value vectors.
+ * Cites: a2a-mcp.org page, "How it works", Stage 1 (normalise, rotate,
+ * Lloyd-Max per coordinate) and Stage 2 (1-bit QJL of the residual, keys);
+ * "How to implement", item 1 (quantize on every cache update).
+ *   t      tables of the stream (t->m > 0 for keys, 0 for values)
+ *   x      in, [out->nseq][out->T][d] of x_dtype (TQ_F32 or TQ_BF16)
+ *   out    packed stream to write; role, bits, d, m must match t
+ */
+tq_status tq_quantize(const tq_tables *t, const void *x, int x_dtype, const tq_packed *out,
+                      hipStream_t stream);
+
+/* Workspace bytes for tq_attn_logits (the rotated queries). */
+size_t tq_logits_workspace(int B, int Hq, int d, int m);
+
+/*
+ * tq_attn_logits -- raw <q, k> estimates straight from packed keys:
+ *   l = ||k|| <Pi q, c[idx]> + sqrt(pi/2)/m * ||k|| ||r|| <S Pi q, 2s - 1>.
+ * Cites: a2a-mcp.org page, Stage 2 closing paragraph and "How to implement",
+ * item 1 (query rotated once, dots from indices, no dequantization pass);
+ * qiita page, "One more stage..." (unbiased inner product).
+ *   tk       key tables
+ *   q        in, [B][Hq][d] of q_dtype (TQ_F32 or TQ_BF16)
+ *   k        packed keys, nseq = B*Hkv, sequence index b*Hkv + g
+ *   logits   out, [B][Hq][T] float32; query head h reads kv head h/(Hq/Hkv)
+ *   ws       workspace of at least tq_logits_workspace(B, Hq, d, m) bytes
+ */
+tq_status tq_attn_logits(const tq_tables *tk, const void *q, int q_dtype, int B, int Hq, int Hkv,
+                         const tq_packed *k, float *logits, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Workspace bytes for tq_attn_decode (rotated queries + split partials). */
+size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m);
+
+/*
+ * tq_attn_decode -- one query token per (batch, query head) attends to all T
+ * cached tokens: softmax(scale * l) over the logits above, then the weighted
+ * sum of the values, accumulated in the rotated domain from the value codes
+ * and rotated back once (out = Pi^T sum_t a_t ||v_t|| c_V[idx_t]).
+ * Cites: a2a-mcp.org page, Stage 2 closing paragraph (no full dequantization
+ * during inference); "How to implement", item 1.
+ *   tk, tv   key / value tables (same d and rotation)
+ *   q        in, [B][Hq][d] of q_dtype
+ *   k, v     packed keys and values, nseq = B*Hkv, same T >= 1
+ *   scale    softmax scale, > 0 (1/sqrt(d) for standard attention)
+ *   out      out, [B][Hq][d] float32
+ *   ws       workspace of at least tq_decode_workspace(B, Hq, Hkv, T, d, m) bytes
+ */
+tq_status tq_attn_decode(const tq_tables *tk, const tq_tables *tv, const void *q, int q_dtype,
+                         int B, int Hq, int Hkv, const tq_packed *k, const tq_packed *v,
+                         float scale, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

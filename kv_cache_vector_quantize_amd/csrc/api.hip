@@ -1,0 +1,173 @@
+// extern "C" entry points of libtq.so: validate on the host, size the
+// workspaces, then hand over to the launchers.  See include/tq.h for the
+// contract of every call.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kSupportedD = 128;
+constexpr int kSupportedM = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
+
+tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+// Tables of a stream as the hot-path kernels need them.
+tq_status check_tables(const tq_tables* t, bool key) {
+  if (t == nullptr) return TQ_EINVAL;
+  if (t->reserved != 0 || t->bits < 1 || t->bits > 4 || t->d <= 0 || t->d % 32 != 0) return TQ_EINVAL;
+  if (t->m < 0 || t->m % 32 != 0) return TQ_EINVAL;
+  if (key ? t->m == 0 : t->m != 0) return TQ_EINVAL;
+  if (!ok_ptr(t->rot) || !ok_ptr(t->centroids) || !ok_ptr(t->bounds)) return TQ_EINVAL;
+  if (key ? !ok_ptr(t->sketch) : t->sketch != nullptr) return TQ_EINVAL;
+  if (t->d != kSupportedD) return TQ_EUNSUPPORTED;
+  if (key && t->m != kSupportedM) return TQ_EUNSUPPORTED;
+  return TQ_OK;
+}
+
+tq_status check_packed(const tq_packed* p, const tq_tables* t, int role) {
+  if (p == nullptr) return TQ_EINVAL;
+  if (p->role != role || p->reserved != 0) return TQ_EINVAL;
+  if (p->bits != t->bits || p->d != t->d || p->m != t->m) return TQ_EINVAL;
+  if (p->nseq < 0 || p->T < 0) return TQ_EINVAL;
+  if (p->norm_dtype != TQ_F32 && p->norm_dtype != TQ_F16) return TQ_EINVAL;
+  const bool empty = p->nseq == 0 || p->T == 0;
+  if (!empty && (!ok_ptr(p->codes) || !ok_ptr(p->norm))) return TQ_EINVAL;
+  if (empty && (!ok_opt(p->codes) || !ok_opt(p->norm))) return TQ_EINVAL;
+  if (role == TQ_KEY) {
+    if (!empty && (!ok_ptr(p->signs) || !ok_ptr(p->rnorm))) return TQ_EINVAL;
+    if (empty && (!ok_opt(p->signs) || !ok_opt(p->rnorm))) return TQ_EINVAL;
+  } else if (p->signs != nullptr || p->rnorm != nullptr) {
+    return TQ_EINVAL;
+  }
+  return TQ_OK;
+}
+
+tq_status check_heads(int B, int Hq, int Hkv, int max_group) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return TQ_EINVAL;
+  const int G = Hq / Hkv;
+  if (G > max_group || (G & (G - 1)) != 0) return TQ_EUNSUPPORTED;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+const char* tq_status_str(int status) {
+  switch (status) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_EINVAL: return "TQ_EINVAL: invalid argument";
+    case TQ_EUNSUPPORTED: return "TQ_EUNSUPPORTED: shape or width not supported by the kernels";
+    case TQ_EWORKSPACE: return "TQ_EWORKSPACE: workspace too small";
+    case TQ_EHIP: return "TQ_EHIP: HIP launch or runtime error";
+    default: return "unknown tq_status";
+  }
+}
+
+tq_status tq_codebook(int d, int bits, double* centroids64, double* bounds64, float* centroids32,
+                      float* bounds32, hipStream_t stream) {
+  if (d < 3 || d > 4096 || bits < 1 || bits > 4) return TQ_EINVAL;
+  if (!ok_ptr(centroids32) || !ok_ptr(bounds32) || !ok_opt(centroids64) || !ok_opt(bounds64))
+    return TQ_EINVAL;
+  return from_hip(tq::launch_codebook(d, bits, centroids64, bounds64, centroids32, bounds32, stream));
+}
+
+tq_status tq_rotation(int d, const double* G, double* rot64, float* rot32, hipStream_t stream) {
+  if (d < 2 || d > 128 || !ok_ptr(G) || !ok_ptr(rot64) || !ok_opt(rot32)) return TQ_EINVAL;
+  return from_hip(tq::launch_rotation(d, G, rot64, rot32, stream));
+}
+
+tq_status tq_quantize(const tq_tables* t, const void* x, int x_dtype, const tq_packed* out,
+                      hipStream_t stream) {
+  if (t == nullptr || out == nullptr) return TQ_EINVAL;
+  const bool key = out->role == TQ_KEY;
+  if (out->role != TQ_KEY && out->role != TQ_VALUE) return TQ_EINVAL;
+  tq_status st = check_tables(t, key);
+  if (st != TQ_OK) return st;
+  st = check_packed(out, t, out->role);
+  if (st != TQ_OK) return st;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
+  if (out->nseq == 0 || out->T == 0) return TQ_OK;
+  if (!ok_ptr(x)) return TQ_EINVAL;
+  return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, stream));
+}
+
+size_t tq_logits_workspace(int B, int Hq, int d, int m) {
+  if (B < 0 || Hq < 0 || d < 0 || m < 0) return 0;
+  const size_t nh = static_cast<size_t>(B) * Hq;
+  return align256(nh * d * sizeof(float)) + align256(nh * m * sizeof(float));
+}
+
+tq_status tq_attn_logits(const tq_tables* tk, const void* q, int q_dtype, int B, int Hq, int Hkv,
+                         const tq_packed* k, float* logits, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  tq_status st = check_tables(tk, true);
+  if (st != TQ_OK) return st;
+  st = check_packed(k, tk, TQ_KEY);
+  if (st != TQ_OK) return st;
+  st = check_heads(B, Hq, Hkv, 16);
+  if (st != TQ_OK) return st;
+  if (k->nseq != static_cast<int64_t>(B) * Hkv) return TQ_EINVAL;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
+  if (B == 0 || k->T == 0) return TQ_OK;
+  if (!ok_ptr(q) || !ok_ptr(logits) || !ok_ptr(ws)) return TQ_EINVAL;
+  if (ws_bytes < tq_logits_workspace(B, Hq, tk->d, tk->m)) return TQ_EWORKSPACE;
+  float* qr = static_cast<float*>(ws);
+  float* u = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                      align256(static_cast<size_t>(B) * Hq * tk->d * sizeof(float)));
+  hipError_t e = tq::launch_qprep(*tk, q, q_dtype, B * Hq, qr, u, stream);
+  if (e != hipSuccess) return TQ_EHIP;
+  return from_hip(tq::launch_logits(*tk, qr, u, B, Hq, Hkv, *k, logits, stream));
+}
+
+size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || T < 0 || d < 0 || m < 0) return 0;
+  const size_t nh = static_cast<size_t>(B) * Hq;
+  const size_t nsplit = static_cast<size_t>(tq::decode_splits(T));
+  return tq_logits_workspace(B, Hq, d, m) + align256(nh * nsplit * (d + 2) * sizeof(float));
+}
+
+tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype,
+                         int B, int Hq, int Hkv, const tq_packed* k, const tq_packed* v,
+                         float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  tq_status st = check_tables(tk, true);
+  if (st != TQ_OK) return st;
+  st = check_tables(tv, false);
+  if (st != TQ_OK) return st;
+  if (tv->d != tk->d) return TQ_EINVAL;
+  st = check_packed(k, tk, TQ_KEY);
+  if (st != TQ_OK) return st;
+  st = check_packed(v, tv, TQ_VALUE);
+  if (st != TQ_OK) return st;
+  st = check_heads(B, Hq, Hkv, 8);
+  if (st != TQ_OK) return st;
+  if (k->nseq != static_cast<int64_t>(B) * Hkv || v->nseq != k->nseq || v->T != k->T)
+    return TQ_EINVAL;
+  if (k->T < 1 && B > 0) return TQ_EINVAL;
+  if (!(scale > 0.0f) || !isfinite(scale)) return TQ_EINVAL;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
+  if (B == 0) return TQ_OK;
+  if (!ok_ptr(q) || !ok_ptr(out) || !ok_ptr(ws)) return TQ_EINVAL;
+  if (ws_bytes < tq_decode_workspace(B, Hq, Hkv, k->T, tk->d, tk->m)) return TQ_EWORKSPACE;
+  const size_t nh = static_cast<size_t>(B) * Hq;
+  char* base = static_cast<char*>(ws);
+  float* qr = reinterpret_cast<float*>(base);
+  float* u = reinterpret_cast<float*>(base + align256(nh * tk->d * sizeof(float)));
+  float* partials = reinterpret_cast<float*>(base + tq_logits_workspace(B, Hq, tk->d, tk->m));
+  hipError_t e = tq::launch_qprep(*tk, q, q_dtype, B * Hq, qr, u, stream);
+  if (e != hipSuccess) return TQ_EHIP;
+  return from_hip(tq::launch_decode(*tk, *tv, qr, u, B, Hq, Hkv, *k, *v, scale, partials, out, stream));
+}
+
+}  // extern "C"

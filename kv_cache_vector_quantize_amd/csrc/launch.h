@@ -1,0 +1,32 @@
+// Internal launchers (host side), one per kernel family.  Arguments have
+// been validated by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+hipError_t launch_codebook(int d, int bits, double* c64, double* b64, float* c32, float* b32,
+                           hipStream_t stream);
+
+hipError_t launch_rotation(int d, const double* G, double* Q, float* Q32, hipStream_t stream);
+
+hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,
+                           hipStream_t stream);
+
+// Pre-rotated queries: qr[h][d] = Pi q, u[h][m] = S qr, for nh = B*Hq heads.
+hipError_t launch_qprep(const tq_tables& tk, const void* q, int q_dtype, int nh, float* qr,
+                        float* u, hipStream_t stream);
+
+hipError_t launch_logits(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
+                         int Hkv, const tq_packed& k, float* logits, hipStream_t stream);
+
+// Split-K decode: partials[h][split][d + 2] then the combine.
+int decode_splits(int64_t T);
+hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* qr, const float* u,
+                         int B, int Hq, int Hkv, const tq_packed& k, const tq_packed& v,
+                         float scale, float* partials, float* out, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,246 @@
+"""Thin ctypes binding of libtq.so over torch tensors.
+
+torch supplies device memory and the current stream; every step of the
+computation runs in the library's HIP kernels.  The names follow the C ABI
+in ``include/tq.h``.  Any non-OK status raises ``TQError``; a missing
+library raises ``ImportError`` (there is no other code path).
+"""
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2, -3, -4
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+TQ_KEY, TQ_VALUE = 0, 1
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {lib().tq_status_str(status).decode()} ({status})")
+        self.status = status
+
+
+class Tables(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("m", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("rot", ctypes.c_void_p),
+                ("sketch", ctypes.c_void_p), ("centroids", ctypes.c_void_p),
+                ("bounds", ctypes.c_void_p)]
+
+
+class Packed(ctypes.Structure):
+    _fields_ = [("role", ctypes.c_int32), ("bits", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("m", ctypes.c_int32), ("nseq", ctypes.c_int64), ("T", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("signs", ctypes.c_void_p),
+                ("norm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p),
+                ("norm_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libtq.so once (raises ImportError if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} not found: build it with "
+                          "`python -m kv_cache_vector_quantize_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    L.tq_abi_version.restype = i32
+    L.tq_status_str.restype = ctypes.c_char_p
+    L.tq_status_str.argtypes = [i32]
+    L.tq_codebook.restype = i32
+    L.tq_codebook.argtypes = [i32, i32, vp, vp, vp, vp, vp]
+    L.tq_rotation.restype = i32
+    L.tq_rotation.argtypes = [i32, vp, vp, vp, vp]
+    L.tq_quantize.restype = i32
+    L.tq_quantize.argtypes = [ctypes.POINTER(Tables), vp, i32, ctypes.POINTER(Packed), vp]
+    L.tq_logits_workspace.restype = sz
+    L.tq_logits_workspace.argtypes = [i32, i32, i32, i32]
+    L.tq_attn_logits.restype = i32
+    L.tq_attn_logits.argtypes = [ctypes.POINTER(Tables), vp, i32, i32, i32, i32,
+                                 ctypes.POINTER(Packed), vp, vp, sz, vp]
+    L.tq_decode_workspace.restype = sz
+    L.tq_decode_workspace.argtypes = [i32, i32, i32, i64, i32, i32]
+    L.tq_attn_decode.restype = i32
+    L.tq_attn_decode.argtypes = [ctypes.POINTER(Tables), ctypes.POINTER(Tables), vp, i32, i32,
+                                 i32, i32, ctypes.POINTER(Packed), ctypes.POINTER(Packed),
+                                 ctypes.c_float, vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def loaded_path():
+    return _LIB_PATH if _lib is not None else None
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status, what):
+    if status != TQ_OK:
+        raise TQError(status, what)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    if t.dtype == torch.float16:
+        return TQ_F16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# --------------------------------------------------------------- setup calls
+def tq_codebook(d, bits, device="cuda"):
+    """Returns (centroids64, bounds64, centroids32, bounds32) device tensors."""
+    L = 2 ** bits
+    c64 = torch.empty(L, dtype=torch.float64, device=device)
+    b64 = torch.empty(max(L - 1, 1), dtype=torch.float64, device=device)
+    c32 = torch.empty(L, dtype=torch.float32, device=device)
+    b32 = torch.empty(max(L - 1, 1), dtype=torch.float32, device=device)
+    _check(lib().tq_codebook(d, bits, _ptr(c64), _ptr(b64), _ptr(c32), _ptr(b32), _stream()),
+           "tq_codebook")
+    return c64, b64[:L - 1], c32, b32[:L - 1]
+
+
+def tq_rotation(G):
+    """G: device float64 [d, d].  Returns (rot64, rot32)."""
+    d = G.shape[0]
+    G = G.contiguous()
+    r64 = torch.empty((d, d), dtype=torch.float64, device=G.device)
+    r32 = torch.empty((d, d), dtype=torch.float32, device=G.device)
+    _check(lib().tq_rotation(d, _ptr(G), _ptr(r64), _ptr(r32), _stream()), "tq_rotation")
+    return r64, r32
+
+
+@dataclass
+class StreamTables:
+    """Device tables of one stream (tensors kept alive here)."""
+    d: int
+    m: int
+    bits: int
+    rot: torch.Tensor
+    sketch: Optional[torch.Tensor]
+    centroids: torch.Tensor
+    bounds: torch.Tensor
+
+    def c_struct(self):
+        return Tables(self.d, self.m, self.bits, 0, self.rot.data_ptr(),
+                      None if self.sketch is None else self.sketch.data_ptr(),
+                      self.centroids.data_ptr(), self.bounds.data_ptr())
+
+
+def make_tables(G, S, bits, device="cuda"):
+    """Rotation from the Gaussian G (numpy/torch float64 [d, d]), sketch S
+    (float64 [m, d] or None) and the Lloyd-Max codebook, all built on the
+    device by the library."""
+    G = torch.as_tensor(G, dtype=torch.float64).to(device)
+    _, rot32 = tq_rotation(G)
+    d = G.shape[0]
+    sk = None if S is None else torch.as_tensor(S, dtype=torch.float64).to(device).float().contiguous()
+    _, _, c32, b32 = tq_codebook(d, bits, device)
+    b32 = b32.clone() if b32.numel() else torch.zeros(1, dtype=torch.float32, device=device)
+    return StreamTables(d, 0 if sk is None else sk.shape[0], bits, rot32, sk, c32, b32)
+
+
+@dataclass
+class PackedStream:
+    role: int
+    bits: int
+    d: int
+    m: int
+    nseq: int
+    T: int
+    codes: torch.Tensor
+    signs: Optional[torch.Tensor]
+    norm: torch.Tensor
+    rnorm: Optional[torch.Tensor]
+    norm_dtype: int
+
+    def c_struct(self):
+        return Packed(self.role, self.bits, self.d, self.m, self.nseq, self.T,
+                      self.codes.data_ptr(), _dp(self.signs), self.norm.data_ptr(),
+                      _dp(self.rnorm), self.norm_dtype, 0)
+
+
+def _dp(t):
+    return None if t is None else t.data_ptr()
+
+
+def alloc_packed(role, tables, nseq, T, norm_dtype="f16", device="cuda"):
+    """Allocate a packed stream in the canonical layout (see include/tq.h)."""
+    nd = TQ_F16 if norm_dtype == "f16" else TQ_F32
+    tdt = torch.float16 if norm_dtype == "f16" else torch.float32
+    d, m, bits = tables.d, tables.m, tables.bits
+    if role == TQ_KEY:
+        codes = torch.zeros((nseq, T, d // 32, bits), dtype=torch.int32, device=device)
+        signs = torch.zeros((nseq, T, m // 32), dtype=torch.int32, device=device)
+        rnorm = torch.zeros((nseq, T), dtype=tdt, device=device)
+    else:
+        codes = torch.zeros((nseq, (T + 31) // 32, d, bits), dtype=torch.int32, device=device)
+        signs, rnorm = None, None
+    norm = torch.zeros((nseq, T), dtype=tdt, device=device)
+    return PackedStream(role, bits, d, m if role == TQ_KEY else 0, nseq, T, codes, signs, norm,
+                        rnorm, nd)
+
+
+# ------------------------------------------------------------ hot-path calls
+def tq_quantize(tables, x, out):
+    """x: [nseq, T, d] float32 / bfloat16 on the device; out: PackedStream."""
+    assert x.is_contiguous()
+    t, p = tables.c_struct(), out.c_struct()
+    _check(lib().tq_quantize(ctypes.byref(t), _ptr(x), _dtype_code(x), ctypes.byref(p),
+                             _stream(x.device)), "tq_quantize")
+    return out
+
+
+def tq_attn_logits(tk, q, k, B, Hq, Hkv, ws=None):
+    """q: [B, Hq, d]; k: packed keys with nseq = B*Hkv.  Returns [B, Hq, T] float32."""
+    assert q.is_contiguous()
+    L = lib()
+    need = L.tq_logits_workspace(B, Hq, tk.d, tk.m)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, k.T), dtype=torch.float32, device=q.device)
+    t, p = tk.c_struct(), k.c_struct()
+    _check(L.tq_attn_logits(ctypes.byref(t), _ptr(q), _dtype_code(q), B, Hq, Hkv, ctypes.byref(p),
+                            _ptr(out), _ptr(ws), ws.numel(), _stream(q.device)), "tq_attn_logits")
+    return out
+
+
+def decode_workspace_bytes(B, Hq, Hkv, T, d, m):
+    return lib().tq_decode_workspace(B, Hq, Hkv, T, d, m)
+
+
+def tq_attn_decode(tk, tv, q, k, v, B, Hq, Hkv, scale=None, ws=None, out=None):
+    """Returns out [B, Hq, d] float32."""
+    assert q.is_contiguous()
+    L = lib()
+    if scale is None:
+        scale = 1.0 / math.sqrt(tk.d)
+    need = L.tq_decode_workspace(B, Hq, Hkv, k.T, tk.d, tk.m)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, tk.d), dtype=torch.float32, device=q.device)
+    t1, t2, p1, p2 = tk.c_struct(), tv.c_struct(), k.c_struct(), v.c_struct()
+    _check(L.tq_attn_decode(ctypes.byref(t1), ctypes.byref(t2), _ptr(q), _dtype_code(q), B, Hq,
+                            Hkv, ctypes.byref(p1), ctypes.byref(p2), float(scale), _ptr(out),
+                            _ptr(ws), ws.numel(), _stream(q.device)), "tq_attn_decode")
+    return out

@@ -72,23 +72,24 @@ def pack_value_codes(idx, bits):
     idx = np.asarray(idx, dtype=np.int64)
     S, T, d = idx.shape
     nb = (T + 31) // 32
+    padded = np.zeros((S, nb * 32, d), dtype=np.int64)
+    padded[:, :T] = idx
+    blocks = padded.reshape(S, nb, 32, d)            # [S, block, k, j]
     words = np.zeros((S, nb, d, bits), dtype=np.uint64)
-    for t in range(T):
-        blk, k = divmod(t, 32)
+    for k in range(32):
         for p in range(bits):
-            words[:, blk, :, p] |= ((idx[:, t, :] >> p) & 1).astype(np.uint64) << np.uint64(k)
+            words[:, :, :, p] |= ((blocks[:, :, k, :] >> p) & 1).astype(np.uint64) << np.uint64(k)
     return words.astype(np.uint32)
 
 
 def unpack_value_codes(words, T):
     words = np.asarray(words, dtype=np.uint32).astype(np.int64)
     S, nb, d, bits = words.shape
-    idx = np.zeros((S, T, d), dtype=np.int64)
-    for t in range(T):
-        blk, k = divmod(t, 32)
+    blocks = np.zeros((S, nb, 32, d), dtype=np.int64)
+    for k in range(32):
         for p in range(bits):
-            idx[:, t, :] |= ((words[:, blk, :, p] >> k) & 1) << p
-    return idx
+            blocks[:, :, k, :] |= ((words[:, :, :, p] >> k) & 1) << p
+    return blocks.reshape(S, nb * 32, d)[:, :T]
 
 
 def round_norms(x, dtype):

@@ -1,0 +1,144 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/tq.h declares, and rejects bad arguments on the host before any
+launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from kv_cache_vector_quantize_amd import tq
+    if not os.path.exists(tq._LIB_PATH):
+        from kv_cache_vector_quantize_amd import build
+        build.build()
+    return tq.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.tq_abi_version() == 1
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, 7):
+        s = L.tq_status_str(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_workspace_sizes(L):
+    assert L.tq_logits_workspace(1, 32, 128, 128) == 32 * 128 * 4 * 2
+    assert L.tq_logits_workspace(1, 1, 128, 0) == 512
+    # rotated queries + one (d + 2)-float partial per head per 1024-token split
+    ws = L.tq_decode_workspace(1, 64, 8, 524288, 128, 128)
+    part = 64 * 512 * 130 * 4
+    assert ws == 64 * 128 * 4 * 2 + ((part + 255) // 256) * 256
+    assert L.tq_decode_workspace(-1, 1, 1, 1, 128, 128) == 0
+
+
+# Fake, aligned device addresses: every call below must be rejected by the
+# host-side validation, so nothing is ever launched with them.  On a machine
+# with a GPU the cases are skipped (the GPU tests cover the same paths with
+# real buffers).
+FAKE = 0x10000
+needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                                  reason="fake device pointers are only used without a GPU")
+
+
+def _tables(tq, d=128, m=128, bits=2, reserved=0, sketch=True):
+    return tq.Tables(d, m, bits, reserved, FAKE, FAKE if sketch else None, FAKE, FAKE)
+
+
+def _packed(tq, role=0, bits=2, d=128, m=128, nseq=1, T=4, nd=2):
+    key = role == 0
+    return tq.Packed(role, bits, d, m, nseq, T, FAKE, FAKE if key else None, FAKE,
+                     FAKE if key else None, nd, 0)
+
+
+@needs_no_gpu
+def test_codebook_and_rotation_validation(L):
+    vp = ctypes.c_void_p
+    assert L.tq_codebook(2, 2, None, None, vp(FAKE), vp(FAKE), None) == -1      # d < 3
+    assert L.tq_codebook(128, 5, None, None, vp(FAKE), vp(FAKE), None) == -1    # bits > 4
+    assert L.tq_codebook(128, 0, None, None, vp(FAKE), vp(FAKE), None) == -1
+    assert L.tq_codebook(128, 2, None, None, None, vp(FAKE), None) == -1        # null out
+    assert L.tq_codebook(128, 2, None, None, vp(FAKE + 4), vp(FAKE), None) == -1  # misaligned
+    assert L.tq_rotation(129, vp(FAKE), vp(FAKE), None, None) == -1
+    assert L.tq_rotation(128, None, vp(FAKE), None, None) == -1
+
+
+@needs_no_gpu
+def test_quantize_validation(L):
+    from kv_cache_vector_quantize_amd import tq
+    by = ctypes.byref
+    x = ctypes.c_void_p(FAKE)
+    cases = [
+        (_tables(tq, reserved=1), _packed(tq), -1),
+        (_tables(tq, bits=5), _packed(tq, bits=5), -1),
+        (_tables(tq, d=96), _packed(tq, d=96), -2),            # valid, unsupported d
+        (_tables(tq, m=64), _packed(tq, m=64), -2),            # unsupported sketch size
+        (_tables(tq), _packed(tq, bits=3), -1),                # bits mismatch
+        (_tables(tq, m=0, sketch=False), _packed(tq, role=0, m=0), -1),  # key without sketch
+        (_tables(tq, m=0, sketch=False), _packed(tq, role=1, m=0, nd=7), -1),  # bad norm dtype
+        (_tables(tq), _packed(tq, role=3), -1),
+        (_tables(tq), _packed(tq, T=-1), -1),
+    ]
+    for t, p, want in cases:
+        assert L.tq_quantize(by(t), x, 1, by(p), None) == want, (want,)
+    # bad input dtype
+    assert L.tq_quantize(by(_tables(tq)), x, 2, by(_packed(tq)), None) == -1
+    # null input with work to do
+    assert L.tq_quantize(by(_tables(tq)), None, 1, by(_packed(tq)), None) == -1
+    # empty stream: nothing to do, OK without touching any pointer
+    assert L.tq_quantize(by(_tables(tq)), None, 1, by(_packed(tq, nseq=0)), None) == 0
+
+
+@needs_no_gpu
+def test_attention_validation(L):
+    from kv_cache_vector_quantize_amd import tq
+    by = ctypes.byref
+    vp = ctypes.c_void_p
+    tk, tv = _tables(tq), _tables(tq, m=0, sketch=False, bits=3)
+    pk = _packed(tq, nseq=16, T=64)
+    pv = _packed(tq, role=1, m=0, bits=3, nseq=16, T=64)
+    ws = L.tq_decode_workspace(2, 32, 8, 64, 128, 128)
+    q = vp(FAKE)
+    # Hq not a multiple of Hkv
+    assert L.tq_attn_logits(by(tk), q, 1, 2, 30, 8, by(pk), vp(FAKE), vp(FAKE), ws, None) == -1
+    # nseq != B * Hkv
+    assert L.tq_attn_logits(by(tk), q, 1, 3, 32, 8, by(pk), vp(FAKE), vp(FAKE), ws, None) == -1
+    # group of 32 query heads per kv head: unsupported
+    assert L.tq_attn_logits(by(tk), q, 1, 16, 32, 1, by(pk), vp(FAKE), vp(FAKE), ws, None) == -2
+    # workspace too small
+    assert L.tq_attn_logits(by(tk), q, 1, 2, 32, 8, by(pk), vp(FAKE), vp(FAKE), 16, None) == -3
+    # value stream passed as keys
+    assert L.tq_attn_logits(by(tv), q, 1, 2, 32, 8, by(pv), vp(FAKE), vp(FAKE), ws, None) == -1
+    args = lambda scale, k, v, w: (by(tk), by(tv), q, 1, 2, 32, 8, by(k), by(v), scale, vp(FAKE),
+                                   vp(FAKE), w, None)
+    assert L.tq_attn_decode(*args(0.0, pk, pv, ws)) == -1                   # bad scale
+    assert L.tq_attn_decode(*args(float("nan"), pk, pv, ws)) == -1
+    assert L.tq_attn_decode(*args(0.1, pk, _packed(tq, role=1, m=0, bits=3, nseq=16, T=65), ws)) == -1
+    assert L.tq_attn_decode(*args(0.1, pk, pv, ws - 1)) == -3
+    assert L.tq_attn_decode(*args(0.1, _packed(tq, nseq=16, T=0),
+                                  _packed(tq, role=1, m=0, bits=3, nseq=16, T=0), ws)) == -1
+    # 16 query heads per kv head: fine for logits, unsupported for decode
+    pk2 = _packed(tq, nseq=2, T=64)
+    pv2 = _packed(tq, role=1, m=0, bits=3, nseq=2, T=64)
+    assert L.tq_attn_decode(by(tk), by(tv), q, 1, 1, 32, 2, by(pk2), by(pv2), 0.1, vp(FAKE),
+                            vp(FAKE), 1 << 30, None) == -2

@@ -1,0 +1,140 @@
+"""GPU parity of tq_attn_logits and tq_attn_decode against the oracle,
+which recomputes every output from the GPU's own packed records."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_vector_quantize_amd import inputs, tq
+
+from gpu_common import gpu_tables, key_records, oracle_tables, say, to64, value_records
+from parity import decode_close, logits_close
+
+pytestmark = pytest.mark.gpu
+D = M = 128
+
+
+def _keys(X, bits, nd):
+    tabs = gpu_tables(D, M, bits)
+    p = tq.alloc_packed(tq.TQ_KEY, tabs, X.shape[0], X.shape[1], nd)
+    tq.tq_quantize(tabs, X, p)
+    return tabs, p
+
+
+def _values(X, bits, nd):
+    tabs = gpu_tables(D, 0, bits)
+    p = tq.alloc_packed(tq.TQ_VALUE, tabs, X.shape[0], X.shape[1], nd)
+    tq.tq_quantize(tabs, X, p)
+    return tabs, p
+
+
+def _oracle_logits(q, p, bits, B, Hq, Hkv):
+    Pi, S, c, _ = oracle_tables(D, M, bits)
+    idx, sg, n, rn = key_records(p)
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, p.T))
+    for b in range(B):
+        for h in range(Hq):
+            s = b * Hkv + h // G
+            out[b, h] = oracle.key_logits(q[b, h], idx[s], sg[s], n[s].astype(np.float64),
+                                          rn[s].astype(np.float64), Pi, S, c)
+    return out
+
+
+def test_tiny_logits():
+    w = inputs.WORKLOADS[1]
+    say("logits", w.name)
+    X = inputs.key_slice(w, 0, 0, device="cuda").unsqueeze(0).contiguous()
+    tk, p = _keys(X, w.k_bits, w.norm_dtype)
+    q = inputs.queries(w, device="cuda")
+    got = tq.tq_attn_logits(tk, q, p, 1, 1, 1)
+    torch.cuda.synchronize()
+    ref = _oracle_logits(to64(q), p, w.k_bits, 1, 1, 1)
+    ok, nbad, mx = logits_close(got.cpu().numpy(), ref)
+    assert ok, (nbad, mx)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_logits_group_sizes_ragged(G):
+    say("logits group", G)
+    B, Hkv, T = 2, 2, 777
+    Hq = G * Hkv
+    X = (torch.randn((B * Hkv, T, D), device="cuda") * 2).to(torch.bfloat16)
+    tk, p = _keys(X.contiguous(), 3, "f16")
+    q = torch.randn((B, Hq, D), device="cuda")
+    got = tq.tq_attn_logits(tk, q, p, B, Hq, Hkv)
+    torch.cuda.synchronize()
+    ref = _oracle_logits(to64(q), p, 3, B, Hq, Hkv)
+    ok, nbad, mx = logits_close(got.cpu().numpy(), ref)
+    assert ok, (nbad, mx)
+
+
+def test_llama8b_logits_full_size():
+    w = inputs.WORKLOADS[2]
+    say("logits full size", w.name)
+    K = inputs.keys(w, device="cuda").reshape(w.nseq, w.T, D)
+    tk, p = _keys(K, w.k_bits, w.norm_dtype)
+    q = inputs.queries(w, device="cuda")
+    got = tq.tq_attn_logits(tk, q, p, w.B, w.Hq, w.Hkv)
+    torch.cuda.synchronize()
+    ref = _oracle_logits(to64(q), p, w.k_bits, w.B, w.Hq, w.Hkv)
+    ok, nbad, mx = logits_close(got.cpu().numpy(), ref)
+    assert ok, (nbad, mx)
+
+
+def _oracle_decode_rows(q, pk, pv, kbits, vbits, B, Hq, Hkv, rows):
+    Pi, S, ck, _ = oracle_tables(D, M, kbits)
+    _, _, cv, _ = oracle_tables(D, 0, vbits)
+    G = Hq // Hkv
+    out = {}
+    for (b, h) in rows:
+        s = b * Hkv + h // G
+        kc = pk.codes[s].cpu().numpy().view(np.uint32)
+        ks = pk.signs[s].cpu().numpy().view(np.uint32)
+        vc = pv.codes[s].cpu().numpy().view(np.uint32)
+        o = oracle.decode_from_records(
+            q[b:b + 1, h:h + 1], kc[None, None], ks[None, None],
+            pk.norm[s].cpu().numpy().astype(np.float64)[None, None],
+            pk.rnorm[s].cpu().numpy().astype(np.float64)[None, None], vc[None, None],
+            pv.norm[s].cpu().numpy().astype(np.float64)[None, None], pk.T, Pi, S, ck, cv)
+        out[(b, h)] = o[0, 0]
+    return out
+
+
+@pytest.mark.parametrize("G,T", [(1, 1), (2, 31), (4, 1000), (8, 2500)])
+def test_decode_small(G, T):
+    say("decode small", G, T)
+    B, Hkv = 2, 2
+    Hq = G * Hkv
+    K = (torch.randn((B * Hkv, T, D), device="cuda") * 1.5).to(torch.bfloat16).contiguous()
+    V = torch.randn((B * Hkv, T, D), device="cuda").to(torch.bfloat16).contiguous()
+    tk, pk = _keys(K, 2, "f16")
+    tv, pv = _values(V, 3, "f16")
+    q = torch.randn((B, Hq, D), device="cuda").to(torch.bfloat16)
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv).cpu().numpy()
+    rows = [(b, h) for b in range(B) for h in range(Hq)]
+    ref = _oracle_decode_rows(to64(q), pk, pv, 2, 3, B, Hq, Hkv, rows)
+    ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
+    assert ok, rel
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_decode_full_size_sampled_rows(cfg):
+    w = inputs.WORKLOADS[cfg]
+    say("decode full size", w.name)
+    K = inputs.keys(w, device="cuda").reshape(w.nseq, w.T, D)
+    tk, pk = _keys(K, w.k_bits, w.norm_dtype)
+    del K
+    V = inputs.values(w, device="cuda").reshape(w.nseq, w.T, D)
+    tv, pv = _values(V, w.v_bits, w.norm_dtype)
+    del V
+    q = inputs.queries(w, device="cuda")
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv).cpu().numpy()
+    rng = np.random.default_rng(cfg)
+    rows = [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(3)]
+    ref = _oracle_decode_rows(to64(q), pk, pv, w.k_bits, w.v_bits, w.B, w.Hq, w.Hkv, rows)
+    ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
+    assert ok, rel

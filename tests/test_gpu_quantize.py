@@ -1,0 +1,149 @@
+"""GPU parity of tq_quantize against the oracle (codes, signs, norms)."""
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_vector_quantize_amd import inputs, tq
+
+from gpu_common import gpu_tables, key_records, oracle_tables, say, to64, value_records
+from parity import check_key_stream, check_value_stream
+
+pytestmark = pytest.mark.gpu
+D = M = 128
+
+
+def _quantize_keys(X, bits, norm_dtype):
+    nseq, T, _ = X.shape
+    tabs = gpu_tables(D, M, bits)
+    p = tq.alloc_packed(tq.TQ_KEY, tabs, nseq, T, norm_dtype)
+    tq.tq_quantize(tabs, X, p)
+    torch.cuda.synchronize()
+    return p
+
+
+def _quantize_values(X, bits, norm_dtype):
+    nseq, T, _ = X.shape
+    tabs = gpu_tables(D, 0, bits)
+    p = tq.alloc_packed(tq.TQ_VALUE, tabs, nseq, T, norm_dtype)
+    tq.tq_quantize(tabs, X, p)
+    torch.cuda.synchronize()
+    return p
+
+
+def _check_keys(X, p, bits, norm_dtype, rows=None):
+    Pi, S, c, t = oracle_tables(D, M, bits)
+    idx, sg, n, rn = key_records(p)
+    x = to64(X).reshape(-1, D)
+    idx, sg, n, rn = idx.reshape(-1, D), sg.reshape(-1, M), n.reshape(-1), rn.reshape(-1)
+    if rows is not None:
+        x, idx, sg, n, rn = x[rows], idx[rows], sg[rows], n[rows], rn[rows]
+    rep = check_key_stream(x, idx, sg, n, rn, Pi, S, c, t, norm_dtype)
+    assert rep["ok"], rep
+    return rep
+
+
+def _check_values(X, p, bits, norm_dtype):
+    Pi, _, c, t = oracle_tables(D, 0, bits)
+    idx, n = value_records(p)
+    rep = check_value_stream(to64(X).reshape(-1, D), idx.reshape(-1, D), n.reshape(-1), Pi, c, t,
+                             norm_dtype)
+    assert rep["ok"], rep
+    return rep
+
+
+def test_tiny_keys_fp32_input_fp32_norms():
+    w = inputs.WORKLOADS[1]
+    say("quantize tiny keys", w.name)
+    X = inputs.key_slice(w, 0, 0, device="cuda").unsqueeze(0).contiguous()
+    p = _quantize_keys(X, w.k_bits, "f32")
+    _check_keys(X, p, w.k_bits, "f32")
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_bf16_keys_student_t_ragged(bits):
+    w = inputs.WORKLOADS[2]
+    say("quantize bf16 keys", bits)
+    X = inputs.key_slice(w, 0, 3, device="cuda", T=1000).reshape(2, 500, D).contiguous()
+    p = _quantize_keys(X, bits, "f16")
+    _check_keys(X, p, bits, "f16")
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_bf16_values_ragged_blocks(bits):
+    w = inputs.WORKLOADS[4]
+    say("quantize bf16 values", bits)
+    X = inputs.value_slice(w, 0, 1, device="cuda", T=3 * 333).reshape(3, 333, D).contiguous()
+    p = _quantize_values(X, bits, "f16")
+    _check_values(X, p, bits, "f16")
+    # padded token bits of the last block are zero
+    codes = p.codes.cpu().numpy().view(np.uint32)
+    tail = 333 - 32 * 10
+    assert np.all((codes[:, 10] >> np.uint32(tail)) == 0)
+
+
+def test_zero_vectors_and_single_token():
+    say("quantize zero vectors")
+    X = torch.randn((3, 1, D), device="cuda")
+    X[1] = 0.0
+    p = _quantize_keys(X.contiguous(), 2, "f32")
+    idx, sg, n, rn = key_records(p)
+    assert n[1, 0] == 0 and rn[1, 0] == 0
+    assert np.all(idx[1, 0] == 2) and np.all(sg[1, 0])
+    _check_keys(X, p, 2, "f32")
+    pv = _quantize_values(X.contiguous(), 3, "f32")
+    vidx, vn = value_records(pv)
+    assert vn[1, 0] == 0 and np.all(vidx[1, 0] == 4)
+
+
+def test_empty_inputs_are_noops():
+    say("quantize empty")
+    tabs = gpu_tables(D, M, 2)
+    for nseq, T in ((0, 5), (2, 0)):
+        p = tq.alloc_packed(tq.TQ_KEY, tabs, nseq, T, "f16")
+        tq.tq_quantize(tabs, torch.empty((nseq, T, D), device="cuda"), p)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_across_runs():
+    w = inputs.WORKLOADS[2]
+    say("quantize determinism")
+    X = inputs.key_slice(w, 0, 0, device="cuda", T=4096).unsqueeze(0).contiguous()
+    a = _quantize_keys(X, 3, "f16")
+    b = _quantize_keys(X, 3, "f16")
+    for u, v in ((a.codes, b.codes), (a.signs, b.signs), (a.norm, b.norm), (a.rnorm, b.rnorm)):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_full_size_quantize_sampled(cfg):
+    """The full workload in the bench's launch configuration; the oracle
+    checks sampled tokens (keys) and sampled 32-token blocks (values)."""
+    w = inputs.WORKLOADS[cfg]
+    say("full-size quantize", w.name)
+    K = inputs.keys(w, device="cuda").reshape(w.nseq, w.T, D)
+    pk = _quantize_keys(K, w.k_bits, w.norm_dtype)
+    rng = np.random.default_rng(cfg)
+    rows = np.sort(rng.choice(w.nseq * w.T, size=3000, replace=False))
+    Pi, S, c, t = oracle_tables(D, M, w.k_bits)
+    sel = torch.as_tensor(rows, device="cuda")
+    x = to64(K.reshape(-1, D)[sel])
+    codes = pk.codes.reshape(-1, D // 32, w.k_bits)[sel].cpu().numpy().view(np.uint32)
+    signs = pk.signs.reshape(-1, M // 32)[sel].cpu().numpy().view(np.uint32)
+    import oracle
+    rep = check_key_stream(x, oracle.unpack_key_codes(codes, D), oracle.unpack_signs(signs, M),
+                           pk.norm.reshape(-1)[sel].cpu().numpy(),
+                           pk.rnorm.reshape(-1)[sel].cpu().numpy(), Pi, S, c, t, w.norm_dtype)
+    assert rep["ok"], rep
+    del K, pk
+    V = inputs.values(w, device="cuda").reshape(w.nseq, w.T, D)
+    pv = _quantize_values(V, w.v_bits, w.norm_dtype)
+    Piv, _, cv, tv = oracle_tables(D, 0, w.v_bits)
+    nblk = (w.T + 31) // 32
+    for s, blk in zip(rng.integers(0, w.nseq, 24), rng.integers(0, nblk, 24)):
+        x = to64(V[s, blk * 32:(blk + 1) * 32])
+        words = pv.codes[s, blk].cpu().numpy().view(np.uint32)[None, None]
+        idx = oracle.unpack_value_codes(words.reshape(1, 1, D, w.v_bits), 32)[0]
+        rep = check_value_stream(x, idx, pv.norm[s, blk * 32:(blk + 1) * 32].cpu().numpy(), Piv,
+                                 cv, tv, w.norm_dtype)
+        assert rep["ok"], (s, blk, rep)
