@@ -16,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
+# layout probes for the GPU unit tests, kept out of libtq.so's exports
+PROBE_LIB = os.path.join(PKG, "libtq_probe.so")
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -42,18 +44,26 @@ def build(verbose=False):
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(_compile, srcs))
-    objs = [o for o, _ in results]
     if verbose:
         for _, err in results:
             if err.strip():
                 print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    objs = [o for o, _ in results]
+    probe = [o for o in objs if os.path.basename(o).startswith("probe")]
+    main = [o for o in objs if o not in probe]
+    _link(main, LIB)
+    if probe:
+        _link(probe, PROBE_LIB)
+    return LIB
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":

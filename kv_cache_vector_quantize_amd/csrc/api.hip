@@ -120,6 +120,7 @@ tq_status tq_attn_logits(const tq_tables* tk, const void* q, int q_dtype, int B,
   if (st != TQ_OK) return st;
   if (k->nseq != static_cast<int64_t>(B) * Hkv) return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
+  if (k->nseq > 65535) return TQ_EUNSUPPORTED;  // one grid row per sequence
   if (B == 0 || k->T == 0) return TQ_OK;
   if (!ok_ptr(q) || !ok_ptr(logits) || !ok_ptr(ws)) return TQ_EINVAL;
   if (ws_bytes < tq_logits_workspace(B, Hq, tk->d, tk->m)) return TQ_EWORKSPACE;
@@ -155,6 +156,7 @@ tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q
   if (k->nseq != static_cast<int64_t>(B) * Hkv || v->nseq != k->nseq || v->T != k->T)
     return TQ_EINVAL;
   if (k->T < 1 && B > 0) return TQ_EINVAL;
+  if (k->nseq > 65535) return TQ_EUNSUPPORTED;  // one grid row per sequence
   if (!(scale > 0.0f) || !isfinite(scale)) return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
   if (B == 0) return TQ_OK;

@@ -3,7 +3,7 @@
 // keys only, 1-bit QJL sketch of the residual).
 //
 // Layout of the work: one unit = 32 consecutive tokens of one sequence (one
-// value-stream word per coordinate and plane).  A persistent workgroup of
+// value-stream record per coordinate).  A persistent workgroup of
 // 256 threads keeps Pi^T and S^T in LDS and walks units; per unit it takes
 // the 32 tokens 8 at a time.  Thread (j, hv): coordinate j = tid % 128,
 // vector half hv = tid / 128 (4 of the 8 vectors).
@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int64_t s = unit / nblk;
     const int64_t blk = unit % nblk;
-    uint32_t vacc[4] = {0u, 0u, 0u, 0u};
+    // value record of coordinate j: token k's index at bits [bits*k, bits*k+bits)
+    uint64_t vlo = 0, vhi = 0;
     for (int it = 0; it < 32 / kVec; ++it) {
       const int64_t t0 = blk * 32 + it * kVec;
       for (int e = tid; e < kD * kVec; e += kQThreads) {
@@ -115,7 +116,14 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
           }
         } else {
           if (valid) {
-            for (int p = 0; p < bits; ++p) vacc[p] |= static_cast<uint32_t>((idx >> p) & 1) << (it * kVec + v);
+            const int pos = bits * (it * kVec + v);
+            const uint64_t f = static_cast<uint64_t>(idx);
+            if (pos < 64) {
+              vlo |= f << pos;
+              if (pos + bits > 64) vhi |= f >> (64 - pos);
+            } else {
+              vhi |= f << (pos - 64);
+            }
           }
         }
       }
@@ -166,13 +174,17 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(
       __syncthreads();
     }
     if constexpr (!KEY) {
+      const uint32_t rec[4] = {static_cast<uint32_t>(vlo), static_cast<uint32_t>(vlo >> 32),
+                               static_cast<uint32_t>(vhi), static_cast<uint32_t>(vhi >> 32)};
       if (hv == 1) {
-        for (int p = 0; p < bits; ++p) vw[j][p] = vacc[p];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) vw[j][p] = rec[p];
       }
       __syncthreads();
       if (hv == 0) {
-        for (int p = 0; p < bits; ++p)
-          codes[((s * nblk + blk) * kD + j) * bits + p] = vacc[p] | vw[j][p];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          if (p < bits) codes[((s * nblk + blk) * kD + j) * bits + p] = rec[p] | vw[j][p];
       }
       __syncthreads();
     }

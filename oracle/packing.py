@@ -11,9 +11,13 @@ All words are little-endian uint32; bit k of a word is (word >> k) & 1.
 Key stream (one record per token, coordinates along the word):
   codes[s, t, w, p]  bit k = bit p of idx[s, t, 32*w + k]     shape [S, T, d/32, b]
   signs[s, t, w]     bit k = sign bit of z[s, t, 32*w + k]    shape [S, T, m/32]
-Value stream (blocks of 32 tokens, tokens along the word):
-  codes[s, B, j, p]  bit k = bit p of idx[s, 32*B + k, j]     shape [S, ceil(T/32), d, b]
-  bits of tokens past T in the last block are 0.
+Value stream (blocks of 32 tokens; one record of b words per coordinate):
+  codes[s, B, j, :]  the 32 b-bit indices idx[s, 32*B + k, j], k = 0..31,
+                     packed in token order: index k occupies bits
+                     [b*k, b*k + b) of the record read as one little-endian
+                     32b-bit integer (word 0 holds the lowest bits; a field
+                     may straddle two words).       shape [S, ceil(T/32), d, b]
+  fields of tokens past T in the last block are 0.
 Norms are one value per token, [S, T], stored as float32 or as float16
 (round to nearest even).
 """
@@ -68,7 +72,7 @@ def unpack_signs(words, m):
 
 
 def pack_value_codes(idx, bits):
-    """idx: [S, T, d] -> words [S, ceil(T/32), d, bits]."""
+    """idx: [S, T, d] -> words [S, ceil(T/32), d, bits] (token-order fields)."""
     idx = np.asarray(idx, dtype=np.int64)
     S, T, d = idx.shape
     nb = (T + 31) // 32
@@ -78,7 +82,9 @@ def pack_value_codes(idx, bits):
     words = np.zeros((S, nb, d, bits), dtype=np.uint64)
     for k in range(32):
         for p in range(bits):
-            words[:, :, :, p] |= ((blocks[:, :, k, :] >> p) & 1).astype(np.uint64) << np.uint64(k)
+            pos = bits * k + p                       # bit position in the record
+            w, sh = divmod(pos, 32)
+            words[:, :, :, w] |= ((blocks[:, :, k, :] >> p) & 1).astype(np.uint64) << np.uint64(sh)
     return words.astype(np.uint32)
 
 
@@ -88,7 +94,8 @@ def unpack_value_codes(words, T):
     blocks = np.zeros((S, nb, 32, d), dtype=np.int64)
     for k in range(32):
         for p in range(bits):
-            blocks[:, :, k, :] |= ((words[:, :, :, p] >> k) & 1) << p
+            w, sh = divmod(bits * k + p, 32)
+            blocks[:, :, k, :] |= ((words[:, :, :, w] >> sh) & 1) << p
     return blocks.reshape(S, nb * 32, d)[:, :T]
 
 

@@ -120,19 +120,15 @@ def test_packing_hand_worked_words():
     assert [int(v) for v in oracle.pack_signs(s)] == [int(h, 16) for h in g["signs"]["words_hex"]]
     vidx = np.zeros((1, 33, 32), dtype=np.int64)
     for j in range(32):
-        vidx[0, j, j] = 3
-    vidx[0, 32, 7] = 1
-    vw = oracle.pack_value_codes(vidx, 2)
-    assert vw.shape == (1, 2, 32, 2)
+        vidx[0, j, j] = 5
+    vidx[0, 32, 7] = 7
+    vidx[0, 11, 0] = 6
+    vw = oracle.pack_value_codes(vidx, 3)
+    assert vw.shape == (1, 2, 32, 3)
     vc = g["value_codes"]
-    for j, h in vc["words_hex_block0_plane0_for_j"].items():
-        assert int(vw[0, 0, int(j), 0]) == int(h, 16)
-    for j, h in vc["words_hex_block0_plane1_for_j"].items():
-        assert int(vw[0, 0, int(j), 1]) == int(h, 16)
-    for j, h in vc["words_hex_block1_plane0_for_j"].items():
-        assert int(vw[0, 1, int(j), 0]) == int(h, 16)
-    for j, h in vc["words_hex_block1_plane1_for_j"].items():
-        assert int(vw[0, 1, int(j), 1]) == int(h, 16)
+    for blk, key in ((0, "records_hex_block0"), (1, "records_hex_block1")):
+        for j, rec in vc[key].items():
+            assert [int(v) for v in vw[0, blk, int(j)]] == [int(h, 16) for h in rec], (blk, j)
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
