@@ -134,9 +134,7 @@ tq_status tq_attn_logits(const tq_tables* tk, const void* q, int q_dtype, int B,
 
 size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m) {
   if (B < 0 || Hq < 0 || Hkv < 1 || T < 0 || d < 0 || m < 0) return 0;
-  const size_t nh = static_cast<size_t>(B) * Hq;
-  const size_t nsplit = static_cast<size_t>(tq::decode_splits(T));
-  return tq_logits_workspace(B, Hq, d, m) + align256(nh * nsplit * (d + 2) * sizeof(float));
+  return tq::decode_workspace_layout(B, Hq, Hkv, T, d, m).total;
 }
 
 tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype,
@@ -157,19 +155,19 @@ tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q
     return TQ_EINVAL;
   if (k->T < 1 && B > 0) return TQ_EINVAL;
   if (k->nseq > 65535) return TQ_EUNSUPPORTED;  // one grid row per sequence
+  if (k->T >= (static_cast<int64_t>(1) << 28)) return TQ_EUNSUPPORTED;  // 32-bit record offsets
   if (!(scale > 0.0f) || !isfinite(scale)) return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
   if (B == 0) return TQ_OK;
   if (!ok_ptr(q) || !ok_ptr(out) || !ok_ptr(ws)) return TQ_EINVAL;
-  if (ws_bytes < tq_decode_workspace(B, Hq, Hkv, k->T, tk->d, tk->m)) return TQ_EWORKSPACE;
-  const size_t nh = static_cast<size_t>(B) * Hq;
+  const tq::DecodeWorkspace lay = tq::decode_workspace_layout(B, Hq, Hkv, k->T, tk->d, tk->m);
+  if (ws_bytes < lay.total) return TQ_EWORKSPACE;
   char* base = static_cast<char*>(ws);
-  float* qr = reinterpret_cast<float*>(base);
-  float* u = reinterpret_cast<float*>(base + align256(nh * tk->d * sizeof(float)));
-  float* partials = reinterpret_cast<float*>(base + tq_logits_workspace(B, Hq, tk->d, tk->m));
+  float* qr = reinterpret_cast<float*>(base + lay.qr);
+  float* u = reinterpret_cast<float*>(base + lay.u);
   hipError_t e = tq::launch_qprep(*tk, q, q_dtype, B * Hq, qr, u, stream);
   if (e != hipSuccess) return TQ_EHIP;
-  return from_hip(tq::launch_decode(*tk, *tv, qr, u, B, Hq, Hkv, *k, *v, scale, partials, out, stream));
+  return from_hip(tq::launch_decode(*tk, *tv, qr, u, B, Hq, Hkv, *k, *v, scale, ws, lay, out, stream));
 }
 
 }  // extern "C"
