@@ -1,5 +1,5 @@
-// Layout probe for the gfx950 matrix-core and DPP primitives the decode
-// kernel relies on; exported for the GPU unit test only (one wave, fixed
+// Layout probes for the gfx950 matrix-core and DPP primitives the decode
+// and quantize kernels rely on; exported for the GPU unit test only (one wave, fixed
 // in-bounds sizes).
 #include "common.h"
 
@@ -26,7 +26,32 @@ __global__ __launch_bounds__(64) void probe_mfma_16x16x32_kernel(const _Float16*
   dpp_out[l] = static_cast<float>(v);
 }
 
+typedef float probe_floatx16 __attribute__((ext_vector_type(16)));
+
+// A: 32x16 row-major fp16, B: 16x32 row-major fp16, D: 32x32 row-major fp32.
+__global__ __launch_bounds__(64) void probe_mfma_32x32x16_kernel(const _Float16* A, const _Float16* B,
+                                                                 float* D) {
+  const int l = threadIdx.x;
+  probe_half8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = A[(l % 32) * 16 + 8 * (l / 32) + i];   // row l%32, k = 8(l/32)+i
+    b[i] = B[(8 * (l / 32) + i) * 32 + (l % 32)]; // k = 8(l/32)+i, col l%32
+  }
+  probe_floatx16 c;
+  for (int i = 0; i < 16; ++i) c[i] = 0.f;
+  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  // col l%32, register v: row 8(v/4) + 4(l/32) + v%4
+  for (int v = 0; v < 16; ++v) D[(8 * (v / 4) + 4 * (l / 32) + v % 4) * 32 + (l % 32)] = c[v];
+}
+
 }  // namespace tq
+
+extern "C" int tq_probe_mfma_32x32x16(const void* A, const void* B, void* D, hipStream_t stream) {
+  hipLaunchKernelGGL(tq::probe_mfma_32x32x16_kernel, dim3(1), dim3(64), 0, stream,
+                     static_cast<const _Float16*>(A), static_cast<const _Float16*>(B),
+                     static_cast<float*>(D));
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 extern "C" int tq_probe_mfma_layout(const void* A, const void* B, void* D, void* dpp_out,
                                     hipStream_t stream) {

@@ -1,193 +1,487 @@
-// Online quantization of key / value vectors (a2a-mcp.org page, "How it
-// works": Stage 1 normalise + rotate + Lloyd-Max per coordinate; Stage 2,
-// keys only, 1-bit QJL sketch of the residual).
+// Online quantization of key / value vectors on the matrix cores.
 //
-// Layout of the work: one unit = 32 consecutive tokens of one sequence (one
-// value-stream record per coordinate).  A persistent workgroup of
-// 256 threads keeps Pi^T and S^T in LDS and walks units; per unit it takes
-// the 32 tokens 8 at a time.  Thread (j, hv): coordinate j = tid % 128,
-// vector half hv = tid / 128 (4 of the 8 vectors).
+// Method (a2a-mcp.org page, "How it works"): Stage 1 normalises the vector,
+// rotates it with Pi and maps every rotated coordinate to a b-bit Lloyd-Max
+// index; Stage 2 (keys only) takes the residual r = Pi x/||x|| - c[idx] and
+// stores the signs of z = S r, one bit per sketch row.
+//
+// Mapping onto gfx950 (wave64, v_mfma_f32_32x32x16_f16):
+//  * a unit of work is 32 consecutive tokens of one sequence.  The 4 waves of
+//    a workgroup share it; wave w owns the 32 rotated coordinates
+//    [32w, 32w+32) and, for keys, the 32 sketch rows [32w, 32w+32), so one
+//    32x32 output tile per product.  Its slices of Pi^T and S^T live in
+//    registers as fp16 hi + lo pairs for the whole kernel.
+//  * the 32 input vectors are staged in LDS as fp16.  Each vector is first
+//    scaled by a power of two that puts its norm just below 2^15: a bf16
+//    input is then exact in fp16, an fp32 input is split into fp16 hi + lo.
+//    Pi is held x16 so that its lo half stays a normal fp16 number.  The
+//    rotation X Pi^T carries about 22 significant bits, fp32-grade.
+//  * result layout: lane l holds coordinate 32w + l%32 of the 16 tokens
+//    16*(l/32) + v, v = 0..15 (A-row r of a tile is token
+//    16*((r/4)%2) + 4*(r/8) + r%4).  A wave-wide compare of register v is then
+//    two finished 32-bit words: the low half is word w of token v, the high
+//    half word w of token 16 + v.  Code planes and sign words are moved from
+//    those masks into lanes with v_writelane and stored lane by lane.
+//  * keys: the residual (x256, fp16 hi + lo) goes through LDS; the sketch is
+//    Z = R S^T with three products (hi*hi, hi*lo, lo*hi) and ||r||^2 is the
+//    diagonal of R R^T, each wave summing the 32 coordinates it owns.
+//  * values: every lane packs the b-bit fields of its 16 consecutive tokens
+//    of one coordinate; the 32-token record is the two lane halves' fields in
+//    token order.
+#include <math.h>
+
 #include "common.h"
 #include "launch.h"
 
+// v_writelane_b32: set lane `lane` of `old` to the wave-uniform `value`.
+extern "C" __device__ int tq_writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
 namespace tq {
 
+typedef _Float16 qhalf8 __attribute__((ext_vector_type(8)));
+typedef _Float16 qhalf2 __attribute__((ext_vector_type(2)));
+typedef float qfloatx4 __attribute__((ext_vector_type(4)));
+typedef float qfloatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t qu32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kD = 128;
-constexpr int kM = 128;
 constexpr int kQThreads = 256;
-constexpr int kVec = 8;  // vectors per inner step
+constexpr int kUnit = 32;          // tokens per unit
+constexpr int kRowH = 136;         // LDS row stride in halves (272 B, a multiple of 16 B)
+constexpr float kPiScale = 16.f;   // Pi is held x16 so that its lo half stays normal
+constexpr float kResScale = 256.f; // rotated coordinates are handled x256 (exact)
 
-template <typename XT, bool KEY>
-__global__ __launch_bounds__(kQThreads) void quantize_kernel(
-    const float* __restrict__ rot, const float* __restrict__ sketch,
-    const float* __restrict__ cent, const float* __restrict__ bnd, int bits,
-    const XT* __restrict__ x, int64_t nseq, int64_t T, uint32_t* __restrict__ codes,
-    uint32_t* __restrict__ signs, void* __restrict__ norm, void* __restrict__ rnorm,
-    int norm_dtype) {
-  __shared__ float PiT[kD][kD];                          // PiT[k][j] = Pi[j][k]
-  __shared__ float ST[KEY ? kD : 1][KEY ? kM : 1];       // ST[j][i] = S[i][j]
-  __shared__ __align__(16) float xs[kD][kVec];
-  __shared__ __align__(16) float rs[kD][kVec];
-  __shared__ float red[4][4], red2[4][4];
-  __shared__ float nrm[kVec], rho[kVec];
-  __shared__ float sc[16], sb[16];
-  __shared__ uint32_t vw[kD][4];
+__device__ __forceinline__ uint32_t writelane(uint32_t value, int lane, uint32_t old) {
+  return static_cast<uint32_t>(tq_writelane_i32(static_cast<int>(value), lane, static_cast<int>(old)));
+}
 
-  const int tid = threadIdx.x;
-  const int j = tid & (kD - 1);
-  const int hv = tid >> 7;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int L = 1 << bits;
+__device__ __forceinline__ uint32_t h2u(qhalf2 h) { return __builtin_bit_cast(uint32_t, h); }
 
-  for (int i = tid; i < kD * kD; i += kQThreads) PiT[i % kD][i / kD] = rot[i];
-  if constexpr (KEY) {
-    for (int i = tid; i < kM * kD; i += kQThreads) ST[i % kD][i / kD] = sketch[i];
+__device__ __forceinline__ qhalf8 qu4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  qu32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(qhalf8, v);
+}
+
+__device__ __forceinline__ float pow2f(int e) {  // 2^e for -126 <= e <= 127
+  return __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
+}
+
+// fp16 hi + lo fragment of 8 consecutive fp32 values scaled by `sc`.
+__device__ __forceinline__ void split_frag(const float* p, float sc, qhalf8& hi, qhalf8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = p[2 * i] * sc, b = p[2 * i + 1] * sc;
+    const qhalf2 hh = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    const qhalf2 ll = {static_cast<_Float16>(a - static_cast<float>(hh[0])),
+                       static_cast<_Float16>(b - static_cast<float>(hh[1]))};
+    h[i] = h2u(hh);
+    l[i] = h2u(ll);
   }
-  if (tid < L) sc[tid] = cent[tid];
-  if (tid < L - 1) sb[tid] = bnd[tid];
-  __syncthreads();
+  hi = qu4(h[0], h[1], h[2], h[3]);
+  lo = qu4(l[0], l[1], l[2], l[3]);
+}
 
-  const int64_t nblk = (T + 31) / 32;
+// Code table of one stream at the x256 scale: positive decision boundaries
+// bounds[L/2 .. L-2] and centroid magnitudes centroids[L/2 .. L-1].  The
+// codebooks are symmetric about 0.
+template <int BITS>
+struct QTab {
+  float tpos[(1 << BITS) / 2 > 1 ? (1 << BITS) / 2 - 1 : 1];
+  float cpos[(1 << BITS) / 2];
+};
+
+// c ? a : b on values (a conditional over two array elements would select
+// an address and keep the table out of registers)
+__device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
+
+// Index of y (x256 scale) = number of boundaries <= y.  Writes the lane masks
+// of the index bits into P (bit BITS-1 is the sign test y >= 0; the lower
+// bits are the magnitude cell, complemented for y < 0), returns the signed
+// centroid through C and the index through idx.
+template <int BITS>
+__device__ __forceinline__ void quant_one(float y, const QTab<BITS>& tab, uint64_t* P, float& C,
+                                          int& idx) {
+  const bool ms = y >= 0.f;
+  const float a = fabsf(y);
+  const uint64_t Ms = __ballot(ms);
+  float mag;
+  int cnt;
+  P[BITS - 1] = Ms;
+  if constexpr (BITS == 1) {
+    mag = tab.cpos[0];
+    cnt = 0;
+  } else if constexpr (BITS == 2) {
+    const bool m1 = a >= tab.tpos[0];
+    P[0] = ~(Ms ^ __ballot(m1));
+    mag = sel(m1, tab.cpos[1], tab.cpos[0]);
+    cnt = m1 ? 1 : 0;
+  } else if constexpr (BITS == 3) {
+    const bool m1 = a >= tab.tpos[1];
+    const bool m2 = a >= sel(m1, tab.tpos[2], tab.tpos[0]);
+    P[1] = ~(Ms ^ __ballot(m1));
+    P[0] = ~(Ms ^ __ballot(m2));
+    mag = sel(m1, sel(m2, tab.cpos[3], tab.cpos[2]), sel(m2, tab.cpos[1], tab.cpos[0]));
+    cnt = (m1 ? 2 : 0) + (m2 ? 1 : 0);
+  } else {
+    const bool m1 = a >= tab.tpos[3];
+    const bool m2 = a >= sel(m1, tab.tpos[5], tab.tpos[1]);
+    const float t3 = sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0]));
+    const bool m3 = a >= t3;
+    P[2] = ~(Ms ^ __ballot(m1));
+    P[1] = ~(Ms ^ __ballot(m2));
+    P[0] = ~(Ms ^ __ballot(m3));
+    const float lo4 = sel(m2, sel(m3, tab.cpos[3], tab.cpos[2]), sel(m3, tab.cpos[1], tab.cpos[0]));
+    const float hi4 = sel(m2, sel(m3, tab.cpos[7], tab.cpos[6]), sel(m3, tab.cpos[5], tab.cpos[4]));
+    mag = sel(m1, hi4, lo4);
+    cnt = (m1 ? 4 : 0) + (m2 ? 2 : 0) + (m3 ? 1 : 0);
+  }
+  constexpr int half = 1 << (BITS - 1);
+  C = ms ? mag : -mag;
+  idx = cnt ^ (ms ? half : half - 1);  // half + cnt, or half - 1 - cnt
+}
+
+template <typename XT>
+struct RawX {
+  static constexpr int kWords = sizeof(XT) == 4 ? 4 : 2;  // uint4 per thread (16 elements)
+  uint4 w[kWords];
+};
+
+template <typename XT>
+__device__ __forceinline__ void unpack_raw(const RawX<XT>& r, float* xv) {
+  if constexpr (sizeof(XT) == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[4 * i + 0] = __uint_as_float(r.w[i].x);
+      xv[4 * i + 1] = __uint_as_float(r.w[i].y);
+      xv[4 * i + 2] = __uint_as_float(r.w[i].z);
+      xv[4 * i + 3] = __uint_as_float(r.w[i].w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t u[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[8 * i + 2 * e] = __uint_as_float(u[e] << 16);
+        xv[8 * i + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// sum over the 8 lanes that stage one token
+__device__ __forceinline__ float sum8(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  return v;
+}
+
+template <typename XT, bool KEY, int BITS>
+__global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
+    const float* __restrict__ rot, const float* __restrict__ sketch,
+    const float* __restrict__ cent, const float* __restrict__ bnd, const XT* __restrict__ x,
+    int64_t nseq, int64_t T, uint32_t* __restrict__ codes, uint32_t* __restrict__ signs,
+    void* __restrict__ norm, void* __restrict__ rnorm, int norm_dtype) {
+  constexpr bool kSplitX = sizeof(XT) == 4;  // fp32 input: stage hi and lo
+  constexpr int kXP = kSplitX ? 2 : 1;
+  __shared__ __align__(16) _Float16 xs[kXP][kUnit][kRowH];
+  __shared__ __align__(16) _Float16 rs[KEY ? 2 : 1][KEY ? kUnit : 1][KEY ? kRowH : 8];
+  __shared__ __align__(16) float rinv_s[kUnit];   // kResScale / (kPiScale * ||scaled x||); 0 for x = 0
+  __shared__ float n_s[2][kUnit];                 // ||x||, by unit parity
+  __shared__ float rho_s[2][4][KEY ? kUnit : 1];  // per-wave sums of the residual squares (x256^2)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, h = lane >> 5;
+
+  QTab<BITS> tab;
+  constexpr int kHalf = (1 << BITS) / 2;
+#pragma unroll
+  for (int i = 0; i < kHalf; ++i) tab.cpos[i] = cent[kHalf + i] * kResScale;
+#pragma unroll
+  for (int i = 0; i + 1 < kHalf; ++i) tab.tpos[i] = bnd[kHalf + i] * kResScale;
+  if constexpr (BITS == 1) tab.tpos[0] = 0.f;
+
+  // B fragments: Pi^T for coordinates j = 32*wave + c32 and (keys) S^T for
+  // sketch rows i = 32*wave + c32; K-step c covers input index 16c + 8h + e.
+  qhalf8 bph[8], bpl[8];
+  qhalf8 bsh[KEY ? 8 : 1], bsl[KEY ? 8 : 1];
+  {
+    const int j = 32 * wave + c32;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) split_frag(rot + j * kD + 16 * c + 8 * h, kPiScale, bph[c], bpl[c]);
+    if constexpr (KEY) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) split_frag(sketch + j * kD + 16 * c + 8 * h, 1.f, bsh[c], bsl[c]);
+    }
+  }
+
+  const int64_t nblk = (T + kUnit - 1) / kUnit;
   const int64_t units = nseq * nblk;
-  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int64_t s = unit / nblk;
-    const int64_t blk = unit % nblk;
-    // value record of coordinate j: token k's index at bits [bits*k, bits*k+bits)
-    uint64_t vlo = 0, vhi = 0;
-    for (int it = 0; it < 32 / kVec; ++it) {
-      const int64_t t0 = blk * 32 + it * kVec;
-      for (int e = tid; e < kD * kVec; e += kQThreads) {
-        const int v = e / kD, k = e % kD;
-        const int64_t t = t0 + v;
-        xs[k][v] = (t < T) ? load_elem(x, (s * T + t) * kD + k) : 0.0f;
-      }
-      __syncthreads();
-      // ||x||: thread partials over its coordinate, wave sums, then 2 waves
+  // A-row c32 of a 32x32 tile holds token atok
+  const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
+  // staging role: token sv, elements 16*sq .. 16*sq+15
+  const int sv = tid >> 3, sq = tid & 7;
+  // (sequence, block) of the first unit and the per-iteration step
+  const int64_t step_s = gridDim.x / nblk, step_b = gridDim.x % nblk;
+  int64_t s = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+
+  auto load_raw = [&](int64_t us, int64_t ub, RawX<XT>& raw) {
+    const int64_t t0 = ub * kUnit;
+    if (us < nseq && t0 + sv < T) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + ((us * T + t0 + sv) * kD + 16 * sq));
 #pragma unroll
-      for (int vi = 0; vi < 4; ++vi) {
-        const float xv = xs[j][hv * 4 + vi];
-        const float sum = wave_sum(xv * xv);
-        if (lane == 0) red[wave][vi] = sum;
-      }
-      __syncthreads();
-      if (tid < kVec) nrm[tid] = sqrtf(red[2 * (tid / 4)][tid % 4] + red[2 * (tid / 4) + 1][tid % 4]);
-      __syncthreads();
-
-      // y_j = sum_k Pi[j][k] x_k for the 4 vectors of this half
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int k = 0; k < kD; ++k) {
-        const float p = PiT[k][j];
-        const float4 xv = *reinterpret_cast<const float4*>(&xs[k][hv * 4]);
-        acc[0] = fmaf(p, xv.x, acc[0]);
-        acc[1] = fmaf(p, xv.y, acc[1]);
-        acc[2] = fmaf(p, xv.z, acc[2]);
-        acc[3] = fmaf(p, xv.w, acc[3]);
-      }
-
-      float rsq[4];
+      for (int r = 0; r < RawX<XT>::kWords; ++r) raw.w[r] = src[r];
+    } else {
 #pragma unroll
-      for (int vi = 0; vi < 4; ++vi) {
-        const int v = hv * 4 + vi;
-        const int64_t t = t0 + v;
-        const bool valid = t < T;
-        const float n = nrm[v];
-        int idx;
-        float yh = 0.f;
-        if (n > 0.f) {
-          yh = acc[vi] / n;
-          idx = 0;
-          for (int i = 0; i < L - 1; ++i) idx += (yh >= sb[i]) ? 1 : 0;
-        } else {
-          idx = L / 2;
+      for (int r = 0; r < RawX<XT>::kWords; ++r) raw.w[r] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  RawX<XT> raw;
+  load_raw(s, blk, raw);
+
+  int par = 0;
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x, par ^= 1) {
+    const int64_t t0 = blk * kUnit;
+    const int nvalid = static_cast<int>((T - t0 < kUnit) ? T - t0 : kUnit);
+    int64_t ns = s + step_s, nb = blk + step_b;
+    if (nb >= nblk) {
+      nb -= nblk;
+      ++ns;
+    }
+
+    // ---------------- stage: norms, power-of-two range scale, fp16 copy
+    {
+      float xv[16];
+      unpack_raw<XT>(raw, xv);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fmaf(xv[i], xv[i], ss);
+      ss = sum8(ss);
+      int sh;
+      if (ss >= 0x1p-100f && ss <= 0x1p100f) {
+        int e;
+        (void)frexpf(ss, &e);      // ss in [2^(e-1), 2^e): ||x|| < 2^ceil(e/2)
+        sh = 15 - ((e + 1) >> 1);  // ||x|| * 2^sh < 2^15
+        const float f = pow2f(sh);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xv[i] *= f;
+        ss *= f * f;
+      } else {
+        // far outside the usual range (or zero): scale from the largest element
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(xv[i]));
+        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+        int e = 0;
+        if (mx > 0.f) (void)frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
+        sh = 11 - e;                         // ||x|| * 2^sh < 2^14.5
+        ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          xv[i] = ldexpf(xv[i], sh);
+          ss = fmaf(xv[i], xv[i], ss);
         }
-        if constexpr (KEY) {
-          const float r = (n > 0.f) ? yh - sc[idx] : 0.f;
-          rs[j][v] = r;
-          rsq[vi] = r * r;
-          for (int p = 0; p < bits; ++p) {
-            const uint64_t mask = __ballot((idx >> p) & 1);
-            if (valid && (lane & 31) == 0) {
-              const uint32_t word = (lane == 0) ? static_cast<uint32_t>(mask)
-                                                : static_cast<uint32_t>(mask >> 32);
-              codes[((s * T + t) * (kD / 32) + j / 32) * bits + p] = word;
-            }
-          }
-        } else {
-          if (valid) {
-            const int pos = bits * (it * kVec + v);
-            const uint64_t f = static_cast<uint64_t>(idx);
-            if (pos < 64) {
-              vlo |= f << pos;
-              if (pos + bits > 64) vhi |= f >> (64 - pos);
-            } else {
-              vhi |= f << (pos - 64);
-            }
-          }
+        ss = sum8(ss);
+      }
+      if (sq == 0) {
+        const float nr = sqrtf(ss);
+        n_s[par][sv] = ldexpf(nr, -sh);
+        rinv_s[sv] = (ss > 0.f) ? kResScale / (kPiScale * nr) : 0.f;
+      }
+      uint32_t wh[8], wl[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const qhalf2 hh = {static_cast<_Float16>(xv[2 * i]), static_cast<_Float16>(xv[2 * i + 1])};
+        wh[i] = h2u(hh);
+        if constexpr (kSplitX) {
+          const qhalf2 ll = {static_cast<_Float16>(xv[2 * i] - static_cast<float>(hh[0])),
+                             static_cast<_Float16>(xv[2 * i + 1] - static_cast<float>(hh[1]))};
+          wl[i] = h2u(ll);
         }
       }
+      uint4* dh = reinterpret_cast<uint4*>(&xs[0][sv][16 * sq]);
+      dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+      dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+      if constexpr (kSplitX) {
+        uint4* dl = reinterpret_cast<uint4*>(&xs[kXP - 1][sv][16 * sq]);
+        dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+        dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+      }
+    }
+    __syncthreads();
+    load_raw(ns, nb, raw);  // next unit's input, in flight during the compute
 
+    // ---------------- rotation: acc = X Pi^T (x kPiScale, inputs scaled)
+    qfloatx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const qhalf8 ah = *reinterpret_cast<const qhalf8*>(&xs[0][atok][16 * c + 8 * h]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bph[c], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bpl[c], acc, 0, 0, 0);
+      if constexpr (kSplitX) {
+        const qhalf8 al = *reinterpret_cast<const qhalf8*>(&xs[kXP - 1][atok][16 * c + 8 * h]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bph[c], acc, 0, 0, 0);
+      }
+    }
+
+    // ---------------- quantize: acc[v] is token 16h + v, coordinate 32*wave + c32
+    float rv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 r4 = *reinterpret_cast<const float4*>(&rinv_s[16 * h + 4 * q]);
+      rv[4 * q] = r4.x;
+      rv[4 * q + 1] = r4.y;
+      rv[4 * q + 2] = r4.z;
+      rv[4 * q + 3] = r4.w;
+    }
+    uint32_t cw0 = 0, cw1 = 0;  // key code words: lane = token + 32 * (plane & 1)
+    uint32_t vlo = 0, vhi = 0;  // value fields of tokens 16h .. 16h+15 (bits BITS*v ..)
+    float rprev = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float y = acc[v] * rv[v];
+      uint64_t P[BITS];
+      float C;
+      int idx;
+      quant_one<BITS>(y, tab, P, C, idx);
       if constexpr (KEY) {
 #pragma unroll
-        for (int vi = 0; vi < 4; ++vi) {
-          const float sum = wave_sum(rsq[vi]);
-          if (lane == 0) red2[wave][vi] = sum;
-        }
-        __syncthreads();
-        if (tid < kVec) {
-          rho[tid] = sqrtf(red2[2 * (tid / 4)][tid % 4] + red2[2 * (tid / 4) + 1][tid % 4]);
-          const int64_t t = t0 + tid;
-          if (t < T) {
-            store_norm(norm, norm_dtype, s * T + t, nrm[tid]);
-            store_norm(rnorm, norm_dtype, s * T + t, nrm[tid] * rho[tid]);
+        for (int p = 0; p < BITS; ++p) {
+          const uint32_t lo = static_cast<uint32_t>(P[p]), hi = static_cast<uint32_t>(P[p] >> 32);
+          const int base = 32 * (p & 1);
+          if (p < 2) {
+            cw0 = writelane(lo, base + v, cw0);
+            cw0 = writelane(hi, base + 16 + v, cw0);
+          } else {
+            cw1 = writelane(lo, base + v, cw1);
+            cw1 = writelane(hi, base + 16 + v, cw1);
           }
         }
-        // z_i = sum_j S[i][j] r_j ; sign bit = [z >= 0]
-        const int i = j;
-        float z[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int jj = 0; jj < kD; ++jj) {
-          const float sv = ST[jj][i];
-          const float4 rv = *reinterpret_cast<const float4*>(&rs[jj][hv * 4]);
-          z[0] = fmaf(sv, rv.x, z[0]);
-          z[1] = fmaf(sv, rv.y, z[1]);
-          z[2] = fmaf(sv, rv.z, z[2]);
-          z[3] = fmaf(sv, rv.w, z[3]);
+        // residual x256 (for a zero vector y = 0 and the residual is unused:
+        // its signs and rnorm are fixed at the store)
+        const float r = y - C;
+        if (v & 1) {
+          // tokens (v-1, v) of coordinate 32*wave + c32: fp16 hi + lo
+          const qhalf2 hh = {static_cast<_Float16>(rprev), static_cast<_Float16>(r)};
+          const qhalf2 ll = {static_cast<_Float16>(rprev - static_cast<float>(hh[0])),
+                             static_cast<_Float16>(r - static_cast<float>(hh[1]))};
+          const int tk = 16 * h + v - 1, j = 32 * wave + c32;
+          rs[0][tk][j] = hh[0];
+          rs[0][tk + 1][j] = hh[1];
+          rs[1][tk][j] = ll[0];
+          rs[1][tk + 1][j] = ll[1];
         }
+        rprev = r;
+      } else {
+        const int sh = BITS * v;
+        const uint32_t u = static_cast<uint32_t>(idx);
+        if (sh < 32) vlo |= u << sh;
+        if (sh + BITS > 32) vhi |= (sh < 32) ? (u >> (32 - sh)) : (u << (sh - 32));
+      }
+    }
+
+    if constexpr (KEY) {
+      {
+        const int tk = lane & 31, p = lane >> 5;
+        if (tk < nvalid && p < BITS) {
+          uint32_t* dst = codes + ((s * T + t0 + tk) * 4 + wave) * BITS;
+          dst[p] = cw0;
+          if (p + 2 < BITS) dst[p + 2] = cw1;
+        }
+      }
+      __syncthreads();
+      // ---------------- sketch Z = R S^T (this wave's 32 sketch rows)
+      qfloatx16 z;
 #pragma unroll
-        for (int vi = 0; vi < 4; ++vi) {
-          const int64_t t = t0 + hv * 4 + vi;
-          const uint64_t mask = __ballot(z[vi] >= 0.f);
-          if (t < T && (lane & 31) == 0) {
-            const uint32_t word = (lane == 0) ? static_cast<uint32_t>(mask)
-                                              : static_cast<uint32_t>(mask >> 32);
-            signs[(s * T + t) * (kM / 32) + i / 32] = word;
-          }
+      for (int i = 0; i < 16; ++i) z[i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const qhalf8 ah = *reinterpret_cast<const qhalf8*>(&rs[0][atok][16 * c + 8 * h]);
+        const qhalf8 al = *reinterpret_cast<const qhalf8*>(&rs[1][atok][16 * c + 8 * h]);
+        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bsh[c], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bsl[c], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bsh[c], z, 0, 0, 0);
+      }
+      // ---------------- ||r||^2 over this wave's coordinates: diagonal of R R^T
+      // (16x16 tiles: A-row n of tile mt is token 16mt + n; k = 32*wave + 8*(lane/16) + e)
+      {
+        const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const qhalf8 gh = *reinterpret_cast<const qhalf8*>(&rs[0][16 * mt + n][32 * wave + 8 * g]);
+          const qhalf8 gl = *reinterpret_cast<const qhalf8*>(&rs[1][16 * mt + n][32 * wave + 8 * g]);
+          qfloatx4 d = {0.f, 0.f, 0.f, 0.f};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(gh, gh, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(gh, gl, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(gl, gh, d, 0, 0, 0);
+          // lane (g, n) holds rows 4g .. 4g+3 of column n: the diagonal when g = n/4
+          const int ii = n & 3;
+          const float dg = ii == 0 ? d[0] : ii == 1 ? d[1] : ii == 2 ? d[2] : d[3];
+          if (g == (n >> 2)) rho_s[par][wave][16 * mt + n] = dg;
+        }
+      }
+      uint32_t sw = 0;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint64_t Z = __ballot(z[v] >= 0.f);
+        sw = writelane(static_cast<uint32_t>(Z), v, sw);
+        sw = writelane(static_cast<uint32_t>(Z >> 32), 16 + v, sw);
+      }
+      if (lane < nvalid) {
+        // a zero vector has every sign bit set
+        if (n_s[par][lane] == 0.f) sw = 0xFFFFFFFFu;
+        signs[(s * T + t0 + lane) * 4 + wave] = sw;
+      }
+    } else {
+      // mask off the fields of padded tokens (zero vectors past the end of T)
+      const int nv = nvalid - 16 * h;  // valid tokens of this lane half
+      if (nv < 16) {
+        const int nbits = nv > 0 ? BITS * nv : 0;
+        const uint32_t mlo = nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u);
+        const uint32_t mhi = nbits <= 32 ? 0u : ((1u << (nbits - 32)) - 1u);
+        vlo &= mlo;
+        vhi &= mhi;
+      }
+      // lane half h holds record bits [16*BITS*h, 16*BITS*(h+1))
+      const int j = 32 * wave + c32;
+      uint32_t* dst = codes + ((s * nblk + blk) * kD + j) * BITS;
+      if constexpr (BITS == 1) {
+        const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
+        if (h == 0) dst[0] = vlo | (other << 16);
+      } else if constexpr (BITS == 2) {
+        dst[h] = vlo;
+      } else if constexpr (BITS == 3) {
+        const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
+        if (h == 0) {
+          dst[0] = vlo;
+          dst[1] = vhi | (other << 16);
+        } else {
+          dst[2] = (vlo >> 16) | (vhi << 16);
         }
       } else {
-        if (tid < kVec) {
-          const int64_t t = t0 + tid;
-          if (t < T) store_norm(norm, norm_dtype, s * T + t, nrm[tid]);
-        }
+        dst[2 * h] = vlo;
+        dst[2 * h + 1] = vhi;
       }
-      __syncthreads();
+      if (tid < nvalid) store_norm(norm, norm_dtype, s * T + t0 + tid, n_s[par][tid]);
     }
-    if constexpr (!KEY) {
-      const uint32_t rec[4] = {static_cast<uint32_t>(vlo), static_cast<uint32_t>(vlo >> 32),
-                               static_cast<uint32_t>(vhi), static_cast<uint32_t>(vhi >> 32)};
-      if (hv == 1) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) vw[j][p] = rec[p];
+    __syncthreads();  // LDS is restaged by the next unit
+    if constexpr (KEY) {
+      if (tid < nvalid) {
+        const float rho2 = rho_s[par][0][tid] + rho_s[par][1][tid] + rho_s[par][2][tid] + rho_s[par][3][tid];
+        const float nx = n_s[par][tid];
+        store_norm(norm, norm_dtype, s * T + t0 + tid, nx);
+        store_norm(rnorm, norm_dtype, s * T + t0 + tid, nx * (sqrtf(rho2) / kResScale));
       }
-      __syncthreads();
-      if (hv == 0) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          if (p < bits) codes[((s * nblk + blk) * kD + j) * bits + p] = rec[p] | vw[j][p];
-      }
-      __syncthreads();
     }
+    s = ns;
+    blk = nb;
   }
 }
 
@@ -199,24 +493,37 @@ static int device_cus() {
   return cus;
 }
 
+template <typename XT, bool KEY>
+static void launch_bits(dim3 grid, hipStream_t stream, const tq_tables& t, const void* x,
+                        const tq_packed& out) {
+#define TQ_QL(B)                                                                                    \
+  hipLaunchKernelGGL((quantize_mfma_kernel<XT, KEY, B>), grid, dim3(kQThreads), 0, stream, t.rot,  \
+                     t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), out.nseq, out.T,  \
+                     out.codes, out.signs, out.norm, out.rnorm, out.norm_dtype)
+  switch (t.bits) {
+    case 1: TQ_QL(1); break;
+    case 2: TQ_QL(2); break;
+    case 3: TQ_QL(3); break;
+    default: TQ_QL(4); break;
+  }
+#undef TQ_QL
+}
+
 hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,
                            hipStream_t stream) {
-  const int64_t nblk = (out.T + 31) / 32;
+  const int64_t nblk = (out.T + kUnit - 1) / kUnit;
   const int64_t units = out.nseq * nblk;
   if (units == 0) return hipSuccess;
-  const int64_t grid = units < device_cus() ? units : device_cus();
   const bool key = out.role == TQ_KEY;
-#define TQ_QLAUNCH(XT, KEYV)                                                                     \
-  hipLaunchKernelGGL((quantize_kernel<XT, KEYV>), dim3(static_cast<unsigned>(grid)),             \
-                     dim3(kQThreads), 0, stream, t.rot, t.sketch, t.centroids, t.bounds, t.bits, \
-                     static_cast<const XT*>(x), out.nseq, out.T, out.codes, out.signs, out.norm, \
-                     out.rnorm, out.norm_dtype)
+  const int64_t cap = (key ? 2 : 3) * static_cast<int64_t>(device_cus());
+  const dim3 grid(static_cast<unsigned>(units < cap ? units : cap));
   if (x_dtype == TQ_BF16) {
-    if (key) TQ_QLAUNCH(uint16_t, true); else TQ_QLAUNCH(uint16_t, false);
+    if (key) launch_bits<uint16_t, true>(grid, stream, t, x, out);
+    else launch_bits<uint16_t, false>(grid, stream, t, x, out);
   } else {
-    if (key) TQ_QLAUNCH(float, true); else TQ_QLAUNCH(float, false);
+    if (key) launch_bits<float, true>(grid, stream, t, x, out);
+    else launch_bits<float, false>(grid, stream, t, x, out);
   }
-#undef TQ_QLAUNCH
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-"""In-bounds check of the matrix-core fragment layout (16x16x32 fp16) and
-the DPP row shift that the decode kernel is written against."""
+"""In-bounds checks of the matrix-core fragment layouts (16x16x32 and
+32x32x16 fp16) and the DPP row shift that the kernels are written against."""
 
 import ctypes
 import os
@@ -33,3 +33,20 @@ def test_mfma_16x16x32_f16_layout_and_dpp_row_shift():
     # row_shl:4 within rows of 16 lanes: lane i receives lane i + 4 (rows end -> old value -1)
     want = np.array([(l + 4) if (l % 16) + 4 < 16 else -1 for l in range(64)])
     assert np.array_equal(got, want), got
+
+
+def test_mfma_32x32x16_f16_layout():
+    tq.lib()
+    L = ctypes.CDLL(os.path.join(os.path.dirname(tq._LIB_PATH), "libtq_probe.so"))
+    L.tq_probe_mfma_32x32x16.restype = ctypes.c_int
+    L.tq_probe_mfma_32x32x16.argtypes = [ctypes.c_void_p] * 4
+    rng = np.random.default_rng(1)
+    A = rng.integers(-3, 4, size=(32, 16)).astype(np.float16)
+    B = rng.integers(-3, 4, size=(16, 32)).astype(np.float16)
+    a, b = torch.tensor(A).cuda(), torch.tensor(B).cuda()
+    d = torch.zeros((32, 32), dtype=torch.float32, device="cuda")
+    assert L.tq_probe_mfma_32x32x16(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                    ctypes.c_void_p(d.data_ptr()),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), A.astype(np.float32) @ B.astype(np.float32))

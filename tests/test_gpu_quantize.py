@@ -85,6 +85,32 @@ def test_bf16_values_ragged_blocks(bits):
             assert rec >> (bits * tail) == 0
 
 
+def test_fp32_values_ragged():
+    w = inputs.WORKLOADS[1]
+    say("quantize fp32 values", w.name)
+    X = inputs.value_slice(w, 0, 0, device="cuda", T=2 * 77).reshape(2, 77, D).contiguous()
+    assert X.dtype == torch.float32
+    for bits in (2, 4):
+        p = _quantize_values(X, bits, "f32")
+        _check_values(X, p, bits, "f32")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_extreme_magnitudes(dtype):
+    """Per-vector power-of-two range scaling: vectors from 1e-30 to 1e30 (the
+    squares of the large ones overflow float32, the small ones' underflow)
+    quantize exactly as at unit scale."""
+    say("quantize extreme magnitudes", dtype)
+    g = torch.Generator().manual_seed(11)
+    scales = torch.tensor([1e-30, 1e-12, 1e-3, 1.0, 1e3, 1e12, 1e30], dtype=torch.float64)
+    X = torch.randn((len(scales), 40, D), generator=g, dtype=torch.float64) * scales[:, None, None]
+    X = X.to(dtype).to("cuda").contiguous()
+    p = _quantize_keys(X, 3, "f32")
+    _check_keys(X, p, 3, "f32")
+    pv = _quantize_values(X, 2, "f32")
+    _check_values(X, pv, 2, "f32")
+
+
 def test_zero_vectors_and_single_token():
     say("quantize zero vectors")
     X = torch.randn((3, 1, D), device="cuda")
