@@ -24,9 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
-FP32_VALU_PEAK_TFLOPS = 78.6    # 256 CU x 64 fp32 FMA lanes x 2 x 2.4 GHz (no packed fp32)
-FP32_MFMA_PEAK_TFLOPS = 157.3
-BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix cores, published
 
 
 def log(*a):
@@ -229,17 +227,23 @@ def main():
     qk_flops = nvec * (2 * d * d + 2 * m * d)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
+    # Roofline of the dominant kernel (key quantization).  Per key vector the
+    # method reads d bf16 elements and writes one packed record, and does
+    # 2 d^2 (rotation) + 2 m d (sketch) flops: 308 B against 65536 flop, so
+    # at the fp16 matrix-core peak it is bound by HBM.
     qsrc = os.path.join(ROOT, "kv_cache_vector_quantize_amd", "csrc", "quantize.hip")
-    kname = "quantize_kernel<bf16, key>"
-    achieved = qk_flops / (qk_ms * 1e-3) / 1e12
+    kname = f"quantize_mfma_kernel<bf16, key, {w.k_bits}>"
+    achieved = qk_bytes / (qk_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(qsrc, kname)
     roofline = {
         "kernel": kname,
-        "bound": "alu", "achieved": round(achieved, 3), "peak": FP32_VALU_PEAK_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4),
+        "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "algorithmic": {"flop_per_vector": 2 * d * d + 2 * m * d, "vectors_per_launch": nvec,
-                        "bytes_per_vector": d * 2 + kb},
+        "algorithmic": {"bytes_per_vector": d * 2 + kb, "vectors_per_launch": nvec,
+                        "flop_per_vector": 2 * d * d + 2 * m * d,
+                        "algorithmic_tflops": round(qk_flops / (qk_ms * 1e-3) / 1e12, 2),
+                        "fp16_mfma_peak_tflops": FP16_MFMA_PEAK_TFLOPS},
     }
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
     res = {

@@ -82,6 +82,24 @@ __device__ __forceinline__ void split_frag(const float* p, float sc, qhalf8& hi,
   lo = qu4(l[0], l[1], l[2], l[3]);
 }
 
+// fp16(a - hi.x), fp16(b - hi.y): the lo halves of an fp16 hi + lo split,
+// each from one mixed-precision fma (hi read as fp16, a and b as fp32)
+__device__ __forceinline__ qhalf2 split_lo(qhalf2 hi, float a, float b) {
+  uint32_t lo = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t h = h2u(hi);
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(h), "v"(a));
+  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(lo)
+      : "v"(h), "v"(b));
+#else
+  (void)hi;
+  (void)a;
+  (void)b;
+#endif
+  return __builtin_bit_cast(qhalf2, lo);
+}
+
 // Code table of one stream at the x256 scale: positive decision boundaries
 // bounds[L/2 .. L-2] and centroid magnitudes centroids[L/2 .. L-1].  The
 // codebooks are symmetric about 0.
@@ -239,18 +257,30 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     }
   };
 
-  RawX<XT> raw;
+  auto advance = [&](int64_t& us, int64_t& ub) {
+    us += step_s;
+    ub += step_b;
+    if (ub >= nblk) {
+      ub -= nblk;
+      ++us;
+    }
+  };
+
+  // input of the current unit and (bf16) of the next one: two units of
+  // loads in flight; fp32 input keeps one (its registers are twice as many)
+  constexpr bool kAhead2 = !kSplitX;
+  RawX<XT> raw, raw_next;
+  int64_t s1 = s, b1 = blk;
+  advance(s1, b1);
+  int64_t s2 = s1, b2 = b1;
+  advance(s2, b2);
   load_raw(s, blk, raw);
+  if constexpr (kAhead2) load_raw(s1, b1, raw_next);
 
   int par = 0;
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x, par ^= 1) {
     const int64_t t0 = blk * kUnit;
     const int nvalid = static_cast<int>((T - t0 < kUnit) ? T - t0 : kUnit);
-    int64_t ns = s + step_s, nb = blk + step_b;
-    if (nb >= nblk) {
-      nb -= nblk;
-      ++ns;
-    }
 
     // ---------------- stage: norms, power-of-two range scale, fp16 copy
     {
@@ -261,7 +291,11 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       for (int i = 0; i < 16; ++i) ss = fmaf(xv[i], xv[i], ss);
       ss = sum8(ss);
       int sh;
-      if (ss >= 0x1p-100f && ss <= 0x1p100f) {
+      if (ss >= 1.f && ss < 0x1p28f) {
+        // ||x|| in [1, 2^14): every element is below 2^14 and those that are
+        // not exact in fp16 (below 2^-17) are negligible against the norm
+        sh = 0;
+      } else if (ss >= 0x1p-100f && ss <= 0x1p100f) {
         int e;
         (void)frexpf(ss, &e);      // ss in [2^(e-1), 2^e): ||x|| < 2^ceil(e/2)
         sh = 15 - ((e + 1) >> 1);  // ||x|| * 2^sh < 2^15
@@ -291,7 +325,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       if (sq == 0) {
         const float nr = sqrtf(ss);
         n_s[par][sv] = ldexpf(nr, -sh);
-        rinv_s[sv] = (ss > 0.f) ? kResScale / (kPiScale * nr) : 0.f;
+        rinv_s[sv] = (ss > 0.f) ? (kResScale / kPiScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
       }
       uint32_t wh[8], wl[8];
 #pragma unroll
@@ -314,7 +348,12 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       }
     }
     __syncthreads();
-    load_raw(ns, nb, raw);  // next unit's input, in flight during the compute
+    if constexpr (kAhead2) {
+      raw = raw_next;
+      load_raw(s2, b2, raw_next);  // the unit after next, in flight during two units' compute
+    } else {
+      load_raw(s1, b1, raw);  // the next unit, in flight during this unit's compute
+    }
 
     // ---------------- rotation: acc = X Pi^T (x kPiScale, inputs scaled)
     qfloatx16 acc;
@@ -370,8 +409,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         if (v & 1) {
           // tokens (v-1, v) of coordinate 32*wave + c32: fp16 hi + lo
           const qhalf2 hh = {static_cast<_Float16>(rprev), static_cast<_Float16>(r)};
-          const qhalf2 ll = {static_cast<_Float16>(rprev - static_cast<float>(hh[0])),
-                             static_cast<_Float16>(r - static_cast<float>(hh[1]))};
+          const qhalf2 ll = split_lo(hh, rprev, r);
           const int tk = 16 * h + v - 1, j = 32 * wave + c32;
           rs[0][tk][j] = hh[0];
           rs[0][tk + 1][j] = hh[1];
@@ -423,7 +461,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
           d = __builtin_amdgcn_mfma_f32_16x16x32_f16(gl, gh, d, 0, 0, 0);
           // lane (g, n) holds rows 4g .. 4g+3 of column n: the diagonal when g = n/4
           const int ii = n & 3;
-          const float dg = ii == 0 ? d[0] : ii == 1 ? d[1] : ii == 2 ? d[2] : d[3];
+          const float dg = sel(ii & 2, sel(ii & 1, d[3], d[2]), sel(ii & 1, d[1], d[0]));
           if (g == (n >> 2)) rho_s[par][wave][16 * mt + n] = dg;
         }
       }
@@ -480,8 +518,11 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         store_norm(rnorm, norm_dtype, s * T + t0 + tid, nx * (sqrtf(rho2) / kResScale));
       }
     }
-    s = ns;
-    blk = nb;
+    s = s1;
+    blk = b1;
+    s1 = s2;
+    b1 = b2;
+    advance(s2, b2);
   }
 }
 
