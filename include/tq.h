@@ -41,8 +41,11 @@
  *                signs[s][t][m/32]        bit k of word w     = [z[s][t][32w+k] >= 0]
  *                norm[s][t]  = ||k||,  rnorm[s][t] = ||k|| * ||r||
  *   value stream codes[s][ceil(T/32)][d][bits]
- *                bit k of word (B,j,p) = bit p of idx[s][32B+k][j]; bits of
- *                tokens past T are 0.        norm[s][t] = ||v||
+ *                the `bits` words (B,j,0..bits-1) form one little-endian
+ *                record of 32*bits bits: token k of block B holds
+ *                idx[s][32B+k][j] in record bits [bits*k, bits*k+bits)
+ *                (a field may straddle two words); fields of tokens past
+ *                T are 0.                    norm[s][t] = ||v||
  *   idx = number of codebook boundaries <= the rotated, normalised coordinate.
  *   z = S r, r = Pi x/||x|| - centroid[idx] (rotated domain, unit scale).
  *   Norms are float32 or float16 (round to nearest even), per tq_packed.
