@@ -59,11 +59,14 @@ def traffic_from_profiles(kernel_src, kernel_name):
         return None
 
 
-def cpu_baseline(w, K, V, pk, pv, q, budget_s=12.0):
-    """The oracle, untouched, on a bounded sample of the same workload:
-    quantize chunks of keys and values (and pack them) until about
-    `budget_s` seconds have passed, plus one decode row over a full
-    sequence from the GPU's packed records.  BLAS pinned to one thread."""
+def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0):
+    """The oracle, untouched, on a bounded sample of the same workload.  Each
+    timed stage of the step gets a share of `budget_s`: quantize + pack chunks
+    of 32768 vectors, logits of one KV head's query group over chunks of its
+    packed keys, or one decode row over a whole sequence from the GPU's packed
+    records.  Every stage's oracle rate (bytes of the stage's algorithmic
+    traffic per second) then prices the whole step.  BLAS pinned to one
+    thread."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -72,51 +75,73 @@ def cpu_baseline(w, K, V, pk, pv, q, budget_s=12.0):
 
     d, m = w.d, w.m
     G, S = inputs.table_gaussians(d, m)
+    share = budget_s / len(stages)
+    notes, cpu_s = [], 0.0
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
         Pi = oracle.rotation_from_gaussian(G)
         ck, tk = oracle.lloyd_max(d, w.k_bits)
-        cv, tv = oracle.lloyd_max(d, w.v_bits)
-        setup_s = time.perf_counter() - t0
-        # decode of one (batch 0, head 0) row over all T tokens
-        kc = pk.codes[0].cpu().numpy().view(np.uint32)[None, None]
-        ks = pk.signs[0].cpu().numpy().view(np.uint32)[None, None]
-        kn = pk.norm[0].cpu().numpy().astype(np.float64)[None, None]
-        kr = pk.rnorm[0].cpu().numpy().astype(np.float64)[None, None]
-        vc = pv.codes[0].cpu().numpy().view(np.uint32)[None, None]
-        vn = pv.norm[0].cpu().numpy().astype(np.float64)[None, None]
-        qq = q[0:1, 0:1].float().double().cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.decode_from_records(qq, kc, ks, kn, kr, vc, vn, w.T, Pi, S, ck, cv)
-        dec_s = time.perf_counter() - t0
-        dec_bytes = w.T * (key_record_bytes(w.k_bits) + value_record_bytes(w.v_bits))
-        # quantize + pack chunks of 32768 keys and 32768 values
-        chunk, nvec, q_s = 32768, 0, 0.0
-        flat_k = K.reshape(-1, d)
-        flat_v = V.reshape(-1, d)
-        while q_s < budget_s and (nvec + chunk) <= flat_k.shape[0]:
-            xk = flat_k[nvec:nvec + chunk].float().double().cpu().numpy()
-            xv = flat_v[nvec:nvec + chunk].float().double().cpu().numpy()
-            t0 = time.perf_counter()
-            rk = oracle.quantize_keys(xk, Pi, S, ck, tk)
-            oracle.pack_key_codes(rk["idx"], w.k_bits)
-            oracle.pack_signs(rk["signs"])
-            oracle.round_norms(rk["norm"], w.norm_dtype)
-            oracle.round_norms(rk["rnorm"], w.norm_dtype)
-            rv = oracle.quantize_values(xv, Pi, cv, tv)
-            oracle.pack_value_codes(rv["idx"].reshape(1, chunk, d), w.v_bits)
-            oracle.round_norms(rv["norm"], w.norm_dtype)
-            q_s += time.perf_counter() - t0
-            nvec += chunk
-    q_bytes = nvec * (2 * w.d * 2 + key_record_bytes(w.k_bits) + value_record_bytes(w.v_bits))
-    total_s = q_s + dec_s
-    gbs = (q_bytes + dec_bytes) / total_s / 1e9
+        cv, tv = (oracle.lloyd_max(d, w.v_bits) if w.v_bits else (None, None))
+        for st in stages:
+            name = st["name"]
+            if name in ("quantize_k", "quantize_v"):
+                X = (K if name == "quantize_k" else V).reshape(-1, d)
+                chunk, n, t_s = 32768, 0, 0.0
+                while t_s < share and n + chunk <= X.shape[0]:
+                    x = X[n:n + chunk].float().double().cpu().numpy()
+                    t0 = time.perf_counter()
+                    if name == "quantize_k":
+                        r = oracle.quantize_keys(x, Pi, S, ck, tk)
+                        oracle.pack_key_codes(r["idx"], w.k_bits)
+                        oracle.pack_signs(r["signs"])
+                        oracle.round_norms(r["rnorm"], w.norm_dtype)
+                    else:
+                        r = oracle.quantize_values(x, Pi, cv, tv)
+                        oracle.pack_value_codes(r["idx"].reshape(1, chunk, d), w.v_bits)
+                    oracle.round_norms(r["norm"], w.norm_dtype)
+                    t_s += time.perf_counter() - t0
+                    n += chunk
+                sample_bytes = n * st["bytes"] / st["units"]
+                notes.append(f"{name}: {n} vectors in {t_s:.1f} s ({n / t_s / 1e6:.3f} Mvec/s)")
+            elif name == "logits":
+                G_ = w.Hq // w.Hkv
+                chunk, n, t_s = 4096, 0, 0.0
+                qq = q[0, :G_].float().double().cpu().numpy()
+                codes = pk.codes[0].cpu().numpy().view(np.uint32)
+                signs = pk.signs[0].cpu().numpy().view(np.uint32)
+                kn = pk.norm[0].cpu().numpy().astype(np.float64)
+                kr = pk.rnorm[0].cpu().numpy().astype(np.float64)
+                while t_s < share and n < w.T:
+                    c = min(chunk, w.T - n)
+                    t0 = time.perf_counter()
+                    for g in range(G_):
+                        oracle.key_logits_from_records(qq[g], codes[n:n + c], signs[n:n + c],
+                                                       kn[n:n + c], kr[n:n + c], Pi, S, ck)
+                    t_s += time.perf_counter() - t0
+                    n += c
+                sample_bytes = n * st["bytes"] / st["units"]
+                notes.append(f"logits: {G_} heads x {n} tokens in {t_s:.1f} s")
+            else:  # decode: one (batch 0, head 0) row over all T tokens
+                kc = pk.codes[0].cpu().numpy().view(np.uint32)[None, None]
+                ks = pk.signs[0].cpu().numpy().view(np.uint32)[None, None]
+                kn = pk.norm[0].cpu().numpy().astype(np.float64)[None, None]
+                kr = pk.rnorm[0].cpu().numpy().astype(np.float64)[None, None]
+                vc = pv.codes[0].cpu().numpy().view(np.uint32)[None, None]
+                vn = pv.norm[0].cpu().numpy().astype(np.float64)[None, None]
+                qq = q[0:1, 0:1].float().double().cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.decode_from_records(qq, kc, ks, kn, kr, vc, vn, w.T, Pi, S, ck, cv)
+                t_s = time.perf_counter() - t0
+                # one query head of B*Hq over one sequence of B*Hkv
+                sample_bytes = st["bytes"] / (w.B * w.Hq)
+                notes.append(f"decode: one query head over {w.T} tokens in {t_s:.1f} s")
+            st["cpu_rate"] = sample_bytes / t_s
+            cpu_s += t_s
+    total_bytes = sum(st["bytes"] for st in stages)
+    est_s = sum(st["bytes"] / st["cpu_rate"] for st in stages)
     return {
-        "value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle, 1 BLAS thread: quantize+pack {nvec} keys and {nvec} values "
-                   f"({q_s:.1f} s) and one decode row over all {w.T} tokens of a sequence "
-                   f"({dec_s:.1f} s); {nvec * 2 / q_s / 1e6:.3f} Mvec/s quantize, "
-                   f"{dec_bytes / dec_s / 1e9:.3f} GB/s decode; table setup {setup_s:.1f} s excluded"),
+        "value": round(total_bytes / est_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": ("fp64 NumPy oracle, 1 BLAS thread, " + f"{cpu_s:.1f} s of samples: " + "; ".join(notes)
+                   + "; each stage's sampled rate prices the whole step"),
         "cpu": _cpu_model(),
     }
 
@@ -136,7 +161,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload number (3 = batched quantize+decode)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload number 1-5 (default 3: batched quantize + decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter scaling)")
@@ -157,43 +183,75 @@ def main():
         build.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = inputs.WORKLOADS[args.config]
-    if not (w.decode and w.v_bits):
-        raise SystemExit("bench.py runs the quantize + decode workloads (3)")
     dev = "cuda"
     d, m = w.d, w.m
+    xb = 2 if w.x_dtype == "bf16" else 4
     log("workload", w.name)
     G, S = inputs.table_gaussians(d, m)
     tk = tq.make_tables(G, S, w.k_bits, dev)
-    tv = tq.make_tables(G, None, w.v_bits, dev)
+    tv = tq.make_tables(G, None, w.v_bits, dev) if w.v_bits else None
     t0 = time.perf_counter()
     K = inputs.keys(w, device=dev).reshape(w.nseq, w.T, d)
-    V = inputs.values(w, device=dev).reshape(w.nseq, w.T, d)
+    V = inputs.values(w, device=dev).reshape(w.nseq, w.T, d) if w.v_bits else None
     q = inputs.queries(w, device=dev).contiguous()
     pk = tq.alloc_packed(tq.TQ_KEY, tk, w.nseq, w.T, w.norm_dtype, dev)
-    pv = tq.alloc_packed(tq.TQ_VALUE, tv, w.nseq, w.T, w.norm_dtype, dev)
-    ws = torch.empty(tq.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.T, d, m), dtype=torch.uint8,
-                     device=dev)
-    out = torch.empty((w.B, w.Hq, d), dtype=torch.float32, device=dev)
+    pv = tq.alloc_packed(tq.TQ_VALUE, tv, w.nseq, w.T, w.norm_dtype, dev) if w.v_bits else None
+    nvec = w.nseq * w.T
+    nb = 2 if w.norm_dtype == "f16" else 4
+    kb = key_record_bytes(w.k_bits, d, m, nb)
+    vb = value_record_bytes(w.v_bits, d, nb) if w.v_bits else 0
+    qbytes = w.B * w.Hq * d * xb
+
+    # the stages of one step, in order, with their algorithmic bytes
+    stages = []
+    if w.quantize_timed:
+        stages.append({"name": "quantize_k", "bytes": nvec * (d * xb + kb), "units": nvec,
+                       "fn": lambda: tq.tq_quantize(tk, K, pk),
+                       "kernel": f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}>",
+                       "flop_per_unit": 2 * d * d + 2 * m * d})
+        if w.v_bits:
+            stages.append({"name": "quantize_v", "bytes": nvec * (d * xb + vb), "units": nvec,
+                           "fn": lambda: tq.tq_quantize(tv, V, pv),
+                           "kernel": f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}>",
+                           "flop_per_unit": 2 * d * d})
+    else:
+        tq.tq_quantize(tk, K, pk)
+        if w.v_bits:
+            tq.tq_quantize(tv, V, pv)
+    if w.logits:
+        logits = torch.empty((w.B, w.Hq, w.T), dtype=torch.float32, device=dev)
+        lws = torch.empty(max(tq.logits_workspace_bytes(w.B, w.Hq, d, m), 256), dtype=torch.uint8,
+                          device=dev)
+        stages.append({"name": "logits", "bytes": nvec * kb + w.B * w.Hq * w.T * 4 + qbytes,
+                       "units": nvec, "kernel": f"logits_kernel<{w.Hq // w.Hkv}>",
+                       "fn": lambda: tq.tq_attn_logits(tk, q, pk, w.B, w.Hq, w.Hkv, ws=lws, out=logits),
+                       "flop_per_unit": 2 * (w.Hq // w.Hkv) * (d + m)})
+    if w.decode:
+        ws = torch.empty(tq.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.T, d, m), dtype=torch.uint8,
+                         device=dev)
+        out = torch.empty((w.B, w.Hq, d), dtype=torch.float32, device=dev)
+        G_ = w.Hq // w.Hkv
+        stages.append({"name": "decode", "bytes": nvec * (kb + vb) + qbytes + w.B * w.Hq * d * 4,
+                       "units": nvec, "kernel": f"decode_mfma_kernel<{G_}, {w.k_bits}, {w.v_bits}>",
+                       "fn": lambda: tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv, ws=ws, out=out),
+                       "flop_per_unit": 2 * G_ * (2 * d + m)})
     torch.cuda.synchronize()
-    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; stages: {[st['name'] for st in stages]}")
+
+    ns = len(stages)
 
     def step(ev=None):
+        for i, st in enumerate(stages):
+            if ev is not None:
+                ev[i].record()
+            st["fn"]()
         if ev is not None:
-            ev[0].record()
-        tq.tq_quantize(tk, K, pk)
-        if ev is not None:
-            ev[1].record()
-        tq.tq_quantize(tv, V, pv)
-        if ev is not None:
-            ev[2].record()
-        tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv, ws=ws, out=out)
-        if ev is not None:
-            ev[3].record()
+            ev[ns].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -204,11 +262,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = start.elapsed_time(end) / args.steps
-    qk_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    qv_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): quantize K {qk_ms:.3f}, "
-        f"quantize V {qv_ms:.3f}, decode {dec_ms:.3f} ms")
+    for i, st in enumerate(stages):
+        st["ms"] = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+    log(f"step {ms_step:.3f} ms (wall {wall / args.steps * 1e3:.3f} ms): "
+        + ", ".join(f"{st['name']} {st['ms']:.3f} ms" for st in stages))
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -218,34 +275,40 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
 
-    nvec = w.nseq * w.T
-    kb, vb = key_record_bytes(w.k_bits), value_record_bytes(w.v_bits)
-    qk_bytes = nvec * (d * 2 + kb)
-    qv_bytes = nvec * (d * 2 + vb)
-    dec_bytes = nvec * (kb + vb) + w.B * w.Hq * d * (2 + 4)
-    step_bytes = qk_bytes + qv_bytes + dec_bytes
-    qk_flops = nvec * (2 * d * d + 2 * m * d)
+    step_bytes = sum(st["bytes"] for st in stages)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # Roofline of the dominant kernel (key quantization).  Per key vector the
-    # method reads d bf16 elements and writes one packed record, and does
-    # 2 d^2 (rotation) + 2 m d (sketch) flops: 308 B against 65536 flop, so
-    # at the fp16 matrix-core peak it is bound by HBM.
-    qsrc = os.path.join(ROOT, "kv_cache_vector_quantize_amd", "csrc", "quantize.hip")
-    kname = f"quantize_mfma_kernel<bf16, key, {w.k_bits}>"
-    achieved = qk_bytes / (qk_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(qsrc, kname)
+    # Roofline of the dominant kernel (the stage that takes longest).  Every
+    # stage is bound by HBM at its algorithmic work: a key vector moves 308 B
+    # (bf16 in, packed record out) against 65536 flop, a value 306 B against
+    # 32768, decode 102 B per (token, KV head) against 2G(2d+m) flop, so at
+    # the fp16 matrix-core peak all of them are bandwidth-bound.
+    dom = max(stages, key=lambda st: st["ms"])
+    src = {"quantize_k": "quantize.hip", "quantize_v": "quantize.hip", "logits": "attention.hip",
+           "decode": "decode.hip"}[dom["name"]]
+    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
     roofline = {
-        "kernel": kname,
+        "kernel": dom["kernel"],
         "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": traffic,
-        "algorithmic": {"bytes_per_vector": d * 2 + kb, "vectors_per_launch": nvec,
-                        "flop_per_vector": 2 * d * d + 2 * m * d,
-                        "algorithmic_tflops": round(qk_flops / (qk_ms * 1e-3) / 1e12, 2),
+        "traffic": traffic_from_profiles(os.path.join(ROOT, "kv_cache_vector_quantize_amd", "csrc", src),
+                                         dom["kernel"]),
+        "algorithmic": {"bytes_per_unit": round(dom["bytes"] / dom["units"], 2), "units_per_launch": dom["units"],
+                        "unit": "vector" if dom["name"].startswith("quantize") else "token of one KV head",
+                        "flop_per_unit": dom["flop_per_unit"],
+                        "algorithmic_tflops": round(dom["flop_per_unit"] * dom["units"] / (dom["ms"] * 1e-3) / 1e12, 2),
                         "fp16_mfma_peak_tflops": FP16_MFMA_PEAK_TFLOPS},
     }
-    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    stage_report = {st["name"]: {"ms": round(st["ms"], 4),
+                                 "gbs": round(st["bytes"] / (st["ms"] * 1e-3) / 1e9, 2),
+                                 "frac_hbm": round(st["bytes"] / (st["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    for st in stages}
+    for st in stages:
+        if st["name"].startswith("quantize"):
+            stage_report[st["name"]]["mvec_s"] = round(nvec / (st["ms"] * 1e-3) / 1e6, 2)
+        else:
+            stage_report[st["name"]]["qhead_tokens_per_s"] = round(w.B * w.Hq * w.T / (st["ms"] * 1e-3), 1)
+    inputs_desc = ("fp32" if w.x_dtype == "f32" else "bf16") + " K" + (", V" if w.v_bits else "") + ", Q"
     res = {
         "metric": "decode attn from packed KV: GB/s & % HBM peak; quantize Mvec/s",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -253,19 +316,16 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "d": d,
                    "k_bits": w.k_bits, "qjl_m": m, "v_bits": w.v_bits, "norms": w.norm_dtype,
-                   "inputs": "bf16 K, V, Q", "parallelism": "1 GPU"},
+                   "inputs": inputs_desc, "step": [st["name"] for st in stages],
+                   "parallelism": "1 GPU"},
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
-        "quantize_mvec_s": round(2 * nvec / ((qk_ms + qv_ms) * 1e-3) / 1e6, 2),
-        "quantize_k_ms": round(qk_ms, 4), "quantize_v_ms": round(qv_ms, 4),
-        "decode_ms": round(dec_ms, 4), "decode_gbs": round(dec_gbs, 2),
-        "decode_frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
-        "decode_qhead_tokens_per_s": round(w.B * w.Hq * w.T / (dec_ms * 1e-3), 1),
+        "stages": stage_report,
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded CPU sample")
-        res["cpu_baseline"] = cpu_baseline(w, K, V, pk, pv, q)
+        res["cpu_baseline"] = cpu_baseline(w, stages, K, V, pk, pv, q)
     print(json.dumps(res), flush=True)
 
 

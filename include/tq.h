@@ -167,6 +167,8 @@ size_t tq_logits_workspace(int B, int Hq, int d, int m);
  *   k        packed keys, nseq = B*Hkv, sequence index b*Hkv + g
  *   logits   out, [B][Hq][T] float32; query head h reads kv head h/(Hq/Hkv)
  *   ws       workspace of at least tq_logits_workspace(B, Hq, d, m) bytes
+ * Hq/Hkv must be 1, 2, 4, 8 or 16 (else TQ_EUNSUPPORTED); T < 2^28 and
+ * B*Hkv <= 65535 (else TQ_EUNSUPPORTED).
  */
 tq_status tq_attn_logits(const tq_tables *tk, const void *q, int q_dtype, int B, int Hq, int Hkv,
                          const tq_packed *k, float *logits, void *ws, size_t ws_bytes,

@@ -16,7 +16,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
 
-size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
 
 tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
 
@@ -103,6 +102,8 @@ tq_status tq_quantize(const tq_tables* t, const void* x, int x_dtype, const tq_p
   return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, stream));
 }
 
+size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
+
 size_t tq_logits_workspace(int B, int Hq, int d, int m) {
   if (B < 0 || Hq < 0 || d < 0 || m < 0) return 0;
   const size_t nh = static_cast<size_t>(B) * Hq;
@@ -124,11 +125,14 @@ tq_status tq_attn_logits(const tq_tables* tk, const void* q, int q_dtype, int B,
   if (B == 0 || k->T == 0) return TQ_OK;
   if (!ok_ptr(q) || !ok_ptr(logits) || !ok_ptr(ws)) return TQ_EINVAL;
   if (ws_bytes < tq_logits_workspace(B, Hq, tk->d, tk->m)) return TQ_EWORKSPACE;
+  if (k->T >= (static_cast<int64_t>(1) << 28)) return TQ_EUNSUPPORTED;  // 32-bit record offsets
   float* qr = static_cast<float*>(ws);
   float* u = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                       align256(static_cast<size_t>(B) * Hq * tk->d * sizeof(float)));
   hipError_t e = tq::launch_qprep(*tk, q, q_dtype, B * Hq, qr, u, stream);
   if (e != hipSuccess) return TQ_EHIP;
+  if (Hq / Hkv <= 8)  // matrix-core tiles; 16 heads per KV head take the vector-ALU kernel
+    return from_hip(tq::launch_logits_mfma(*tk, qr, u, B, Hq, Hkv, *k, logits, stream));
   return from_hip(tq::launch_logits(*tk, qr, u, B, Hq, Hkv, *k, logits, stream));
 }
 

@@ -8,9 +8,9 @@
 // combine kernel.  No pass dequantizes the cache to memory.
 //
 // Mapping onto gfx950 (wave64, v_mfma_f32_16x16x32_f16):
-//  * decode_prep (one wave per KV head) lays the G rotated queries out as
+//  * every workgroup lays the G rotated queries of its KV head out as
 //    matrix-core B fragments -- fp16 hi in columns [0,G), the fp16 residual
-//    in [G,2G) -- and builds the code tables once.
+//    in [G,2G) -- and builds its code tables in LDS from the codebooks.
 //  * one workgroup = 4 waves = one split of the context of one KV head;
 //    wave w owns 32-token blocks w, w+4, ... and keeps its own
 //    online-softmax state; the 4 states merge through LDS.
@@ -43,9 +43,6 @@ constexpr int kDD = 128;
 constexpr int kDecThreads = 256;
 constexpr int kMaxSplit = 2048;   // tokens staged per workgroup (LDS)
 constexpr float kTau = 8.0f;      // raise the reference max when a block exceeds it by 2^8
-constexpr size_t kLutBytes = 4096;
-constexpr int kSLutOff = 2048;    // byte offsets inside the table area
-constexpr int kVLutOff = 2064;
 
 __device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
@@ -76,74 +73,141 @@ __device__ __forceinline__ uint32_t pair_index(const uint32_t* p, int m) {
   return x;
 }
 
-// ------------------------------------------------------------ preparation
+// ------------------------------------------------------------ query operands
 // Per KV head s and lane (n = lane%16, g4 = lane/16), 12 B-fragments of 8 fp16:
-//  frag[s][0..7][lane]: centroid K-steps c' = 0..7.  The K slots hold the
-//    coordinates 32*g4 + 4c' + {0,1,0,1,2,3,2,3}: every coordinate twice, once
-//    against the hi and once against the lo half of its centroid.
-//  frag[s][8..11][lane]: sign K-steps c = 0..3, coordinates 32*g4 + 8c + i.
+//  bq[0..7]: centroid K-steps c' = 0..7.  The K slots hold the coordinates
+//    32*g4 + 4c' + {0,1,0,1,2,3,2,3}: every coordinate twice, once against
+//    the hi and once against the lo half of its centroid.
+//  bu[0..3]: sign K-steps c = 0..3, coordinates 32*g4 + 8c + i.
 // Columns n < G carry the fp16 value, G <= n < 2G its fp16 residual, the
 // rest zero.
-constexpr int kFragsPerSeq = 12;
 
+// Centroid and sign dots of one 16-token tile (tile 0 or 1 of a 32-token
+// block) for this lane's query-head column: lane (g4, n) gets, for rows
+// 4*g4 + i, the centroid dot <q', c[idx]> (cen) and the sign dot
+// <u, 2s - 1> (qj) of head n (n < G; the other lanes hold partial sums).
+// pw: the tile token's KB plane words of coordinate word g4; sw: its sign word.
+template <int G, int KB>
+__device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
+                                            const half8 (&bu)[4], const char* khi_b,
+                                            const char* klo_b, const char* slut_b, float (&cen)[4],
+                                            float (&qj)[4]) {
+  // nibble q of E / O: the 4-bit index of the coordinate pair (4q, 4q+1) /
+  // (4q+2, 4q+3); table entries are 4 bytes, so offset = nibble << 2
+  uint32_t E = 0, Od = 0;
+  if constexpr (KB == 2) {
+    E = (pw[0] & 0x33333333u) | ((pw[1] << 2) & 0xCCCCCCCCu);
+    Od = ((pw[0] >> 2) & 0x33333333u) | (pw[1] & 0xCCCCCCCCu);
+  }
+  const uint32_t sv0 = sw << 2, sv2 = sw >> 2, sv3 = sw >> 4;
+  floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    // coordinates 4c .. 4c+3 of word g4: A = (hi, lo) of pair (4c, 4c+1), then of (4c+2, 4c+3)
+    uint32_t offA, offB;
+    if constexpr (KB == 2) {
+      offA = (c == 0) ? (E << 2) & 0x3Cu : (E >> (4 * c - 2)) & 0x3Cu;
+      offB = (c == 0) ? (Od << 2) & 0x3Cu : (Od >> (4 * c - 2)) & 0x3Cu;
+    } else {
+      offA = pair_index<KB>(pw, 2 * c) << 2;
+      offB = pair_index<KB>(pw, 2 * c + 1) << 2;
+    }
+    const uint32_t a0 = *reinterpret_cast<const uint32_t*>(khi_b + offA);
+    const uint32_t a1 = *reinterpret_cast<const uint32_t*>(klo_b + offA);
+    const uint32_t a2 = *reinterpret_cast<const uint32_t*>(khi_b + offB);
+    const uint32_t a3 = *reinterpret_cast<const uint32_t*>(klo_b + offB);
+    accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a0, a1, a2, a3), bq[c], accC, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t as[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t ssrc = (q == 0) ? sv0 : (q == 1) ? sw : (q == 2) ? sv2 : sv3;
+      as[q] = *reinterpret_cast<const uint32_t*>(slut_b + ((ssrc >> (8 * c)) & 0xCu));
+    }
+    accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(as[0], as[1], as[2], as[3]), bu[c], accS, 0, 0, 0);
+  }
+  // the hi column n plus the lo column G + n
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cen[i] = accC[i] + row_shl<G>(accC[i]);
+    qj[i] = accS[i] + row_shl<G>(accS[i]);
+  }
+}
+
+// This lane's query fragments for KV head s, built from the rotated queries
+// (q' = Pi q, u = S q', one row of d floats per query head) in the layout
+// described above.
 template <int G>
-__global__ __launch_bounds__(64) void decode_prep_kernel(const float* __restrict__ qr,
-                                                         const float* __restrict__ u, int kb, int vb,
-                                                         const float* __restrict__ ck,
-                                                         const float* __restrict__ cv,
-                                                         uint4* __restrict__ frag,
-                                                         char* __restrict__ lut) {
-  const int lane = threadIdx.x, n = lane & 15, g4 = lane >> 4;
-  const int64_t s = blockIdx.x, h0 = s * G;
+__device__ __forceinline__ void query_frags(const float* __restrict__ qr, const float* __restrict__ u,
+                                            int64_t s, int lane, half8 (&bq)[8], half8 (&bu)[4]) {
+  const int n = lane & 15, g4 = lane >> 4;
   const bool hi_col = n < G, lo_col = (n >= G) && (n < 2 * G);
   const int g = hi_col ? n : (lo_col ? n - G : 0);
-  auto part = [&](const float* src, int j) -> _Float16 {
-    if (!(hi_col || lo_col)) return static_cast<_Float16>(0.f);
-    const float x = src[(h0 + g) * kDD + j];
+  const float* qg = qr + (s * G + g) * kDD;
+  const float* ug = u + (s * G + g) * kDD;
+  auto part = [&](float x) -> _Float16 {
     const _Float16 a = static_cast<_Float16>(x);
-    return hi_col ? a : static_cast<_Float16>(x - static_cast<float>(a));
+    if (hi_col) return a;
+    if (lo_col) return static_cast<_Float16>(x - static_cast<float>(a));
+    return static_cast<_Float16>(0.f);
   };
   constexpr int kSlot[8] = {0, 1, 0, 1, 2, 3, 2, 3};
+#pragma unroll
   for (int c = 0; c < 8; ++c) {
     _Float16 h[8];
-    for (int i = 0; i < 8; ++i) h[i] = part(qr, 32 * g4 + 4 * c + kSlot[i]);
-    frag[(s * kFragsPerSeq + c) * 64 + lane] =
-        make_uint4(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = part(qg[32 * g4 + 4 * c + kSlot[i]]);
+    bq[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
   }
+#pragma unroll
   for (int c = 0; c < 4; ++c) {
     _Float16 h[8];
-    for (int i = 0; i < 8; ++i) h[i] = part(u, 32 * g4 + 8 * c + i);
-    frag[(s * kFragsPerSeq + 8 + c) * 64 + lane] =
-        make_uint4(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = part(ug[32 * g4 + 8 * c + i]);
+    bu[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
   }
-  if (s != 0) return;
-  // key pair table: entry x -> (hi pair, lo pair) of the two coordinates' centroids
-  uint2* klut = reinterpret_cast<uint2*>(lut);
-  for (int x = lane; x < (1 << (2 * kb)); x += 64) {
+}
+
+// The workgroup's code tables in LDS, from the codebooks:
+//  khi[x] / klo[x]: fp16 hi / lo halves of the centroids of the coordinate
+//    pair whose 2*KB-bit index is x (bit 2p: plane p of the lower coordinate,
+//    bit 2p+1: plane p of the upper);
+//  slut[x]: the +-1 pair of two sign bits;
+//  vlut[x] (VB > 0): the value centroids of the token pair whose fields are
+//    x & (2^VB - 1) and x >> VB.
+template <int KB, int VB>
+__device__ __forceinline__ void build_tables(const float* __restrict__ ck, const float* __restrict__ cv,
+                                             uint32_t* khi, uint32_t* klo, uint32_t* slut,
+                                             uint32_t* vlut, int tid, int nthreads) {
+  for (int x = tid; x < (1 << (2 * KB)); x += nthreads) {
     int ia = 0, ib = 0;
-    for (int q = 0; q < kb; ++q) {
-      ia |= ((x >> (2 * q)) & 1) << q;
-      ib |= ((x >> (2 * q + 1)) & 1) << q;
+#pragma unroll
+    for (int p = 0; p < KB; ++p) {
+      ia |= ((x >> (2 * p)) & 1) << p;
+      ib |= ((x >> (2 * p + 1)) & 1) << p;
     }
     const float ca = ck[ia], cb = ck[ib];
     const _Float16 ha = static_cast<_Float16>(ca), hb = static_cast<_Float16>(cb);
-    klut[x] = make_uint2(h2u(ha, hb), h2u(static_cast<_Float16>(ca - static_cast<float>(ha)),
-                                          static_cast<_Float16>(cb - static_cast<float>(hb))));
+    khi[x] = h2u(ha, hb);
+    klo[x] = h2u(static_cast<_Float16>(ca - static_cast<float>(ha)),
+                 static_cast<_Float16>(cb - static_cast<float>(hb)));
   }
-  uint32_t* slut = reinterpret_cast<uint32_t*>(lut + kSLutOff);
-  if (lane < 4)
-    slut[lane] = h2u(static_cast<_Float16>((lane & 1) ? 1.f : -1.f),
-                     static_cast<_Float16>((lane & 2) ? 1.f : -1.f));
-  // value pair table: entry x -> (c[x & mask], c[x >> vb]) for tokens (2q, 2q+1)
-  uint32_t* vlut = reinterpret_cast<uint32_t*>(lut + kVLutOff);
-  for (int x = lane; x < (1 << (2 * vb)); x += 64)
-    vlut[x] = h2u(static_cast<_Float16>(cv[x & ((1 << vb) - 1)]), static_cast<_Float16>(cv[x >> vb]));
+  if (tid < 4)
+    slut[tid] = h2u(static_cast<_Float16>((tid & 1) ? 1.f : -1.f),
+                    static_cast<_Float16>((tid & 2) ? 1.f : -1.f));
+  if constexpr (VB > 0) {
+    for (int x = tid; x < (1 << (2 * VB)); x += nthreads)
+      vlut[x] = h2u(static_cast<_Float16>(cv[x & ((1 << VB) - 1)]), static_cast<_Float16>(cv[x >> VB]));
+  }
 }
 
 // ------------------------------------------------------------ the kernel
 template <int G, int KB, int VB>
 __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
-    const uint4* __restrict__ frag, const char* __restrict__ lut, int64_t T, int split_len,
+    const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
+    const float* __restrict__ cv, int64_t T, int split_len,
     const uint32_t* __restrict__ kcodes, const uint32_t* __restrict__ ksigns, const void* knorm,
     const void* krnorm, int knd, const uint32_t* __restrict__ vcodes, const void* vnorm, int vnd,
     float sl2, int nsplit, float* __restrict__ partials) {
@@ -183,13 +247,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
   const int ntok = t1 - t0;
   const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
 
-  for (int x = tid; x < KL; x += kDecThreads) {
-    const uint2 e = reinterpret_cast<const uint2*>(lut)[x];
-    khi[x] = e.x;
-    klo[x] = e.y;
-  }  // visible after the staging barrier below
-  if (tid < 4) slut[tid] = reinterpret_cast<const uint32_t*>(lut + kSLutOff)[tid];
-  for (int x = tid; x < VL; x += kDecThreads) vlut[x] = reinterpret_cast<const uint32_t*>(lut + kVLutOff)[x];
+  build_tables<KB, VB>(ck, cv, khi, klo, slut, vlut, tid, kDecThreads);  // visible after the barrier below
   float sigma;
   {
     const int64_t rec0 = s * T + t0;
@@ -216,10 +274,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
     for (int i = tid; i < nst; i += kDecThreads) nv_s[i] *= inv;
   }
   half8 bq[8], bu[4];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) bq[c] = __builtin_bit_cast(half8, frag[(s * kFragsPerSeq + c) * 64 + lane]);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) bu[c] = __builtin_bit_cast(half8, frag[(s * kFragsPerSeq + 8 + c) * 64 + lane]);
+  query_frags<G>(qr, u, s, lane, bq, bu);
   __syncthreads();
 
   floatx4 O[8];
@@ -284,50 +339,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
     float sv[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const uint32_t* pw = kw_c[tile];
-      // nibble q of E / O: the 4-bit index of the coordinate pair (4q, 4q+1) /
-      // (4q+2, 4q+3); table entries are 4 bytes, so offset = nibble << 2
-      uint32_t E = 0, Od = 0;
-      if constexpr (KB == 2) {
-        E = (pw[0] & 0x33333333u) | ((pw[1] << 2) & 0xCCCCCCCCu);
-        Od = ((pw[0] >> 2) & 0x33333333u) | (pw[1] & 0xCCCCCCCCu);
-      }
-      const uint32_t sw = sw_c[tile];
-      const uint32_t sv0 = sw << 2, sv2 = sw >> 2, sv3 = sw >> 4;
-      floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        // coordinates 4c .. 4c+3 of word g4: A = (hi, lo) of pair (4c, 4c+1), then of (4c+2, 4c+3)
-        uint32_t offA, offB;
-        if constexpr (KB == 2) {
-          offA = (c == 0) ? (E << 2) & 0x3Cu : (E >> (4 * c - 2)) & 0x3Cu;
-          offB = (c == 0) ? (Od << 2) & 0x3Cu : (Od >> (4 * c - 2)) & 0x3Cu;
-        } else {
-          offA = pair_index<KB>(pw, 2 * c) << 2;
-          offB = pair_index<KB>(pw, 2 * c + 1) << 2;
-        }
-        const uint32_t a0 = *reinterpret_cast<const uint32_t*>(khi_b + offA);
-        const uint32_t a1 = *reinterpret_cast<const uint32_t*>(klo_b + offA);
-        const uint32_t a2 = *reinterpret_cast<const uint32_t*>(khi_b + offB);
-        const uint32_t a3 = *reinterpret_cast<const uint32_t*>(klo_b + offB);
-        accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a0, a1, a2, a3), bq[c], accC, 0, 0, 0);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t as[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t ssrc = (q == 0) ? sv0 : (q == 1) ? sw : (q == 2) ? sv2 : sv3;
-          as[q] = *reinterpret_cast<const uint32_t*>(slut_b + ((ssrc >> (8 * c)) & 0xCu));
-        }
-        accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(as[0], as[1], as[2], as[3]), bu[c], accS, 0, 0, 0);
-      }
+      float cen[4], qj[4];
+      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, khi_b, klo_b, slut_b, cen, qj);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float cen = accC[i] + row_shl<G>(accC[i]);
-        const float qj = accS[i] + row_shl<G>(accS[i]);
         const int li = lb + 8 * g4 + 4 * tile + i;
-        float v = nk_s[li] * cen + rq_s[li] * qj;
+        float v = nk_s[li] * cen[i] + rq_s[li] * qj[i];
         if (!full && tb + (li - lb) >= Ti) v = -INFINITY;
         sv[4 * tile + i] = v;
       }
@@ -411,49 +428,161 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
   }
 }
 
+// ------------------------------------------------------------ logits only
+// Raw logits of the G query heads sharing KV head s (same page, Stage 2
+// closing paragraph): l_t = ||k_t|| <q', c[idx_t]> + sqrt(pi/2)/m ||r_t|| <u, 2 s_t - 1>
+// with ||r_t|| the stored ||k|| ||r^||.  One workgroup per (split, KV head),
+// the same tiles as decode; out[(s*G + g) * T + t].
+template <int G, int KB>
+__global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
+    const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
+    int64_t T, int split_len, const uint32_t* __restrict__ kcodes,
+    const uint32_t* __restrict__ ksigns, const void* knorm, const void* krnorm, int knd,
+    float* __restrict__ out) {
+  constexpr int KL = 1 << (2 * KB);
+  constexpr int kKhi = 0, kKlo = 1024, kSlu = 2048, kStage = 2064;
+  __shared__ __align__(16) char lds[kStage + 2 * kMaxSplit * 4];
+  uint32_t* khi = reinterpret_cast<uint32_t*>(lds + kKhi);
+  uint32_t* klo = reinterpret_cast<uint32_t*>(lds + kKlo);
+  uint32_t* slut = reinterpret_cast<uint32_t*>(lds + kSlu);
+  float* nk_s = reinterpret_cast<float*>(lds + kStage);   // ||k||
+  float* rq_s = nk_s + kMaxSplit;                          // sqrt(pi/2)/m ||k|| ||r||
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x;
+  const int64_t s = blockIdx.y;
+  const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
+  const int Ti = static_cast<int>(T);
+  const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
+  const int ntok = t1 - t0;
+  const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
+
+  build_tables<KB, 0>(ck, nullptr, khi, klo, slut, nullptr, tid, kDecThreads);
+  {
+    const int64_t rec0 = s * T + t0;
+    const int nst = (ntok + 31) & ~31;
+    for (int i = tid; i < nst; i += kDecThreads) {
+      float a = 0.f, b = 0.f;
+      if (i < ntok) {
+        a = load_norm(knorm, knd, rec0 + i);
+        b = load_norm(krnorm, knd, rec0 + i);
+      }
+      nk_s[i] = a;
+      rq_s[i] = qjl * b;
+    }
+  }
+  half8 bq[8], bu[4];
+  query_frags<G>(qr, u, s, lane, bq, bu);
+  __syncthreads();
+
+  const int nb_split = (ntok + 31) / 32;
+  const uint32_t* kc_seq = kcodes + s * T * 4 * KB;
+  const uint32_t* ks_seq = ksigns + s * T * 4;
+  const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
+  float* out_h = out + (s * G + (n < G ? n : 0)) * T;
+  const bool vec_ok = (Ti & 3) == 0;                  // 16-byte aligned output rows
+
+  uint32_t kw_n[2][KB], sw_n[2];
+  auto fetch = [&](int bb) {
+    const int tb = t0 + 32 * bb;
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      int t = tb + rowtok + 4 * tile;
+      t = (t < Ti) ? t : Ti - 1;                       // clamped: tail tokens are not stored
+      const uint32_t* kw = kc_seq + static_cast<uint32_t>(t * 4 + g4) * KB;
+#pragma unroll
+      for (int q = 0; q < KB; ++q) kw_n[tile][q] = kw[q];
+      sw_n[tile] = ks_seq[static_cast<uint32_t>(t * 4 + g4)];
+    }
+  };
+  if (wave < nb_split) fetch(wave);
+
+  for (int bb = wave; bb < nb_split; bb += 4) {
+    uint32_t kw_c[2][KB], sw_c[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+#pragma unroll
+      for (int q = 0; q < KB; ++q) kw_c[tile][q] = kw_n[tile][q];
+      sw_c[tile] = sw_n[tile];
+    }
+    if (bb + 4 < nb_split) fetch(bb + 4);              // in flight during this block
+    const int lb = 32 * bb;
+    const int tb = t0 + lb;
+    float lv[8];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      float cen[4], qj[4];
+      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, lds + kKhi, lds + kKlo, lds + kSlu, cen, qj);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int li = lb + 8 * g4 + 4 * tile + i;
+        lv[4 * tile + i] = nk_s[li] * cen[i] + rq_s[li] * qj[i];
+      }
+    }
+    // lane (g4, n < G): tokens tb + 8*g4 .. tb + 8*g4 + 7 of head n
+    if (n < G) {
+      const int tt = tb + 8 * g4;
+      if (vec_ok && tt + 8 <= Ti) {
+        float4* o4 = reinterpret_cast<float4*>(out_h + tt);
+        o4[0] = make_float4(lv[0], lv[1], lv[2], lv[3]);
+        o4[1] = make_float4(lv[4], lv[5], lv[6], lv[7]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (tt + k < Ti) out_h[tt + k] = lv[k];
+      }
+    }
+  }
+}
+
 // Merge the splits of one query head by log-sum-exp (base 2), then rotate
-// back once: out = Pi^T (acc / L).
-constexpr int kCombThreads = 256;
+// back once: out = Pi^T (acc / L).  512 threads: 4 groups of splits x 128
+// coordinates, then 4 groups of rows of Pi^T.
+constexpr int kCombThreads = 512;
 
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
     const float* __restrict__ rot, const float* __restrict__ partials, int nsplit,
     float* __restrict__ out) {
   __shared__ float red[kCombThreads];
-  __shared__ float half_acc[kDD];
+  __shared__ float part_acc[4][kDD];
+  __shared__ float part_l[4];
   __shared__ float a[kDD];
   const int64_t h = blockIdx.x;
   const int tid = threadIdx.x;
   const float* p = partials + h * nsplit * (kDD + 2);
   float M = -INFINITY;
   for (int sidx = tid; sidx < nsplit; sidx += kCombThreads) M = fmaxf(M, p[sidx * (kDD + 2) + kDD]);
-  red[tid] = M;
+  M = wave_max(M);
+  if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
-  for (int o = kCombThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
   M = red[0];
-  __syncthreads();
+#pragma unroll
+  for (int w = 1; w < kCombThreads / 64; ++w) M = fmaxf(M, red[w]);
   const int j = tid & (kDD - 1), part = tid >> 7;
   float acc = 0.f, L = 0.f;
-  int sidx = part;
-#pragma unroll 4
-  for (; sidx < nsplit; sidx += 2) {
+#pragma unroll 8
+  for (int sidx = part; sidx < nsplit; sidx += 4) {
     const float* q = p + sidx * (kDD + 2);
     const float w = __builtin_amdgcn_exp2f(q[kDD] - M);
     acc = fmaf(q[j], w, acc);
     L = fmaf(q[kDD + 1], w, L);
   }
-  if (part == 1) half_acc[j] = acc;
-  red[tid] = L;
-  __syncthreads();
-  if (part == 0) a[j] = (acc + half_acc[j]) / (red[j] + red[j + kDD]);
+  part_acc[part][j] = acc;
+  if (j == 0) part_l[part] = L;
   __syncthreads();
   if (tid < kDD) {
-    float o = 0.f;
-    for (int jj = 0; jj < kDD; ++jj) o = fmaf(rot[jj * kDD + tid], a[jj], o);
-    out[h * kDD + tid] = o;
+    const float Lt = part_l[0] + part_l[1] + part_l[2] + part_l[3];
+    a[tid] = (part_acc[0][tid] + part_acc[1][tid] + part_acc[2][tid] + part_acc[3][tid]) / Lt;
   }
+  __syncthreads();
+  // out[j] = sum_jj Pi[jj][j] a[jj]; group `part` takes rows jj = 32 part .. 32 part + 31
+  float o = 0.f;
+#pragma unroll 8
+  for (int jj = 32 * part; jj < 32 * part + 32; ++jj) o = fmaf(rot[jj * kDD + j], a[jj], o);
+  part_acc[part][j] = o;  // every thread read a[] only after the barrier above
+  __syncthreads();
+  if (tid < kDD) out[h * kDD + tid] = part_acc[0][tid] + part_acc[1][tid] + part_acc[2][tid] + part_acc[3][tid];
 }
 
 // Split length: enough workgroups for about two rounds of the chip at two
@@ -482,21 +611,19 @@ DecodeWorkspace decode_workspace_layout(int B, int Hq, int Hkv, int64_t T, int d
   const size_t nsplit = static_cast<size_t>((T + len - 1) / len);
   w.qr = 0;
   w.u = a256(nh * d * sizeof(float));
-  w.frag = w.u + a256(nh * m * sizeof(float));
-  w.lut = w.frag + a256(static_cast<size_t>(nseq) * kFragsPerSeq * 64 * sizeof(uint4));
-  w.partials = w.lut + kLutBytes;
+  w.partials = w.u + a256(nh * m * sizeof(float));
   w.total = w.partials + a256(nh * nsplit * (d + 2) * sizeof(float));
   return w;
 }
 
 template <int G, int KB>
-static void launch_vb(int vb, dim3 grid, hipStream_t stream, const uint4* frag, const char* lut,
-                      const tq_packed& k, const tq_packed& v, int len, float sl2, int nsplit,
-                      float* partials) {
+static void launch_vb(int vb, dim3 grid, hipStream_t stream, const tq_tables& tk,
+                      const tq_tables& tv, const float* qr, const float* u, const tq_packed& k,
+                      const tq_packed& v, int len, float sl2, int nsplit, float* partials) {
 #define TQ_DEC(VBV)                                                                            \
   hipLaunchKernelGGL((decode_mfma_kernel<G, KB, VBV>), grid, dim3(kDecThreads), 0, stream,     \
-                     frag, lut, k.T, len, k.codes, k.signs, k.norm, k.rnorm, k.norm_dtype,     \
-                     v.codes, v.norm, v.norm_dtype, sl2, nsplit, partials)
+                     qr, u, tk.centroids, tv.centroids, k.T, len, k.codes, k.signs, k.norm,    \
+                     k.rnorm, k.norm_dtype, v.codes, v.norm, v.norm_dtype, sl2, nsplit, partials)
   switch (vb) {
     case 1: TQ_DEC(1); break;
     case 2: TQ_DEC(2); break;
@@ -509,21 +636,13 @@ static void launch_vb(int vb, dim3 grid, hipStream_t stream, const uint4* frag, 
 template <int G>
 static hipError_t launch_g(const tq_tables& tk, const tq_tables& tv, const float* qr,
                            const float* u, int64_t nseq, const tq_packed& k, const tq_packed& v,
-                           float sl2, char* ws, const DecodeWorkspace& lay, int len, int nsplit,
-                           hipStream_t stream) {
-  uint4* frag = reinterpret_cast<uint4*>(ws + lay.frag);
-  char* lut = ws + lay.lut;
-  float* partials = reinterpret_cast<float*>(ws + lay.partials);
-  hipLaunchKernelGGL(decode_prep_kernel<G>, dim3(static_cast<unsigned>(nseq)), dim3(64), 0, stream,
-                     qr, u, tk.bits, tv.bits, tk.centroids, tv.centroids, frag, lut);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                           float sl2, float* partials, int len, int nsplit, hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(nsplit), static_cast<unsigned>(nseq));
   switch (tk.bits) {
-    case 1: launch_vb<G, 1>(tv.bits, grid, stream, frag, lut, k, v, len, sl2, nsplit, partials); break;
-    case 2: launch_vb<G, 2>(tv.bits, grid, stream, frag, lut, k, v, len, sl2, nsplit, partials); break;
-    case 3: launch_vb<G, 3>(tv.bits, grid, stream, frag, lut, k, v, len, sl2, nsplit, partials); break;
-    default: launch_vb<G, 4>(tv.bits, grid, stream, frag, lut, k, v, len, sl2, nsplit, partials); break;
+    case 1: launch_vb<G, 1>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
+    case 2: launch_vb<G, 2>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
+    case 3: launch_vb<G, 3>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
+    default: launch_vb<G, 4>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
   }
   return hipGetLastError();
 }
@@ -538,19 +657,53 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
   const int len = split_length(nseq, k.T);
   const int nsplit = static_cast<int>((k.T + len - 1) / len);
   const float sl2 = scale * 1.4426950408889634f;  // softmax in base 2
-  char* base = static_cast<char*>(ws);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.partials);
   hipError_t e;
   switch (G) {
-    case 1: e = launch_g<1>(tk, tv, qr, u, nseq, k, v, sl2, base, lay, len, nsplit, stream); break;
-    case 2: e = launch_g<2>(tk, tv, qr, u, nseq, k, v, sl2, base, lay, len, nsplit, stream); break;
-    case 4: e = launch_g<4>(tk, tv, qr, u, nseq, k, v, sl2, base, lay, len, nsplit, stream); break;
-    case 8: e = launch_g<8>(tk, tv, qr, u, nseq, k, v, sl2, base, lay, len, nsplit, stream); break;
+    case 1: e = launch_g<1>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
+    case 2: e = launch_g<2>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
+    case 4: e = launch_g<4>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
+    case 8: e = launch_g<8>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombThreads), 0, stream, tk.rot,
-                     reinterpret_cast<const float*>(base + lay.partials), nsplit, out);
+                     partials, nsplit, out);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_logits_g(const tq_tables& tk, const float* qr, const float* u,
+                                  int64_t nseq, const tq_packed& k, int len, int nsplit, float* out,
+                                  hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(nsplit), static_cast<unsigned>(nseq));
+#define TQ_LOG(KBV)                                                                                \
+  hipLaunchKernelGGL((logits_mfma_kernel<G, KBV>), grid, dim3(kDecThreads), 0, stream, qr, u,     \
+                     tk.centroids, k.T, len, k.codes, k.signs, k.norm, k.rnorm, k.norm_dtype, out)
+  switch (tk.bits) {
+    case 1: TQ_LOG(1); break;
+    case 2: TQ_LOG(2); break;
+    case 3: TQ_LOG(3); break;
+    default: TQ_LOG(4); break;
+  }
+#undef TQ_LOG
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
+                              int Hkv, const tq_packed& k, float* logits, hipStream_t stream) {
+  if (B == 0 || k.T == 0) return hipSuccess;
+  const int G = Hq / Hkv;
+  const int64_t nseq = static_cast<int64_t>(B) * Hkv;
+  const int len = split_length(nseq, k.T);
+  const int nsplit = static_cast<int>((k.T + len - 1) / len);
+  switch (G) {
+    case 1: return launch_logits_g<1>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 2: return launch_logits_g<2>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 4: return launch_logits_g<4>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 8: return launch_logits_g<8>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tq

@@ -23,16 +23,20 @@ hipError_t launch_qprep(const tq_tables& tk, const void* q, int q_dtype, int nh,
 hipError_t launch_logits(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
                          int Hkv, const tq_packed& k, float* logits, hipStream_t stream);
 
-// Split-K decode.  Workspace: rotated queries (qr, u), then per KV head the
-// query fragments in matrix-core lane order, the code tables, and one
+// Split-K decode.  Workspace: rotated queries (qr, u), then one
 // (acc[d], max, sum) partial per query head and split.
 struct DecodeWorkspace {
-  size_t qr, u, frag, lut, partials, total;
+  size_t qr, u, partials, total;
 };
 DecodeWorkspace decode_workspace_layout(int B, int Hq, int Hkv, int64_t T, int d, int m);
 hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* qr, const float* u,
                          int B, int Hq, int Hkv, const tq_packed& k, const tq_packed& v,
                          float scale, void* ws, const DecodeWorkspace& lay, float* out,
                          hipStream_t stream);
+
+// Logits through the decode tiles (G = Hq/Hkv in {1, 2, 4, 8}) from the
+// rotated queries.
+hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
+                              int Hkv, const tq_packed& k, float* logits, hipStream_t stream);
 
 }  // namespace tq

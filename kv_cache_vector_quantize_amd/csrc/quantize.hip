@@ -188,12 +188,50 @@ __device__ __forceinline__ void unpack_raw(const RawX<XT>& r, float* xv) {
   }
 }
 
-// sum over the 8 lanes that stage one token
+// DPP lane permutations within rows of 16 lanes: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1] and row_half_mirror (lane i <-> 7 - i within 8 lanes)
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// sum / max over the 8 lanes that stage one token (lanes 8k .. 8k+7)
 __device__ __forceinline__ float sum8(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
+  v += dpp<kDppSwap1>(v);
+  v += dpp<kDppSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
   return v;
+}
+
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, dpp<kDppSwap1>(v));
+  v = fmaxf(v, dpp<kDppSwap2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return v;
+}
+
+// sum of squares of the 16 staged elements; bf16 pairs go through v_dot2
+template <typename XT>
+__device__ __forceinline__ float sumsq16(const RawX<XT>& r, const float* xv) {
+  float ss = 0.f;
+  if constexpr (sizeof(XT) == 2) {
+    typedef __bf16 qbf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t u[4] = {r.w[i].x, r.w[i].y, r.w[i].z, r.w[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const qbf2 b = __builtin_bit_cast(qbf2, u[e]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(b, b, ss, false);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss = fmaf(xv[i], xv[i], ss);
+  }
+  return ss;
 }
 
 template <typename XT, bool KEY, int BITS>
@@ -204,9 +242,12 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     void* __restrict__ norm, void* __restrict__ rnorm, int norm_dtype) {
   constexpr bool kSplitX = sizeof(XT) == 4;  // fp32 input: stage hi and lo
   constexpr int kXP = kSplitX ? 2 : 1;
-  __shared__ __align__(16) _Float16 xs[kXP][kUnit][kRowH];
+  // keys: one staging buffer (the sketch barrier separates its reads from the
+  // next unit's writes); values: two, so that one barrier per unit suffices
+  constexpr int kXB = KEY ? 1 : 2;
+  __shared__ __align__(16) _Float16 xs[kXB][kXP][kUnit][kRowH];
   __shared__ __align__(16) _Float16 rs[KEY ? 2 : 1][KEY ? kUnit : 1][KEY ? kRowH : 8];
-  __shared__ __align__(16) float rinv_s[kUnit];   // kResScale / (kPiScale * ||scaled x||); 0 for x = 0
+  __shared__ __align__(16) float rinv_s[2][kUnit];  // kResScale / (kPiScale * ||scaled x||); 0 for x = 0
   __shared__ float n_s[2][kUnit];                 // ||x||, by unit parity
   __shared__ float rho_s[2][4][KEY ? kUnit : 1];  // per-wave sums of the residual squares (x256^2)
 
@@ -277,8 +318,22 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   load_raw(s, blk, raw);
   if constexpr (kAhead2) load_raw(s1, b1, raw_next);
 
+  // keys: the norms of a unit are stored after the next unit's first barrier
+  // (they need every wave's share of ||r||^2)
+  int64_t pend_base = 0;
+  int pend_n = 0;
+  auto store_key_norms = [&](int pp) {
+    if (tid < pend_n) {
+      const float rho2 = rho_s[pp][0][tid] + rho_s[pp][1][tid] + rho_s[pp][2][tid] + rho_s[pp][3][tid];
+      const float nx = n_s[pp][tid];
+      store_norm(norm, norm_dtype, pend_base + tid, nx);
+      store_norm(rnorm, norm_dtype, pend_base + tid, nx * (sqrtf(rho2) / kResScale));
+    }
+  };
+
   int par = 0;
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x, par ^= 1) {
+    const int xb = KEY ? 0 : par;
     const int64_t t0 = blk * kUnit;
     const int nvalid = static_cast<int>((T - t0 < kUnit) ? T - t0 : kUnit);
 
@@ -286,10 +341,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     {
       float xv[16];
       unpack_raw<XT>(raw, xv);
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ss = fmaf(xv[i], xv[i], ss);
-      ss = sum8(ss);
+      float ss = sum8(sumsq16<XT>(raw, xv));
       int sh;
       if (ss >= 1.f && ss < 0x1p28f) {
         // ||x|| in [1, 2^14): every element is below 2^14 and those that are
@@ -308,9 +360,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         float mx = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(xv[i]));
-        mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+        mx = max8(mx);
         int e = 0;
         if (mx > 0.f) (void)frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
         sh = 11 - e;                         // ||x|| * 2^sh < 2^14.5
@@ -325,7 +375,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       if (sq == 0) {
         const float nr = sqrtf(ss);
         n_s[par][sv] = ldexpf(nr, -sh);
-        rinv_s[sv] = (ss > 0.f) ? (kResScale / kPiScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
+        rinv_s[par][sv] = (ss > 0.f) ? (kResScale / kPiScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
       }
       uint32_t wh[8], wl[8];
 #pragma unroll
@@ -338,16 +388,17 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
           wl[i] = h2u(ll);
         }
       }
-      uint4* dh = reinterpret_cast<uint4*>(&xs[0][sv][16 * sq]);
+      uint4* dh = reinterpret_cast<uint4*>(&xs[xb][0][sv][16 * sq]);
       dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
       dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
       if constexpr (kSplitX) {
-        uint4* dl = reinterpret_cast<uint4*>(&xs[kXP - 1][sv][16 * sq]);
+        uint4* dl = reinterpret_cast<uint4*>(&xs[xb][kXP - 1][sv][16 * sq]);
         dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
         dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
       }
     }
     __syncthreads();
+    if constexpr (KEY) store_key_norms(par ^ 1);  // the previous unit's
     if constexpr (kAhead2) {
       raw = raw_next;
       load_raw(s2, b2, raw_next);  // the unit after next, in flight during two units' compute
@@ -361,11 +412,11 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const qhalf8 ah = *reinterpret_cast<const qhalf8*>(&xs[0][atok][16 * c + 8 * h]);
+      const qhalf8 ah = *reinterpret_cast<const qhalf8*>(&xs[xb][0][atok][16 * c + 8 * h]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bph[c], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bpl[c], acc, 0, 0, 0);
       if constexpr (kSplitX) {
-        const qhalf8 al = *reinterpret_cast<const qhalf8*>(&xs[kXP - 1][atok][16 * c + 8 * h]);
+        const qhalf8 al = *reinterpret_cast<const qhalf8*>(&xs[xb][kXP - 1][atok][16 * c + 8 * h]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bph[c], acc, 0, 0, 0);
       }
     }
@@ -374,7 +425,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     float rv[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 r4 = *reinterpret_cast<const float4*>(&rinv_s[16 * h + 4 * q]);
+      const float4 r4 = *reinterpret_cast<const float4*>(&rinv_s[par][16 * h + 4 * q]);
       rv[4 * q] = r4.x;
       rv[4 * q + 1] = r4.y;
       rv[4 * q + 2] = r4.z;
@@ -509,20 +560,19 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       }
       if (tid < nvalid) store_norm(norm, norm_dtype, s * T + t0 + tid, n_s[par][tid]);
     }
-    __syncthreads();  // LDS is restaged by the next unit
     if constexpr (KEY) {
-      if (tid < nvalid) {
-        const float rho2 = rho_s[par][0][tid] + rho_s[par][1][tid] + rho_s[par][2][tid] + rho_s[par][3][tid];
-        const float nx = n_s[par][tid];
-        store_norm(norm, norm_dtype, s * T + t0 + tid, nx);
-        store_norm(rnorm, norm_dtype, s * T + t0 + tid, nx * (sqrtf(rho2) / kResScale));
-      }
+      pend_base = s * T + t0;
+      pend_n = nvalid;
     }
     s = s1;
     blk = b1;
     s1 = s2;
     b1 = b2;
     advance(s2, b2);
+  }
+  if constexpr (KEY) {
+    __syncthreads();
+    store_key_norms(par ^ 1);
   }
 }
 

@@ -210,14 +210,20 @@ def tq_quantize(tables, x, out):
     return out
 
 
-def tq_attn_logits(tk, q, k, B, Hq, Hkv, ws=None):
+def logits_workspace_bytes(B, Hq, d, m):
+    return lib().tq_logits_workspace(B, Hq, d, m)
+
+
+def tq_attn_logits(tk, q, k, B, Hq, Hkv, ws=None, out=None):
     """q: [B, Hq, d]; k: packed keys with nseq = B*Hkv.  Returns [B, Hq, T] float32."""
     assert q.is_contiguous()
     L = lib()
     need = L.tq_logits_workspace(B, Hq, tk.d, tk.m)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    out = torch.empty((B, Hq, k.T), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, k.T), dtype=torch.float32, device=q.device)
+    assert out.is_contiguous() and out.numel() == B * Hq * k.T and out.dtype == torch.float32
     t, p = tk.c_struct(), k.c_struct()
     _check(L.tq_attn_logits(ctypes.byref(t), _ptr(q), _dtype_code(q), B, Hq, Hkv, ctypes.byref(p),
                             _ptr(out), _ptr(ws), ws.numel(), _stream(q.device)), "tq_attn_logits")

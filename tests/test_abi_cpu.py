@@ -45,12 +45,11 @@ def test_status_strings(L):
 def test_workspace_sizes(L):
     assert L.tq_logits_workspace(1, 32, 128, 128) == 32 * 128 * 4 * 2
     assert L.tq_logits_workspace(1, 1, 128, 0) == 512
-    # rotated queries (q', u: 2 x 64 heads x 128 floats), per KV head 12 KiB of
-    # matrix-core query fragments, 4 KiB of code tables, and one (d + 2)-float
+    # rotated queries (q', u: 2 x 64 heads x 128 floats) and one (d + 2)-float
     # partial per query head per split; T = 524288 over 8 KV heads is cut into
     # 256 splits of 2048 tokens.
     ws = L.tq_decode_workspace(1, 64, 8, 524288, 128, 128)
-    assert ws == 2 * 64 * 128 * 4 + 8 * 12288 + 4096 + 64 * 256 * 130 * 4
+    assert ws == 2 * 64 * 128 * 4 + 64 * 256 * 130 * 4
     assert L.tq_decode_workspace(-1, 1, 1, 1, 128, 128) == 0
 
 

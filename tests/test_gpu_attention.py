@@ -72,6 +72,23 @@ def test_logits_group_sizes_ragged(G):
     assert ok, (nbad, mx)
 
 
+@pytest.mark.parametrize("bits,T", [(1, 100), (2, 2049), (4, 64)])
+def test_logits_code_widths_and_splits(bits, T):
+    """Every key width through the matrix-core logits; T = 2049 leaves a
+    one-token last split, T = 100 a partial 32-token block."""
+    say("logits bits", bits, "T", T)
+    B, Hkv, G = 1, 4, 4
+    Hq = G * Hkv
+    X = (torch.randn((B * Hkv, T, D), device="cuda") * 2).to(torch.bfloat16)
+    tk, p = _keys(X.contiguous(), bits, "f16")
+    q = torch.randn((B, Hq, D), device="cuda")
+    got = tq.tq_attn_logits(tk, q, p, B, Hq, Hkv)
+    torch.cuda.synchronize()
+    ref = _oracle_logits(to64(q), p, bits, B, Hq, Hkv)
+    ok, nbad, mx = logits_close(got.cpu().numpy(), ref)
+    assert ok, (nbad, mx)
+
+
 def test_llama8b_logits_full_size():
     w = inputs.WORKLOADS[2]
     say("logits full size", w.name)
