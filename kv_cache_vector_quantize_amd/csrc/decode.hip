@@ -43,6 +43,9 @@ constexpr int kDD = 128;
 constexpr int kDecThreads = 256;
 constexpr int kMaxSplit = 2048;   // tokens staged per workgroup (LDS)
 constexpr float kTau = 8.0f;      // raise the reference max when a block exceeds it by 2^8
+// LDS code tables (built by build_tables): key tables at 0, sign table at
+// kS8Off, value table at kVluOff
+constexpr int kS8Off = 4096, kVluOff = 8192, kTabBytes = 9216;
 
 __device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
@@ -61,6 +64,15 @@ template <int SH>
 __device__ __forceinline__ float row_shl(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                                0x100 + SH, 0xf, 0xf, false));
+}
+
+// max over the 4 rows of 16 lanes (lanes n, n+16, n+32, n+48), in every lane:
+// v_permlane16_swap / v_permlane32_swap exchange rows without LDS
+__device__ __forceinline__ float max_over_rows(float v) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
 
 // 2b-bit index of the coordinate pair (2m, 2m+1) of one 32-coordinate word:
@@ -86,47 +98,44 @@ __device__ __forceinline__ uint32_t pair_index(const uint32_t* p, int m) {
 // block) for this lane's query-head column: lane (g4, n) gets, for rows
 // 4*g4 + i, the centroid dot <q', c[idx]> (cen) and the sign dot
 // <u, 2s - 1> (qj) of head n (n < G; the other lanes hold partial sums).
-// pw: the tile token's KB plane words of coordinate word g4; sw: its sign word.
+// pw: the tile token's KB plane words of coordinate word g4; sw: its sign
+// word; tab: the LDS tables of build_tables.
 template <int G, int KB>
 __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
-                                            const half8 (&bu)[4], const char* khi_b,
-                                            const char* klo_b, const char* slut_b, float (&cen)[4],
+                                            const half8 (&bu)[4], const char* tab, float (&cen)[4],
                                             float (&qj)[4]) {
-  // nibble q of E / O: the 4-bit index of the coordinate pair (4q, 4q+1) /
-  // (4q+2, 4q+3); table entries are 4 bytes, so offset = nibble << 2
-  uint32_t E = 0, Od = 0;
-  if constexpr (KB == 2) {
-    E = (pw[0] & 0x33333333u) | ((pw[1] << 2) & 0xCCCCCCCCu);
-    Od = ((pw[0] >> 2) & 0x33333333u) | (pw[1] & 0xCCCCCCCCu);
-  }
-  const uint32_t sv0 = sw << 2, sv2 = sw >> 2, sv3 = sw >> 4;
   floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KB == 2) {
+    // byte k of E / O: the quad-table index of coordinates 8k .. 8k+3 /
+    // 8k+4 .. 8k+7 (plane-0 nibble | plane-1 nibble << 4)
+    const uint32_t E = (pw[0] & 0x0F0F0F0Fu) | ((pw[1] & 0x0F0F0F0Fu) << 4);
+    const uint32_t O = ((pw[0] >> 4) & 0x0F0F0F0Fu) | (pw[1] & 0xF0F0F0F0u);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    // coordinates 4c .. 4c+3 of word g4: A = (hi, lo) of pair (4c, 4c+1), then of (4c+2, 4c+3)
-    uint32_t offA, offB;
-    if constexpr (KB == 2) {
-      offA = (c == 0) ? (E << 2) & 0x3Cu : (E >> (4 * c - 2)) & 0x3Cu;
-      offB = (c == 0) ? (Od << 2) & 0x3Cu : (Od >> (4 * c - 2)) & 0x3Cu;
-    } else {
-      offA = pair_index<KB>(pw, 2 * c) << 2;
-      offB = pair_index<KB>(pw, 2 * c + 1) << 2;
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t x = ((c & 1) ? O : E) >> (8 * (c >> 1)) & 0xFFu;
+      const uint4 a = *reinterpret_cast<const uint4*>(tab + 16 * x);
+      accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a.x, a.y, a.z, a.w), bq[c], accC, 0, 0, 0);
     }
-    const uint32_t a0 = *reinterpret_cast<const uint32_t*>(khi_b + offA);
-    const uint32_t a1 = *reinterpret_cast<const uint32_t*>(klo_b + offA);
-    const uint32_t a2 = *reinterpret_cast<const uint32_t*>(khi_b + offB);
-    const uint32_t a3 = *reinterpret_cast<const uint32_t*>(klo_b + offB);
-    accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a0, a1, a2, a3), bq[c], accC, 0, 0, 0);
+  } else {
+    const char* khi_b = tab;
+    const char* klo_b = tab + 1024;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // coordinates 4c .. 4c+3 of word g4: A = (hi, lo) of pair (4c, 4c+1), then of (4c+2, 4c+3)
+      const uint32_t offA = pair_index<KB>(pw, 2 * c) << 2;
+      const uint32_t offB = pair_index<KB>(pw, 2 * c + 1) << 2;
+      const uint32_t a0 = *reinterpret_cast<const uint32_t*>(khi_b + offA);
+      const uint32_t a1 = *reinterpret_cast<const uint32_t*>(klo_b + offA);
+      const uint32_t a2 = *reinterpret_cast<const uint32_t*>(khi_b + offB);
+      const uint32_t a3 = *reinterpret_cast<const uint32_t*>(klo_b + offB);
+      accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a0, a1, a2, a3), bq[c], accC, 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    uint32_t as[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t ssrc = (q == 0) ? sv0 : (q == 1) ? sw : (q == 2) ? sv2 : sv3;
-      as[q] = *reinterpret_cast<const uint32_t*>(slut_b + ((ssrc >> (8 * c)) & 0xCu));
-    }
-    accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(as[0], as[1], as[2], as[3]), bu[c], accS, 0, 0, 0);
+    // sign K-step c: coordinates 8c .. 8c+7 of word g4 = byte c of the sign word
+    const uint4 a = *reinterpret_cast<const uint4*>(tab + kS8Off + 16 * ((sw >> (8 * c)) & 0xFFu));
+    accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a.x, a.y, a.z, a.w), bu[c], accS, 0, 0, 0);
   }
   // the hi column n plus the lo column G + n
 #pragma unroll
@@ -170,34 +179,62 @@ __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const 
   }
 }
 
-// The workgroup's code tables in LDS, from the codebooks:
-//  khi[x] / klo[x]: fp16 hi / lo halves of the centroids of the coordinate
-//    pair whose 2*KB-bit index is x (bit 2p: plane p of the lower coordinate,
-//    bit 2p+1: plane p of the upper);
-//  slut[x]: the +-1 pair of two sign bits;
-//  vlut[x] (VB > 0): the value centroids of the token pair whose fields are
-//    x & (2^VB - 1) and x >> VB.
+// The workgroup's code tables in LDS (kTabBytes at the start of its LDS),
+// built from the codebooks:
+//  * 2-bit keys: entry x of the quad table (uint4 at 16x) holds the centroids
+//    of 4 consecutive coordinates whose plane-0 bits are x & 15 and plane-1
+//    bits x >> 4, as {hi(c0,c1), lo(c0,c1), hi(c2,c3), lo(c2,c3)} -- the
+//    order of a centroid K-step's slots;
+//  * other widths: pair tables khi[x] / klo[x] (uint32 at 4x and 1024 + 4x)
+//    with the fp16 hi / lo halves of the centroids of a coordinate pair whose
+//    2*KB-bit index is x (bit 2p: plane p of the lower coordinate, bit 2p+1:
+//    plane p of the upper);
+//  * at kS8Off, entry x (uint4): the +-1 values of 8 sign bits x, as fp16;
+//  * at kVluOff (VB > 0), vlut[x]: the value centroids of the token pair
+//    whose fields are x & (2^VB - 1) and x >> VB.
 template <int KB, int VB>
 __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const float* __restrict__ cv,
-                                             uint32_t* khi, uint32_t* klo, uint32_t* slut,
-                                             uint32_t* vlut, int tid, int nthreads) {
-  for (int x = tid; x < (1 << (2 * KB)); x += nthreads) {
-    int ia = 0, ib = 0;
+                                             char* tab, int tid, int nthreads) {
+  auto hilo = [&](float c, _Float16& h, _Float16& l) {
+    h = static_cast<_Float16>(c);
+    l = static_cast<_Float16>(c - static_cast<float>(h));
+  };
+  if constexpr (KB == 2) {
+    uint4* quad = reinterpret_cast<uint4*>(tab);
+    for (int x = tid; x < 256; x += nthreads) {
+      _Float16 h[4], l[4];
 #pragma unroll
-    for (int p = 0; p < KB; ++p) {
-      ia |= ((x >> (2 * p)) & 1) << p;
-      ib |= ((x >> (2 * p + 1)) & 1) << p;
+      for (int i = 0; i < 4; ++i) hilo(ck[((x >> i) & 1) | (((x >> (4 + i)) & 1) << 1)], h[i], l[i]);
+      quad[x] = make_uint4(h2u(h[0], h[1]), h2u(l[0], l[1]), h2u(h[2], h[3]), h2u(l[2], l[3]));
     }
-    const float ca = ck[ia], cb = ck[ib];
-    const _Float16 ha = static_cast<_Float16>(ca), hb = static_cast<_Float16>(cb);
-    khi[x] = h2u(ha, hb);
-    klo[x] = h2u(static_cast<_Float16>(ca - static_cast<float>(ha)),
-                 static_cast<_Float16>(cb - static_cast<float>(hb)));
+  } else {
+    uint32_t* khi = reinterpret_cast<uint32_t*>(tab);
+    uint32_t* klo = reinterpret_cast<uint32_t*>(tab + 1024);
+    for (int x = tid; x < (1 << (2 * KB)); x += nthreads) {
+      int ia = 0, ib = 0;
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        ia |= ((x >> (2 * p)) & 1) << p;
+        ib |= ((x >> (2 * p + 1)) & 1) << p;
+      }
+      _Float16 ha, la, hb, lb;
+      hilo(ck[ia], ha, la);
+      hilo(ck[ib], hb, lb);
+      khi[x] = h2u(ha, hb);
+      klo[x] = h2u(la, lb);
+    }
   }
-  if (tid < 4)
-    slut[tid] = h2u(static_cast<_Float16>((tid & 1) ? 1.f : -1.f),
-                    static_cast<_Float16>((tid & 2) ? 1.f : -1.f));
+  uint4* s8 = reinterpret_cast<uint4*>(tab + kS8Off);
+  for (int x = tid; x < 256; x += nthreads) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = h2u(static_cast<_Float16>(((x >> (2 * i)) & 1) ? 1.f : -1.f),
+                 static_cast<_Float16>(((x >> (2 * i + 1)) & 1) ? 1.f : -1.f));
+    s8[x] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
   if constexpr (VB > 0) {
+    uint32_t* vlut = reinterpret_cast<uint32_t*>(tab + kVluOff);
     for (int x = tid; x < (1 << (2 * VB)); x += nthreads)
       vlut[x] = h2u(static_cast<_Float16>(cv[x & ((1 << VB) - 1)]), static_cast<_Float16>(cv[x >> VB]));
   }
@@ -205,13 +242,12 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const
 
 // ------------------------------------------------------------ the kernel
 template <int G, int KB, int VB>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
+__global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
     const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
     const float* __restrict__ cv, int64_t T, int split_len,
     const uint32_t* __restrict__ kcodes, const uint32_t* __restrict__ ksigns, const void* knorm,
     const void* krnorm, int knd, const uint32_t* __restrict__ vcodes, const void* vnorm, int vnd,
     float sl2, int nsplit, float* __restrict__ partials) {
-  constexpr int KL = 1 << (2 * KB);
   constexpr int VL = 1 << (2 * VB);
   // One LDS buffer with a fixed layout: the code tables first (small
   // offsets fold into the ds_read instructions; the hi and lo key tables sit
@@ -219,15 +255,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
   // matrix-core operand registers), then the staged norms of the split.
   // After the main loop the staging bytes hold the four waves' softmax
   // states for the merge.
-  constexpr int kKhi = 0, kKlo = 1024, kSlu = 2048, kVlu = 2064, kStage = 3104;
+  constexpr int kStage = kTabBytes;
   constexpr int kStageBytes = kMaxSplit * 12;
   constexpr int kMergeBytes = (2 * 4 * 16 + 4 * G * kDD + 4) * 4;
   constexpr int kRed = kStage + (kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes);
   __shared__ __align__(16) char lds[kRed + 16];
-  uint32_t* khi = reinterpret_cast<uint32_t*>(lds + kKhi);
-  uint32_t* klo = reinterpret_cast<uint32_t*>(lds + kKlo);
-  uint32_t* slut = reinterpret_cast<uint32_t*>(lds + kSlu);
-  uint32_t* vlut = reinterpret_cast<uint32_t*>(lds + kVlu);
+  const uint32_t* vlut = reinterpret_cast<const uint32_t*>(lds + kVluOff);
   float* nk_s = reinterpret_cast<float*>(lds + kStage);   // ||k|| * scale * log2(e)
   float* rq_s = nk_s + kMaxSplit;          // sqrt(pi/2)/m ||k|| ||r|| * scale * log2(e)
   float* nv_s = rq_s + kMaxSplit;          // ||v|| / sigma, sigma = the split's largest ||v||
@@ -247,7 +280,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
   const int ntok = t1 - t0;
   const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
 
-  build_tables<KB, VB>(ck, cv, khi, klo, slut, vlut, tid, kDecThreads);  // visible after the barrier below
+  build_tables<KB, VB>(ck, cv, lds, tid, kDecThreads);  // visible after the barrier below
   float sigma;
   {
     const int64_t rec0 = s * T + t0;
@@ -289,11 +322,12 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
   const uint32_t* vc_seq = vcodes + s * nblk * kDD * VB;
   const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
   const int vbit0 = 8 * VB * g4;                       // this lane group's 8 value fields
+  // the lane group's fields span at most two record words: load the pair
+  // (vw0, vw0 + 1) that holds them (one 8-byte load; vw0 <= VB - 2 keeps it
+  // inside the record) and funnel-shift them out
   const int vwlo = vbit0 >> 5, vsh = vbit0 & 31;
-  const int vwhi = (vwlo + 1 < VB) ? vwlo + 1 : VB - 1;
-  const char* khi_b = lds + kKhi;
-  const char* klo_b = lds + kKlo;
-  const char* slut_b = lds + kSlu;
+  const int vw0 = (VB >= 2 && vwlo > VB - 2) ? VB - 2 : vwlo;
+  const bool vhi_only = vwlo > vw0;                    // fields lie in the upper word
 
   // this wave's next block: key plane words and the sign word of both tiles
   uint32_t kw_n[2][KB], sw_n[2];
@@ -326,8 +360,15 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
       const uint32_t* vb_blk = vc_seq + static_cast<uint32_t>(((t0 >> 5) + bb) * kDD + n) * VB;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        vw_c[nt][0] = vb_blk[16 * nt * VB + vwlo];
-        vw_c[nt][1] = vb_blk[16 * nt * VB + vwhi];
+        if constexpr (VB >= 2) {
+          typedef uint2 __attribute__((aligned(4))) uint2_a4;  // record words are 4-byte aligned
+          const uint2 w2 = *reinterpret_cast<const uint2_a4*>(vb_blk + 16 * nt * VB + vw0);
+          vw_c[nt][0] = w2.x;
+          vw_c[nt][1] = w2.y;
+        } else {
+          vw_c[nt][0] = vb_blk[16 * nt * VB];
+          vw_c[nt][1] = 0u;
+        }
       }
     }
     if (bb + 4 < nb_split) fetch(bb + 4);              // in flight during this block
@@ -340,20 +381,23 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       float cen[4], qj[4];
-      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, khi_b, klo_b, slut_b, cen, qj);
+      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, lds, cen, qj);
+      const int l0 = lb + 8 * g4 + 4 * tile;
+      const float4 nk4 = *reinterpret_cast<const float4*>(&nk_s[l0]);
+      const float4 rq4 = *reinterpret_cast<const float4*>(&rq_s[l0]);
+      const float nk[4] = {nk4.x, nk4.y, nk4.z, nk4.w}, rq[4] = {rq4.x, rq4.y, rq4.z, rq4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int li = lb + 8 * g4 + 4 * tile + i;
-        float v = nk_s[li] * cen[i] + rq_s[li] * qj[i];
-        if (!full && tb + (li - lb) >= Ti) v = -INFINITY;
-        sv[4 * tile + i] = v;
+      for (int i = 0; i < 4; ++i) sv[4 * tile + i] = nk[i] * cen[i] + rq[i] * qj[i];
+      if (!full) {  // the context's last, partial block: tokens past T get no weight
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tb + (l0 + i - lb) >= Ti) sv[4 * tile + i] = -INFINITY;
       }
     }
     // ---------------- online softmax, base 2
     float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = max_over_rows(bm);
     if (__ballot(bm > m_ref + kTau)) {
       const float m_new = fmaxf(m_ref, bm);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first block
@@ -381,7 +425,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(
     }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const uint32_t X = __builtin_amdgcn_alignbit(vw_c[nt][1], vw_c[nt][0], vsh);
+      const uint32_t X = vhi_only ? (vw_c[nt][1] >> vsh)
+                                  : __builtin_amdgcn_alignbit(vw_c[nt][1], vw_c[nt][0], vsh);
       uint32_t bw[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) bw[q] = vlut[(X >> (2 * VB * q)) & (VL - 1)];
@@ -439,12 +484,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
     int64_t T, int split_len, const uint32_t* __restrict__ kcodes,
     const uint32_t* __restrict__ ksigns, const void* knorm, const void* krnorm, int knd,
     float* __restrict__ out) {
-  constexpr int KL = 1 << (2 * KB);
-  constexpr int kKhi = 0, kKlo = 1024, kSlu = 2048, kStage = 2064;
+  constexpr int kStage = kTabBytes;
   __shared__ __align__(16) char lds[kStage + 2 * kMaxSplit * 4];
-  uint32_t* khi = reinterpret_cast<uint32_t*>(lds + kKhi);
-  uint32_t* klo = reinterpret_cast<uint32_t*>(lds + kKlo);
-  uint32_t* slut = reinterpret_cast<uint32_t*>(lds + kSlu);
   float* nk_s = reinterpret_cast<float*>(lds + kStage);   // ||k||
   float* rq_s = nk_s + kMaxSplit;                          // sqrt(pi/2)/m ||k|| ||r||
 
@@ -458,7 +499,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
   const int ntok = t1 - t0;
   const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
 
-  build_tables<KB, 0>(ck, nullptr, khi, klo, slut, nullptr, tid, kDecThreads);
+  build_tables<KB, 0>(ck, nullptr, lds, tid, kDecThreads);
   {
     const int64_t rec0 = s * T + t0;
     const int nst = (ntok + 31) & ~31;
@@ -513,7 +554,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       float cen[4], qj[4];
-      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, lds + kKhi, lds + kKlo, lds + kSlu, cen, qj);
+      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, lds, cen, qj);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int li = lb + 8 * g4 + 4 * tile + i;
