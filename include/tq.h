@@ -36,16 +36,21 @@
  *   - Device pointers must be 16-byte aligned.  Layouts are dense, row-major,
  *     little-endian.  No global mutable state: calls are thread-safe.
  *
- * Packed layout (bit k of a uint32 word is (word >> k) & 1):
- *   key stream   codes[s][t][d/32][bits]  bit k of word (w,p) = bit p of idx[s][t][32w+k]
- *                signs[s][t][m/32]        bit k of word w     = [z[s][t][32w+k] >= 0]
- *                norm[s][t]  = ||k||,  rnorm[s][t] = ||k|| * ||r||
- *   value stream codes[s][ceil(T/32)][d][bits]
+ * Packed layout (bit k of a uint32 word is (word >> k) & 1).  Every stream
+ * stores Tp = 32 * ceil(T / 32) tokens per sequence: the context is cut into
+ * 32-token blocks, so every block of every sequence starts 16-byte aligned
+ * and can be streamed whole.  Tokens T .. Tp-1 are padding written by
+ * tq_quantize (keys: the encoding of a zero vector; values: fields 0; norms
+ * 0) and never contribute to a result.
+ *   key stream   codes[s][Tp][d/32][bits] bit k of word (w,p) = bit p of idx[s][t][32w+k]
+ *                signs[s][Tp][m/32]       bit k of word w     = [z[s][t][32w+k] >= 0]
+ *                norm[s][Tp]  = ||k||,  rnorm[s][Tp] = ||k|| * ||r||
+ *   value stream codes[s][Tp/32][d][bits]
  *                the `bits` words (B,j,0..bits-1) form one little-endian
  *                record of 32*bits bits: token k of block B holds
  *                idx[s][32B+k][j] in record bits [bits*k, bits*k+bits)
  *                (a field may straddle two words); fields of tokens past
- *                T are 0.                    norm[s][t] = ||v||
+ *                T are 0.                    norm[s][Tp] = ||v||
  *   idx = number of codebook boundaries <= the rotated, normalised coordinate.
  *   z = S r, r = Pi x/||x|| - centroid[idx] (rotated domain, unit scale).
  *   Norms are float32 or float16 (round to nearest even), per tq_packed.
@@ -62,7 +67,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef enum {
   TQ_OK = 0,
@@ -98,8 +103,8 @@ typedef struct {
   int64_t T;               /* tokens per sequence, >= 0                           */
   uint32_t *codes;         /* layout above                                        */
   uint32_t *signs;         /* keys only, else NULL                                */
-  void *norm;              /* [nseq][T] of norm_dtype                             */
-  void *rnorm;             /* keys only, [nseq][T] of norm_dtype, else NULL       */
+  void *norm;              /* [nseq][Tp] of norm_dtype                            */
+  void *rnorm;             /* keys only, [nseq][Tp] of norm_dtype, else NULL      */
   int32_t norm_dtype;      /* TQ_F32 or TQ_F16                                    */
   int32_t reserved;        /* must be 0                                           */
 } tq_packed;

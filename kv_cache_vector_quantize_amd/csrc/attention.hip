@@ -120,7 +120,8 @@ __global__ __launch_bounds__(kLThreads) void logits_kernel(
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kLThreads + tid;
   if (t >= T) return;
   float l[G];
-  key_logits_one<G>(codes, signs, norm, rnorm, nd, bits, m, s * T + t, qs, us, cs, qjl, l);
+  const int64_t Tp = (T + 31) / 32 * 32;  // padded tokens per sequence of the key stream
+  key_logits_one<G>(codes, signs, norm, rnorm, nd, bits, m, s * Tp + t, qs, us, cs, qjl, l);
 #pragma unroll
   for (int g = 0; g < G; ++g) logits[(h0 + g) * T + t] = l[g];
 }

@@ -276,6 +276,7 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
   const int64_t h0 = s * G;
   const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
   const int Ti = static_cast<int>(T);
+  const int64_t Tp = (T + 31) / 32 * 32;             // padded tokens per sequence (streams)
   const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
   const int ntok = t1 - t0;
   const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
   build_tables<KB, VB>(ck, cv, lds, tid, kDecThreads);  // visible after the barrier below
   float sigma;
   {
-    const int64_t rec0 = s * T + t0;
+    const int64_t rec0 = s * Tp + t0;
     const int nst = (ntok + 31) & ~31;
     float vmax = 0.f;
     for (int i = tid; i < nst; i += kDecThreads) {
@@ -317,8 +318,8 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
   float m_ref = (n < G) ? -INFINITY : 0.f, lsum = 0.f;
   const int nblk = (Ti + 31) / 32;
   const int nb_split = (ntok + 31) / 32;
-  const uint32_t* kc_seq = kcodes + s * T * 4 * KB;
-  const uint32_t* ks_seq = ksigns + s * T * 4;
+  const uint32_t* kc_seq = kcodes + s * Tp * 4 * KB;
+  const uint32_t* ks_seq = ksigns + s * Tp * 4;
   const uint32_t* vc_seq = vcodes + s * nblk * kDD * VB;
   const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
   const int vbit0 = 8 * VB * g4;                       // this lane group's 8 value fields
@@ -495,13 +496,14 @@ __global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
   const int64_t s = blockIdx.y;
   const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
   const int Ti = static_cast<int>(T);
+  const int64_t Tp = (T + 31) / 32 * 32;             // padded tokens per sequence (streams)
   const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
   const int ntok = t1 - t0;
   const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
 
   build_tables<KB, 0>(ck, nullptr, lds, tid, kDecThreads);
   {
-    const int64_t rec0 = s * T + t0;
+    const int64_t rec0 = s * Tp + t0;
     const int nst = (ntok + 31) & ~31;
     for (int i = tid; i < nst; i += kDecThreads) {
       float a = 0.f, b = 0.f;
@@ -518,8 +520,8 @@ __global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
   __syncthreads();
 
   const int nb_split = (ntok + 31) / 32;
-  const uint32_t* kc_seq = kcodes + s * T * 4 * KB;
-  const uint32_t* ks_seq = ksigns + s * T * 4;
+  const uint32_t* kc_seq = kcodes + s * Tp * 4 * KB;
+  const uint32_t* ks_seq = ksigns + s * Tp * 4;
   const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
   float* out_h = out + (s * G + (n < G ? n : 0)) * T;
   const bool vec_ok = (Ti & 3) == 0;                  // 16-byte aligned output rows

@@ -277,6 +277,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   }
 
   const int64_t nblk = (T + kUnit - 1) / kUnit;
+  const int64_t Tp = nblk * kUnit;  // padded tokens per sequence in the packed streams
   const int64_t units = nseq * nblk;
   // A-row c32 of a 32x32 tile holds token atok
   const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   int64_t pend_base = 0;
   int pend_n = 0;
   auto store_key_norms = [&](int pp) {
-    if (tid < pend_n) {
+    if (tid < pend_n) {  // every token of the unit, padding included
       const float rho2 = rho_s[pp][0][tid] + rho_s[pp][1][tid] + rho_s[pp][2][tid] + rho_s[pp][3][tid];
       const float nx = n_s[pp][tid];
       store_norm(norm, norm_dtype, pend_base + tid, nx);
@@ -479,8 +480,8 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     if constexpr (KEY) {
       {
         const int tk = lane & 31, p = lane >> 5;
-        if (tk < nvalid && p < BITS) {
-          uint32_t* dst = codes + ((s * T + t0 + tk) * 4 + wave) * BITS;
+        if (p < BITS) {  // padding tokens get the zero-vector encoding
+          uint32_t* dst = codes + ((s * Tp + t0 + tk) * 4 + wave) * BITS;
           dst[p] = cw0;
           if (p + 2 < BITS) dst[p + 2] = cw1;
         }
@@ -523,10 +524,10 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         sw = writelane(static_cast<uint32_t>(Z), v, sw);
         sw = writelane(static_cast<uint32_t>(Z >> 32), 16 + v, sw);
       }
-      if (lane < nvalid) {
-        // a zero vector has every sign bit set
+      if (lane < kUnit) {
+        // a zero vector (padding included) has every sign bit set
         if (n_s[par][lane] == 0.f) sw = 0xFFFFFFFFu;
-        signs[(s * T + t0 + lane) * 4 + wave] = sw;
+        signs[(s * Tp + t0 + lane) * 4 + wave] = sw;
       }
     } else {
       // mask off the fields of padded tokens (zero vectors past the end of T)
@@ -558,11 +559,11 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         dst[2 * h] = vlo;
         dst[2 * h + 1] = vhi;
       }
-      if (tid < nvalid) store_norm(norm, norm_dtype, s * T + t0 + tid, n_s[par][tid]);
+      if (tid < kUnit) store_norm(norm, norm_dtype, s * Tp + t0 + tid, n_s[par][tid]);
     }
     if constexpr (KEY) {
-      pend_base = s * T + t0;
-      pend_n = nvalid;
+      pend_base = s * Tp + t0;
+      pend_n = kUnit;
     }
     s = s1;
     blk = b1;

@@ -161,22 +161,50 @@ def make_tables(G, S, bits, device="cuda"):
 
 @dataclass
 class PackedStream:
+    """A packed key or value stream.  The device buffers (``buf_*``) hold Tp =
+    32 * ceil(T / 32) tokens per sequence; ``codes``/``signs``/``norm``/``rnorm``
+    are views of the first T tokens (value codes are block records already)."""
     role: int
     bits: int
     d: int
     m: int
     nseq: int
     T: int
-    codes: torch.Tensor
-    signs: Optional[torch.Tensor]
-    norm: torch.Tensor
-    rnorm: Optional[torch.Tensor]
+    buf_codes: torch.Tensor
+    buf_signs: Optional[torch.Tensor]
+    buf_norm: torch.Tensor
+    buf_rnorm: Optional[torch.Tensor]
     norm_dtype: int
+
+    @property
+    def Tp(self):
+        return padded_tokens(self.T)
+
+    @property
+    def codes(self):
+        return self.buf_codes[:, : self.T] if self.role == TQ_KEY else self.buf_codes
+
+    @property
+    def signs(self):
+        return None if self.buf_signs is None else self.buf_signs[:, : self.T]
+
+    @property
+    def norm(self):
+        return self.buf_norm[:, : self.T]
+
+    @property
+    def rnorm(self):
+        return None if self.buf_rnorm is None else self.buf_rnorm[:, : self.T]
 
     def c_struct(self):
         return Packed(self.role, self.bits, self.d, self.m, self.nseq, self.T,
-                      self.codes.data_ptr(), _dp(self.signs), self.norm.data_ptr(),
-                      _dp(self.rnorm), self.norm_dtype, 0)
+                      self.buf_codes.data_ptr(), _dp(self.buf_signs), self.buf_norm.data_ptr(),
+                      _dp(self.buf_rnorm), self.norm_dtype, 0)
+
+
+def padded_tokens(T):
+    """Tokens per sequence stored in a packed stream: T rounded up to a 32-token block."""
+    return (T + 31) // 32 * 32
 
 
 def _dp(t):
@@ -188,14 +216,15 @@ def alloc_packed(role, tables, nseq, T, norm_dtype="f16", device="cuda"):
     nd = TQ_F16 if norm_dtype == "f16" else TQ_F32
     tdt = torch.float16 if norm_dtype == "f16" else torch.float32
     d, m, bits = tables.d, tables.m, tables.bits
+    Tp = padded_tokens(T)
     if role == TQ_KEY:
-        codes = torch.zeros((nseq, T, d // 32, bits), dtype=torch.int32, device=device)
-        signs = torch.zeros((nseq, T, m // 32), dtype=torch.int32, device=device)
-        rnorm = torch.zeros((nseq, T), dtype=tdt, device=device)
+        codes = torch.zeros((nseq, Tp, d // 32, bits), dtype=torch.int32, device=device)
+        signs = torch.zeros((nseq, Tp, m // 32), dtype=torch.int32, device=device)
+        rnorm = torch.zeros((nseq, Tp), dtype=tdt, device=device)
     else:
-        codes = torch.zeros((nseq, (T + 31) // 32, d, bits), dtype=torch.int32, device=device)
+        codes = torch.zeros((nseq, Tp // 32, d, bits), dtype=torch.int32, device=device)
         signs, rnorm = None, None
-    norm = torch.zeros((nseq, T), dtype=tdt, device=device)
+    norm = torch.zeros((nseq, Tp), dtype=tdt, device=device)
     return PackedStream(role, bits, d, m if role == TQ_KEY else 0, nseq, T, codes, signs, norm,
                         rnorm, nd)
 

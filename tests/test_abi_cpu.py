@@ -33,7 +33,7 @@ def test_exports_every_declared_function(L):
     assert len(names) == 9, names
     for n in names:
         assert hasattr(L, n), n
-    assert L.tq_abi_version() == 1
+    assert L.tq_abi_version() == 2
 
 
 def test_status_strings(L):

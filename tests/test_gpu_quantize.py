@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from kv_cache_vector_quantize_amd import inputs, tq
 
 from gpu_common import gpu_tables, key_records, oracle_tables, say, to64, value_records
@@ -67,6 +68,13 @@ def test_bf16_keys_student_t_ragged(bits):
     X = inputs.key_slice(w, 0, 3, device="cuda", T=1000).reshape(2, 500, D).contiguous()
     p = _quantize_keys(X, bits, "f16")
     _check_keys(X, p, bits, "f16")
+    # the padding tokens 500 .. 511 of each sequence hold a zero vector's record
+    assert p.Tp == 512
+    codes = p.buf_codes[:, 500:].cpu().numpy().view(np.uint32)
+    idx = oracle.unpack_key_codes(codes, D)
+    assert np.all(idx == 1 << (bits - 1))
+    assert np.all(p.buf_signs[:, 500:].cpu().numpy().view(np.uint32) == 0xFFFFFFFF)
+    assert not torch.any(p.buf_norm[:, 500:]) and not torch.any(p.buf_rnorm[:, 500:])
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
@@ -83,6 +91,7 @@ def test_bf16_values_ragged_blocks(bits):
         for j in range(D):
             rec = sum(int(codes[s_, 10, j, q]) << (32 * q) for q in range(bits))
             assert rec >> (bits * tail) == 0
+    assert not torch.any(p.buf_norm[:, 333:])
 
 
 def test_fp32_values_ragged():
@@ -159,7 +168,6 @@ def test_full_size_quantize_sampled(cfg):
     x = to64(K.reshape(-1, D)[sel])
     codes = pk.codes.reshape(-1, D // 32, w.k_bits)[sel].cpu().numpy().view(np.uint32)
     signs = pk.signs.reshape(-1, M // 32)[sel].cpu().numpy().view(np.uint32)
-    import oracle
     rep = check_key_stream(x, oracle.unpack_key_codes(codes, D), oracle.unpack_signs(signs, M),
                            pk.norm.reshape(-1)[sel].cpu().numpy(),
                            pk.rnorm.reshape(-1)[sel].cpu().numpy(), Pi, S, c, t, w.norm_dtype)
