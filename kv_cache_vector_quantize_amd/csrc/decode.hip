@@ -44,8 +44,11 @@ constexpr int kDecThreads = 256;
 constexpr int kMaxSplit = 2048;   // tokens staged per workgroup (LDS)
 constexpr float kTau = 8.0f;      // raise the reference max when a block exceeds it by 2^8
 // LDS code tables (built by build_tables): key tables at 0, sign table at
-// kS8Off, value table at kVluOff
-constexpr int kS8Off = 4096, kVluOff = 8192, kTabBytes = 9216;
+// kS8Off, value table at kVluOff.  The 16-byte tables are stored kKRep /
+// kSRep times, interleaved entry by entry: lane n reads copy n % k?Rep, so
+// lanes that look up different entries spread over more LDS banks.
+constexpr int kKRep = 1, kSRep = 1;
+constexpr int kS8Off = kKRep * 4096, kVluOff = kS8Off + kSRep * 4096, kTabBytes = kVluOff + 1024;
 
 __device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
@@ -113,7 +116,7 @@ __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, con
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t x = ((c & 1) ? O : E) >> (8 * (c >> 1)) & 0xFFu;
-      const uint4 a = *reinterpret_cast<const uint4*>(tab + 16 * x);
+      const uint4 a = *reinterpret_cast<const uint4*>(tab + 16 * kKRep * x + 16 * ((threadIdx.x & 15) % kKRep));
       accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a.x, a.y, a.z, a.w), bq[c], accC, 0, 0, 0);
     }
   } else {
@@ -134,7 +137,8 @@ __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, con
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     // sign K-step c: coordinates 8c .. 8c+7 of word g4 = byte c of the sign word
-    const uint4 a = *reinterpret_cast<const uint4*>(tab + kS8Off + 16 * ((sw >> (8 * c)) & 0xFFu));
+    const uint4 a = *reinterpret_cast<const uint4*>(tab + kS8Off + 16 * kSRep * ((sw >> (8 * c)) & 0xFFu) +
+                                                    16 * ((threadIdx.x & 15) % kSRep));
     accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a.x, a.y, a.z, a.w), bu[c], accS, 0, 0, 0);
   }
   // the hi column n plus the lo column G + n
@@ -146,11 +150,12 @@ __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, con
 }
 
 // This lane's query fragments for KV head s, built from the rotated queries
-// (q' = Pi q, u = S q', one row of d floats per query head) in the layout
-// described above.
+// (q' = Pi q, u = S q', one row of d floats per query head) times the
+// factors fq and fu, in the layout described above.
 template <int G>
 __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const float* __restrict__ u,
-                                            int64_t s, int lane, half8 (&bq)[8], half8 (&bu)[4]) {
+                                            int64_t s, int lane, float fq, float fu, half8 (&bq)[8],
+                                            half8 (&bu)[4]) {
   const int n = lane & 15, g4 = lane >> 4;
   const bool hi_col = n < G, lo_col = (n >= G) && (n < 2 * G);
   const int g = hi_col ? n : (lo_col ? n - G : 0);
@@ -167,14 +172,14 @@ __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const 
   for (int c = 0; c < 8; ++c) {
     _Float16 h[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = part(qg[32 * g4 + 4 * c + kSlot[i]]);
+    for (int i = 0; i < 8; ++i) h[i] = part(fq * qg[32 * g4 + 4 * c + kSlot[i]]);
     bq[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     _Float16 h[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = part(ug[32 * g4 + 8 * c + i]);
+    for (int i = 0; i < 8; ++i) h[i] = part(fu * ug[32 * g4 + 8 * c + i]);
     bu[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
   }
 }
@@ -201,11 +206,12 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const
   };
   if constexpr (KB == 2) {
     uint4* quad = reinterpret_cast<uint4*>(tab);
-    for (int x = tid; x < 256; x += nthreads) {
+    for (int e = tid; e < 256 * kKRep; e += nthreads) {
+      const int x = e / kKRep;
       _Float16 h[4], l[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) hilo(ck[((x >> i) & 1) | (((x >> (4 + i)) & 1) << 1)], h[i], l[i]);
-      quad[x] = make_uint4(h2u(h[0], h[1]), h2u(l[0], l[1]), h2u(h[2], h[3]), h2u(l[2], l[3]));
+      quad[e] = make_uint4(h2u(h[0], h[1]), h2u(l[0], l[1]), h2u(h[2], h[3]), h2u(l[2], l[3]));
     }
   } else {
     uint32_t* khi = reinterpret_cast<uint32_t*>(tab);
@@ -225,13 +231,14 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const
     }
   }
   uint4* s8 = reinterpret_cast<uint4*>(tab + kS8Off);
-  for (int x = tid; x < 256; x += nthreads) {
+  for (int e = tid; e < 256 * kSRep; e += nthreads) {
+    const int x = e / kSRep;
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = h2u(static_cast<_Float16>(((x >> (2 * i)) & 1) ? 1.f : -1.f),
                  static_cast<_Float16>(((x >> (2 * i + 1)) & 1) ? 1.f : -1.f));
-    s8[x] = make_uint4(w[0], w[1], w[2], w[3]);
+    s8[e] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if constexpr (VB > 0) {
     uint32_t* vlut = reinterpret_cast<uint32_t*>(tab + kVluOff);
@@ -241,35 +248,83 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const
 }
 
 // ------------------------------------------------------------ the kernel
-template <int G, int KB, int VB>
+// Every 32-token block a wave works on is streamed whole into the wave's
+// part of an LDS ring by LDS DMA (global_load_lds_dwordx4: 16 bytes per lane
+// straight into LDS, no registers), kRing blocks deep: while the wave
+// computes block j, blocks j+1 and j+2 are in flight.  A block's packet is
+// the concatenation of its key plane words, sign words, value records and
+// the three norm rows -- all contiguous, 16-byte aligned runs in the packed
+// streams, since every stream holds whole 32-token blocks.
+constexpr int kRing = 3;
+static_assert(kRing == 2 || kRing == 3, "the waits below cover rings of 2 or 3 blocks");
+
+// NK / NV: bytes per stored key / value norm (2: float16, 4: float32)
+template <int KB, int VB, int NK, int NV>
+struct Packet {
+  static constexpr int kKC = 0;                // key plane words [32 tokens][4][KB]
+  static constexpr int kSG = 512 * KB;         // sign words [32][4]
+  static constexpr int kVC = kSG + 512;        // value records [128 coordinates][VB]
+  static constexpr int kNK = kVC + 512 * VB;   // ||k|| [32]
+  static constexpr int kNR = kNK + 32 * NK;    // ||k|| ||r|| [32]
+  static constexpr int kNV = kNR + 32 * NK;    // ||v|| [32]
+  static constexpr int kBytes = kNV + 32 * NV;
+  static constexpr int kChunks = kBytes / 16;
+  static constexpr int kInstr = (kChunks + 63) / 64;   // DMA instructions per block
+  static constexpr int kTail = kChunks - 64 * (kInstr - 1);  // lanes of the last one
+};
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
+// 16 bytes from global `src` (this lane's) to LDS at lds + 16 * lane; `lds`
+// is wave-uniform.  Issued as inline assembly so that the compiler does not
+// treat the ring as written by a load it tracks (it would then wait for every
+// DMA in flight before any LDS read); the waits are explicit instead.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+#endif
+}
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
+#endif
+}
+
+template <int NB>
+__device__ __forceinline__ float norm_at(const char* p, int i) {
+  if constexpr (NB == 2) return static_cast<float>(reinterpret_cast<const _Float16*>(p)[i]);
+  else return reinterpret_cast<const float*>(p)[i];
+}
+
+template <int G, int KB, int VB, int NK, int NV>
 __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
     const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
     const float* __restrict__ cv, int64_t T, int split_len,
     const uint32_t* __restrict__ kcodes, const uint32_t* __restrict__ ksigns, const void* knorm,
-    const void* krnorm, int knd, const uint32_t* __restrict__ vcodes, const void* vnorm, int vnd,
-    float sl2, int nsplit, float* __restrict__ partials) {
+    const void* krnorm, const uint32_t* __restrict__ vcodes, const void* vnorm, float fq, float fu,
+    int nsplit, float* __restrict__ partials) {
+  using P = Packet<KB, VB, NK, NV>;
   constexpr int VL = 1 << (2 * VB);
-  // One LDS buffer with a fixed layout: the code tables first (small
-  // offsets fold into the ds_read instructions; the hi and lo key tables sit
-  // 1 KiB apart so that their reads stay separate and land directly in the
-  // matrix-core operand registers), then the staged norms of the split.
-  // After the main loop the staging bytes hold the four waves' softmax
-  // states for the merge.
-  constexpr int kStage = kTabBytes;
-  constexpr int kStageBytes = kMaxSplit * 12;
-  constexpr int kMergeBytes = (2 * 4 * 16 + 4 * G * kDD + 4) * 4;
-  constexpr int kRed = kStage + (kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes);
-  __shared__ __align__(16) char lds[kRed + 16];
+  constexpr int kSlot = 4 * P::kBytes;   // one ring slot: the 4 waves' packets
+  // code tables (build_tables); the ring; after the main loop the ring holds
+  // the four waves' softmax states for the merge
+  __shared__ __align__(16) char lds[kTabBytes];
+  constexpr int kMerge = (2 * 4 * 16 + 4 * G * kDD) * 4;
+  __shared__ __align__(16) char ring[kRing * kSlot > kMerge ? kRing * kSlot : kMerge];
   const uint32_t* vlut = reinterpret_cast<const uint32_t*>(lds + kVluOff);
-  float* nk_s = reinterpret_cast<float*>(lds + kStage);   // ||k|| * scale * log2(e)
-  float* rq_s = nk_s + kMaxSplit;          // sqrt(pi/2)/m ||k|| ||r|| * scale * log2(e)
-  float* nv_s = rq_s + kMaxSplit;          // ||v|| / sigma, sigma = the split's largest ||v||
-  float (*m_s)[16] = reinterpret_cast<float (*)[16]>(lds + kStage);
-  float (*l_s)[16] = reinterpret_cast<float (*)[16]>(lds + kStage + 4 * 16 * 4);
-  float (*o_s)[G][kDD] = reinterpret_cast<float (*)[G][kDD]>(lds + kStage + 2 * 4 * 16 * 4);
-  float* red_s = reinterpret_cast<float*>(lds + kRed);   // the 4 waves' largest ||v||
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g4 = lane >> 4;
   const int split = blockIdx.x;
   const int64_t s = blockIdx.y;
@@ -278,132 +333,146 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
   const int Ti = static_cast<int>(T);
   const int64_t Tp = (T + 31) / 32 * 32;             // padded tokens per sequence (streams)
   const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
-  const int ntok = t1 - t0;
-  const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
+  const int nb_split = (t1 - t0 + 31) / 32;
+  // this wave takes the split's blocks wave, wave + 4, ...
+  const int nbw = (nb_split > wave) ? (nb_split - wave + 3) / 4 : 0;
+
+  // DMA source of each of this lane's chunks for the wave's first block, and
+  // its advance per block of the wave (4 blocks of the split)
+  const char* src[P::kInstr];
+  int64_t step[P::kInstr];
+  {
+    const int64_t tok = s * Tp + t0 + 32 * wave;     // padded token index of the first block
+#pragma unroll
+    for (int i = 0; i < P::kInstr; ++i) {
+      const int c = 64 * i + lane;
+      const char* p = reinterpret_cast<const char*>(kcodes);
+      int64_t st = 0;
+      if (c < 32 * KB) {
+        p = reinterpret_cast<const char*>(kcodes) + tok * 16 * KB + 16 * c;
+        st = 4 * 32 * 16 * KB;
+      } else if (c < 32 * KB + 32) {
+        p = reinterpret_cast<const char*>(ksigns) + tok * 16 + 16 * (c - 32 * KB);
+        st = 4 * 32 * 16;
+      } else if (c < 32 * (KB + 1 + VB)) {
+        p = reinterpret_cast<const char*>(vcodes) + (tok / 32) * 512 * VB + 16 * (c - 32 * (KB + 1));
+        st = 4 * 512 * VB;
+      } else if (c < 32 * (KB + 1 + VB) + 4 * NK) {
+        const int e = c - 32 * (KB + 1 + VB);        // 2 NK chunks per key norm row
+        const int row = e / (2 * NK);
+        p = reinterpret_cast<const char*>(row == 0 ? knorm : krnorm) + tok * NK + 16 * (e - 2 * NK * row);
+        st = 4 * 32 * NK;
+      } else if (c < P::kChunks) {
+        const int e = c - 32 * (KB + 1 + VB) - 4 * NK;
+        p = reinterpret_cast<const char*>(vnorm) + tok * NV + 16 * e;
+        st = 4 * 32 * NV;
+      }
+      src[i] = p;
+      step[i] = st;
+    }
+  }
+  const uint32_t ring0 = lds_addr(ring) + wave * P::kBytes;
+  auto issue = [&](int j, int slot) {
+    const uint32_t l = ring0 + slot * kSlot;
+#pragma unroll
+    for (int i = 0; i < P::kInstr; ++i) {
+      const char* a = src[i] + j * step[i];
+      if (i + 1 < P::kInstr || lane < P::kTail) dma16(a, l + 1024 * i);
+    }
+  };
+#pragma unroll
+  for (int jj = 0; jj + 1 < kRing; ++jj)
+    if (jj < nbw) issue(jj, jj);
 
   build_tables<KB, VB>(ck, cv, lds, tid, kDecThreads);  // visible after the barrier below
-  float sigma;
-  {
-    const int64_t rec0 = s * Tp + t0;
-    const int nst = (ntok + 31) & ~31;
-    float vmax = 0.f;
-    for (int i = tid; i < nst; i += kDecThreads) {
-      float a = 0.f, b = 0.f, c = 0.f;
-      if (i < ntok) {
-        a = load_norm(knorm, knd, rec0 + i);
-        b = load_norm(krnorm, knd, rec0 + i);
-        c = load_norm(vnorm, vnd, rec0 + i);
-      }
-      nk_s[i] = a * sl2;
-      rq_s[i] = qjl * b * sl2;
-      nv_s[i] = c;
-      vmax = fmaxf(vmax, c);
-    }
-    vmax = wave_max(vmax);
-    if (lane == 0) red_s[wave] = vmax;
-    __syncthreads();
-    sigma = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-    if (!(sigma > 0.f)) sigma = 1.f;
-    const float inv = 1.f / sigma;
-    for (int i = tid; i < nst; i += kDecThreads) nv_s[i] *= inv;
-  }
   half8 bq[8], bu[4];
-  query_frags<G>(qr, u, s, lane, bq, bu);
+  query_frags<G>(qr, u, s, lane, fq, fu, bq, bu);
   __syncthreads();
 
   floatx4 O[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // lanes outside the G heads never rescale (their reference stays 0)
-  float m_ref = (n < G) ? -INFINITY : 0.f, lsum = 0.f;
-  const int nblk = (Ti + 31) / 32;
-  const int nb_split = (ntok + 31) / 32;
-  const uint32_t* kc_seq = kcodes + s * Tp * 4 * KB;
-  const uint32_t* ks_seq = ksigns + s * Tp * 4;
-  const uint32_t* vc_seq = vcodes + s * nblk * kDD * VB;
+  // Online softmax in base 2, per head column n (every lane group of a
+  // column holds the same state).  Logits arrive as sv = l - r with the
+  // reference r = m + log2(sigma): m a lazily raised running max, sigma the
+  // running max of ||v||.  Then p'' = 2^sv = p / sigma and the value weight
+  // p'' ||v|| = p ||v|| / sigma stays <= 2^kTau, inside float16 range.
+  // lsum and O are both kept in units of 2^-r, so out = O / lsum.
+  float r_ref = 0.f, m_ref = -INFINITY, lsum = 0.f;
+  float sig = 0.f, lthr = 0.f;                         // sigma; kTau - log2(sigma)
+  bool first = true;
   const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
   const int vbit0 = 8 * VB * g4;                       // this lane group's 8 value fields
-  // the lane group's fields span at most two record words: load the pair
-  // (vw0, vw0 + 1) that holds them (one 8-byte load; vw0 <= VB - 2 keeps it
-  // inside the record) and funnel-shift them out
+  // the fields lie in record words vwlo and vwlo + 1 (the word after a
+  // record is the next record's first, or the first norm row: read, unused)
   const int vwlo = vbit0 >> 5, vsh = vbit0 & 31;
-  const int vw0 = (VB >= 2 && vwlo > VB - 2) ? VB - 2 : vwlo;
-  const bool vhi_only = vwlo > vw0;                    // fields lie in the upper word
 
-  // this wave's next block: key plane words and the sign word of both tiles
-  uint32_t kw_n[2][KB], sw_n[2];
-  auto fetch = [&](int bb) {
-    const int tb = t0 + 32 * bb;
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      int t = tb + rowtok + 4 * tile;
-      t = (t < Ti) ? t : Ti - 1;                       // clamped: tail tokens are masked later
-      const uint32_t* kw = kc_seq + static_cast<uint32_t>(t * 4 + g4) * KB;
-#pragma unroll
-      for (int q = 0; q < KB; ++q) kw_n[tile][q] = kw[q];
-      sw_n[tile] = ks_seq[static_cast<uint32_t>(t * 4 + g4)];
+  int slot = 0;
+  for (int j = 0; j < nbw; ++j) {
+    // blocks j+1 .. j+kRing-1 stay in flight while block j is waited for
+    if (j + kRing - 1 < nbw) {
+      issue(j + kRing - 1, slot == 0 ? kRing - 1 : slot - 1);
+      wait_vm<(kRing - 1) * P::kInstr>();
+    } else if (kRing > 2 && j + 2 < nbw) {
+      wait_vm<(kRing > 2 ? 2 : 0) * P::kInstr>();
+    } else if (j + 1 < nbw) {
+      wait_vm<P::kInstr>();
+    } else {
+      wait_vm<0>();
     }
-  };
-  if (wave < nb_split) fetch(wave);
-
-  for (int bb = wave; bb < nb_split; bb += 4) {
-    uint32_t kw_c[2][KB], sw_c[2];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-#pragma unroll
-      for (int q = 0; q < KB; ++q) kw_c[tile][q] = kw_n[tile][q];
-      sw_c[tile] = sw_n[tile];
-    }
-    // the (lo, hi) record words of this lane group's value fields, for the 8
-    // coordinate tiles: issued now, consumed after the logits
-    uint32_t vw_c[8][2];
-    {
-      const uint32_t* vb_blk = vc_seq + static_cast<uint32_t>(((t0 >> 5) + bb) * kDD + n) * VB;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        if constexpr (VB >= 2) {
-          typedef uint2 __attribute__((aligned(4))) uint2_a4;  // record words are 4-byte aligned
-          const uint2 w2 = *reinterpret_cast<const uint2_a4*>(vb_blk + 16 * nt * VB + vw0);
-          vw_c[nt][0] = w2.x;
-          vw_c[nt][1] = w2.y;
-        } else {
-          vw_c[nt][0] = vb_blk[16 * nt * VB];
-          vw_c[nt][1] = 0u;
-        }
-      }
-    }
-    if (bb + 4 < nb_split) fetch(bb + 4);              // in flight during this block
-
-    const int tb = t0 + 32 * bb;                       // first token of the block
+    const char* pk = ring + slot * kSlot + wave * P::kBytes;
+    slot = (slot == kRing - 1) ? 0 : slot + 1;
+    const int tb = t0 + 32 * (wave + 4 * j);           // first token of the block
     const bool full = tb + 32 <= Ti;
-    const int lb = 32 * bb;                            // block offset in the staged norms
+
     // ---------------- logits of the block's 32 tokens
     float sv[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
+      const int row = rowtok + 4 * tile;
+      uint32_t kw[KB];
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(pk + P::kKC) + (row * 4 + g4) * KB;
+#pragma unroll
+      for (int q = 0; q < KB; ++q) kw[q] = kp[q];
+      const uint32_t sw = reinterpret_cast<const uint32_t*>(pk + P::kSG)[row * 4 + g4];
       float cen[4], qj[4];
-      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, lds, cen, qj);
-      const int l0 = lb + 8 * g4 + 4 * tile;
-      const float4 nk4 = *reinterpret_cast<const float4*>(&nk_s[l0]);
-      const float4 rq4 = *reinterpret_cast<const float4*>(&rq_s[l0]);
-      const float nk[4] = {nk4.x, nk4.y, nk4.z, nk4.w}, rq[4] = {rq4.x, rq4.y, rq4.z, rq4.w};
+      tile_logits<G, KB>(kw, sw, bq, bu, lds, cen, qj);
+      const int l0 = 8 * g4 + 4 * tile;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[4 * tile + i] = nk[i] * cen[i] + rq[i] * qj[i];
-      if (!full) {  // the context's last, partial block: tokens past T get no weight
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tb + (l0 + i - lb) >= Ti) sv[4 * tile + i] = -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const float nk = norm_at<NK>(pk + P::kNK, l0 + i), nr = norm_at<NK>(pk + P::kNR, l0 + i);
+        sv[4 * tile + i] = fmaf(nk, cen[i], fmaf(nr, qj[i], -r_ref));
       }
     }
-    // ---------------- online softmax, base 2
+    if (!full) {  // the context's last, partial block: tokens past T get no weight
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (tb + 8 * g4 + k >= Ti) sv[k] = -INFINITY;
+    }
+    float nv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) nv[k] = norm_at<NV>(pk + P::kNV, 8 * g4 + k);
+    // ---------------- raise the reference when a logit passes m + kTau or a
+    // value norm passes sigma (rare after the first block)
     float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     bm = max_over_rows(bm);
-    if (__ballot(bm > m_ref + kTau)) {
-      const float m_new = fmaxf(m_ref, bm);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first block
+    const float vm = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])),
+                           fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
+    if (__ballot(first || bm > lthr || vm > sig)) {
+      sig = fmaxf(sig, max_over_rows(vm));
+      const float ls = __builtin_amdgcn_logf(fmaxf(sig, 0x1p-90f));   // log2
+      const float m_new = fmaxf(m_ref, bm + r_ref);
+      const float r_new = m_new + ls;
+      const float delta = r_ref - r_new;
+      const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(delta);
+      first = false;
       lsum *= alpha;
       m_ref = m_new;
+      r_ref = r_new;
+      lthr = kTau - ls;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sv[k] += delta;
       float a4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g4 + i);
@@ -413,21 +482,18 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
         for (int i = 0; i < 4; ++i) O[nt][i] *= a4[i];
       }
     }
-    // A = p * ||v|| / sigma (fp16, <= 2^8); B = c_V[idx] for tokens 8*g4 .. 8*g4+7
-    const float4 nva = *reinterpret_cast<const float4*>(&nv_s[lb + 8 * g4]);
-    const float4 nvb = *reinterpret_cast<const float4*>(&nv_s[lb + 8 * g4 + 4]);
-    const float nvk[8] = {nva.x, nva.y, nva.z, nva.w, nvb.x, nvb.y, nvb.z, nvb.w};
+    // A = p'' ||v|| (float16, <= 2^kTau); B = c_V[idx] for tokens 8*g4 .. 8*g4+7
     half8 pa;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float p = __builtin_amdgcn_exp2f(sv[k] - m_ref);
+      const float p = __builtin_amdgcn_exp2f(sv[k]);
       lsum += p;
-      pa[k] = static_cast<_Float16>(p * nvk[k]);
+      pa[k] = static_cast<_Float16>(p * nv[k]);
     }
+    const uint32_t* vrec = reinterpret_cast<const uint32_t*>(pk + P::kVC) + n * VB + vwlo;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const uint32_t X = vhi_only ? (vw_c[nt][1] >> vsh)
-                                  : __builtin_amdgcn_alignbit(vw_c[nt][1], vw_c[nt][0], vsh);
+      const uint32_t X = __builtin_amdgcn_alignbit(vrec[16 * nt * VB + 1], vrec[16 * nt * VB], vsh);
       uint32_t bw[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) bw[q] = vlut[(X >> (2 * VB * q)) & (VL - 1)];
@@ -436,12 +502,15 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
   }
 
   // ---------------- merge the 4 waves' states, write this split's partial
-  __syncthreads();  // the staging area is reused below
+  __syncthreads();  // every wave is done with the ring, which holds the merge area
+  float (*m_s)[16] = reinterpret_cast<float (*)[16]>(ring);
+  float (*l_s)[16] = reinterpret_cast<float (*)[16]>(ring + 4 * 16 * 4);
+  float (*o_s)[G][kDD] = reinterpret_cast<float (*)[G][kDD]>(ring + 2 * 4 * 16 * 4);
   float ltot = lsum;
   ltot += __shfl_xor(ltot, 16);
   ltot += __shfl_xor(ltot, 32);
   if (g4 == 0) {
-    m_s[wave][n] = m_ref;
+    m_s[wave][n] = (nbw > 0) ? r_ref : -INFINITY;    // a wave without blocks adds nothing
     l_s[wave][n] = ltot;
   }
 #pragma unroll
@@ -454,7 +523,7 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
   }
   __syncthreads();
   for (int e = tid; e < G * kDD; e += kDecThreads) {
-    const int g = e / kDD, j = e % kDD;
+    const int g = e / kDD, jj = e % kDD;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, m_s[w][g]);
@@ -462,12 +531,12 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float f = (m_s[w][g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_s[w][g] - M);
-      acc += f * o_s[w][g][j];
+      acc += f * o_s[w][g][jj];
       L += f * l_s[w][g];
     }
     float* out = partials + ((h0 + g) * nsplit + split) * (kDD + 2);
-    out[j] = acc * sigma;
-    if (j == 0) {
+    out[jj] = acc;
+    if (jj == 0) {
       out[kDD] = M;
       out[kDD + 1] = L;
     }
@@ -516,7 +585,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
     }
   }
   half8 bq[8], bu[4];
-  query_frags<G>(qr, u, s, lane, bq, bu);
+  query_frags<G>(qr, u, s, lane, 1.f, 1.f, bq, bu);
   __syncthreads();
 
   const int nb_split = (ntok + 31) / 32;
@@ -659,33 +728,45 @@ DecodeWorkspace decode_workspace_layout(int B, int Hq, int Hkv, int64_t T, int d
   return w;
 }
 
+template <int G, int KB, int VB>
+static void launch_norms(dim3 grid, hipStream_t stream, const tq_tables& tk, const tq_tables& tv,
+                         const float* qr, const float* u, const tq_packed& k, const tq_packed& v,
+                         int len, float fq, float fu, int nsplit, float* partials) {
+#define TQ_DEC(NKB, NVB)                                                                       \
+  hipLaunchKernelGGL((decode_mfma_kernel<G, KB, VB, NKB, NVB>), grid, dim3(kDecThreads), 0,    \
+                     stream, qr, u, tk.centroids, tv.centroids, k.T, len, k.codes, k.signs,    \
+                     k.norm, k.rnorm, v.codes, v.norm, fq, fu, nsplit, partials)
+  const bool k16 = k.norm_dtype == TQ_F16, v16 = v.norm_dtype == TQ_F16;
+  if (k16 && v16) TQ_DEC(2, 2);
+  else if (k16) TQ_DEC(2, 4);
+  else if (v16) TQ_DEC(4, 2);
+  else TQ_DEC(4, 4);
+#undef TQ_DEC
+}
+
 template <int G, int KB>
 static void launch_vb(int vb, dim3 grid, hipStream_t stream, const tq_tables& tk,
                       const tq_tables& tv, const float* qr, const float* u, const tq_packed& k,
-                      const tq_packed& v, int len, float sl2, int nsplit, float* partials) {
-#define TQ_DEC(VBV)                                                                            \
-  hipLaunchKernelGGL((decode_mfma_kernel<G, KB, VBV>), grid, dim3(kDecThreads), 0, stream,     \
-                     qr, u, tk.centroids, tv.centroids, k.T, len, k.codes, k.signs, k.norm,    \
-                     k.rnorm, k.norm_dtype, v.codes, v.norm, v.norm_dtype, sl2, nsplit, partials)
+                      const tq_packed& v, int len, float fq, float fu, int nsplit, float* partials) {
   switch (vb) {
-    case 1: TQ_DEC(1); break;
-    case 2: TQ_DEC(2); break;
-    case 3: TQ_DEC(3); break;
-    default: TQ_DEC(4); break;
+    case 1: launch_norms<G, KB, 1>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
+    case 2: launch_norms<G, KB, 2>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
+    case 3: launch_norms<G, KB, 3>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
+    default: launch_norms<G, KB, 4>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
   }
-#undef TQ_DEC
 }
 
 template <int G>
 static hipError_t launch_g(const tq_tables& tk, const tq_tables& tv, const float* qr,
                            const float* u, int64_t nseq, const tq_packed& k, const tq_packed& v,
-                           float sl2, float* partials, int len, int nsplit, hipStream_t stream) {
+                           float fq, float fu, float* partials, int len, int nsplit,
+                           hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(nsplit), static_cast<unsigned>(nseq));
   switch (tk.bits) {
-    case 1: launch_vb<G, 1>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
-    case 2: launch_vb<G, 2>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
-    case 3: launch_vb<G, 3>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
-    default: launch_vb<G, 4>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, sl2, nsplit, partials); break;
+    case 1: launch_vb<G, 1>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
+    case 2: launch_vb<G, 2>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
+    case 3: launch_vb<G, 3>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
+    default: launch_vb<G, 4>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
   }
   return hipGetLastError();
 }
@@ -699,14 +780,17 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
   const int64_t nseq = static_cast<int64_t>(B) * Hkv;
   const int len = split_length(nseq, k.T);
   const int nsplit = static_cast<int>((k.T + len - 1) / len);
-  const float sl2 = scale * 1.4426950408889634f;  // softmax in base 2
+  // the softmax runs in base 2: the query fragments carry scale * log2(e),
+  // the sign fragments also the QJL factor sqrt(pi/2) / m
+  const float fq = scale * 1.4426950408889634f;
+  const float fu = fq * (1.2533141373155003f / static_cast<float>(tk.m));
   float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.partials);
   hipError_t e;
   switch (G) {
-    case 1: e = launch_g<1>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
-    case 2: e = launch_g<2>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
-    case 4: e = launch_g<4>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
-    case 8: e = launch_g<8>(tk, tv, qr, u, nseq, k, v, sl2, partials, len, nsplit, stream); break;
+    case 1: e = launch_g<1>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
+    case 2: e = launch_g<2>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
+    case 4: e = launch_g<4>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
+    case 8: e = launch_g<8>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

@@ -155,3 +155,47 @@ def test_decode_full_size_sampled_rows(cfg):
     ref = _oracle_decode_rows(to64(q), pk, pv, w.k_bits, w.v_bits, w.B, w.Hq, w.Hkv, rows)
     ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
     assert ok, rel
+
+
+@pytest.mark.parametrize("kbits,vbits,knd,vnd,G", [
+    (1, 4, "f32", "f32", 4), (3, 1, "f16", "f32", 2), (4, 2, "f32", "f16", 8), (2, 3, "f32", "f16", 1)])
+def test_decode_code_widths_and_norm_dtypes(kbits, vbits, knd, vnd, G):
+    """Every key / value width and norm storage mix, several splits with a
+    ragged last block."""
+    say("decode widths", kbits, vbits, knd, vnd, G)
+    B, Hkv, T = 2, 2, 777
+    Hq = G * Hkv
+    K = torch.randn((B * Hkv, T, D), device="cuda").contiguous()
+    V = (torch.randn((B * Hkv, T, D), device="cuda") * 0.5).contiguous()
+    tk, pk = _keys(K, kbits, knd)
+    tv, pv = _values(V, vbits, vnd)
+    q = torch.randn((B, Hq, D), device="cuda")
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv).cpu().numpy()
+    rows = [(b, h) for b in range(B) for h in range(Hq)]
+    ref = _oracle_decode_rows(to64(q), pk, pv, kbits, vbits, B, Hq, Hkv, rows)
+    ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
+    assert ok, rel
+
+
+def test_decode_value_norm_range():
+    """Value norms from 0 to 1e6 rising along the context (float32 norms): the
+    running largest norm and the softmax reference are raised many times
+    inside a split, and the first blocks hold zero vectors only."""
+    say("decode value norm range")
+    B, Hkv, G, T = 1, 2, 4, 3000
+    Hq = G * Hkv
+    g = torch.Generator().manual_seed(5)
+    K = torch.randn((B * Hkv, T, D), generator=g) * 2.0
+    V = torch.randn((B * Hkv, T, D), generator=g)
+    scale = torch.logspace(-6, 6, T, dtype=torch.float64).float()
+    scale[:100] = 0.0
+    V = V * scale[None, :, None]
+    K[:, 2000:2010] *= 6.0  # a few tokens with large logits late in the context
+    tk, pk = _keys(K.cuda().contiguous(), 2, "f32")
+    tv, pv = _values(V.cuda().contiguous(), 3, "f32")
+    q = torch.randn((B, Hq, D), generator=g).cuda()
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv).cpu().numpy()
+    rows = [(0, h) for h in range(Hq)]
+    ref = _oracle_decode_rows(to64(q), pk, pv, 2, 3, B, Hq, Hkv, rows)
+    ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
+    assert ok, rel
