@@ -43,12 +43,13 @@ constexpr int kDD = 128;
 constexpr int kDecThreads = 256;
 constexpr int kMaxSplit = 2048;   // tokens staged per workgroup (LDS)
 constexpr float kTau = 8.0f;      // raise the reference max when a block exceeds it by 2^8
-// LDS code tables (built by build_tables): key tables at 0, sign table at
-// kS8Off, value table at kVluOff.  The 16-byte tables are stored kKRep /
-// kSRep times, interleaved entry by entry: lane n reads copy n % k?Rep, so
-// lanes that look up different entries spread over more LDS banks.
-constexpr int kKRep = 1, kSRep = 1;
-constexpr int kS8Off = kKRep * 4096, kVluOff = kS8Off + kSRep * 4096, kTabBytes = kVluOff + 1024;
+// LDS code tables (built by build_tables): key tables at 0, value table at
+// kVluOff.  Random lookups by 64 lanes are free of LDS bank conflicts only
+// while a table fits in the 64 banks (256 bytes; 128 for 4-byte reads): the
+// 2-bit key table is therefore indexed by coordinate pairs (16 entries)
+// rather than quads.
+constexpr int kSgnOff = 2048, kVluOff = 4096, kTabBytes = kVluOff + 1024;
+
 
 __device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
@@ -97,6 +98,51 @@ __device__ __forceinline__ uint32_t pair_index(const uint32_t* p, int m) {
 // Columns n < G carry the fp16 value, G <= n < 2G its fp16 residual, the
 // rest zero.
 
+
+// (x >> 8K) & 0xF0: the high nibble of byte K of x, as a 16-byte-stride
+// table offset, in one instruction (a byte-select operand for K > 0)
+template <int K>
+__device__ __forceinline__ uint32_t high_nibble16(uint32_t x) {
+  if constexpr (K == 0) {
+    return x & 0xF0u;
+  } else {
+    uint32_t r = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (K == 1)
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+          : "=v"(r) : "v"(x), "s"(0xF0u));
+    else if constexpr (K == 2)
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
+          : "=v"(r) : "v"(x), "s"(0xF0u));
+    else
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+          : "=v"(r) : "v"(x), "s"(0xF0u));
+#endif
+    return r;
+  }
+}
+
+// centroid K-step C of a 2-bit tile (coordinates 4C .. 4C+3 = the pairs
+// (4C, 4C+1) and (4C+2, 4C+3)) from the pair table at `tab`
+template <int C>
+__device__ __forceinline__ floatx4 key2_kstep(uint32_t Q, uint32_t Q2, uint32_t Qs, uint32_t Q2s,
+                                              const char* tab, const half8& b, floatx4 acc) {
+  const uint32_t oa = high_nibble16<C / 2>((C & 1) ? Q : Qs);
+  const uint32_t ob = high_nibble16<C / 2>((C & 1) ? Q2 : Q2s);
+  const uint2 x = *reinterpret_cast<const uint2*>(tab + oa);
+  const uint2 y = *reinterpret_cast<const uint2*>(tab + ob);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), b, acc, 0, 0, 0);
+}
+
+// sign K-step C: byte C of the sign word sw; sws = sw << 4
+template <int C>
+__device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const char* tab, const half8& b,
+                                              floatx4 acc) {
+  const uint2 x = *reinterpret_cast<const uint2*>(tab + high_nibble16<C>(sws));
+  const uint2 y = *reinterpret_cast<const uint2*>(tab + high_nibble16<C>(sw));
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), b, acc, 0, 0, 0);
+}
+
 // Centroid and sign dots of one 16-token tile (tile 0 or 1 of a 32-token
 // block) for this lane's query-head column: lane (g4, n) gets, for rows
 // 4*g4 + i, the centroid dot <q', c[idx]> (cen) and the sign dot
@@ -109,38 +155,36 @@ __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, con
                                             float (&qj)[4]) {
   floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
   if constexpr (KB == 2) {
-    // byte k of E / O: the quad-table index of coordinates 8k .. 8k+3 /
-    // 8k+4 .. 8k+7 (plane-0 nibble | plane-1 nibble << 4)
-    const uint32_t E = (pw[0] & 0x0F0F0F0Fu) | ((pw[1] & 0x0F0F0F0Fu) << 4);
-    const uint32_t O = ((pw[0] >> 4) & 0x0F0F0F0Fu) | (pw[1] & 0xF0F0F0F0u);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t x = ((c & 1) ? O : E) >> (8 * (c >> 1)) & 0xFFu;
-      const uint4 a = *reinterpret_cast<const uint4*>(tab + 16 * kKRep * x + 16 * ((threadIdx.x & 15) % kKRep));
-      accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a.x, a.y, a.z, a.w), bq[c], accC, 0, 0, 0);
-    }
+    // nibble j of Q / Q2: the pair-table index of coordinates (4j, 4j+1) /
+    // (4j+2, 4j+3): bits 0, 1 = plane 0 of the two, bits 2, 3 = plane 1.
+    // Qs / Q2s hold the same shifted up by 4, so that every nibble is the
+    // high nibble of some byte: x16 table offsets with one masked byte read.
+    const uint32_t Q = ((pw[1] << 2) & 0xCCCCCCCCu) | (pw[0] & 0x33333333u);
+    const uint32_t Q2 = (pw[1] & 0xCCCCCCCCu) | ((pw[0] >> 2) & 0x33333333u);
+    const uint32_t Qs = Q << 4, Q2s = Q2 << 4;
+    accC = key2_kstep<0>(Q, Q2, Qs, Q2s, tab, bq[0], accC);
+    accC = key2_kstep<1>(Q, Q2, Qs, Q2s, tab, bq[1], accC);
+    accC = key2_kstep<2>(Q, Q2, Qs, Q2s, tab, bq[2], accC);
+    accC = key2_kstep<3>(Q, Q2, Qs, Q2s, tab, bq[3], accC);
+    accC = key2_kstep<4>(Q, Q2, Qs, Q2s, tab, bq[4], accC);
+    accC = key2_kstep<5>(Q, Q2, Qs, Q2s, tab, bq[5], accC);
+    accC = key2_kstep<6>(Q, Q2, Qs, Q2s, tab, bq[6], accC);
+    accC = key2_kstep<7>(Q, Q2, Qs, Q2s, tab, bq[7], accC);
   } else {
-    const char* khi_b = tab;
-    const char* klo_b = tab + 1024;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       // coordinates 4c .. 4c+3 of word g4: A = (hi, lo) of pair (4c, 4c+1), then of (4c+2, 4c+3)
-      const uint32_t offA = pair_index<KB>(pw, 2 * c) << 2;
-      const uint32_t offB = pair_index<KB>(pw, 2 * c + 1) << 2;
-      const uint32_t a0 = *reinterpret_cast<const uint32_t*>(khi_b + offA);
-      const uint32_t a1 = *reinterpret_cast<const uint32_t*>(klo_b + offA);
-      const uint32_t a2 = *reinterpret_cast<const uint32_t*>(khi_b + offB);
-      const uint32_t a3 = *reinterpret_cast<const uint32_t*>(klo_b + offB);
-      accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a0, a1, a2, a3), bq[c], accC, 0, 0, 0);
+      const uint2 x = *reinterpret_cast<const uint2*>(tab + (pair_index<KB>(pw, 2 * c) << 3));
+      const uint2 y = *reinterpret_cast<const uint2*>(tab + (pair_index<KB>(pw, 2 * c + 1) << 3));
+      accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), bq[c], accC, 0, 0, 0);
     }
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    // sign K-step c: coordinates 8c .. 8c+7 of word g4 = byte c of the sign word
-    const uint4 a = *reinterpret_cast<const uint4*>(tab + kS8Off + 16 * kSRep * ((sw >> (8 * c)) & 0xFFu) +
-                                                    16 * ((threadIdx.x & 15) % kSRep));
-    accS = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(a.x, a.y, a.z, a.w), bu[c], accS, 0, 0, 0);
-  }
+  // sign K-step c: coordinates 8c .. 8c+7 of word g4 = byte c of the sign
+  // word; its low / high nibble selects the +-1 quad of slots 0..3 / 4..7
+  accS = sign_kstep<0>(sw, sw << 4, tab + kSgnOff, bu[0], accS);
+  accS = sign_kstep<1>(sw, sw << 4, tab + kSgnOff, bu[1], accS);
+  accS = sign_kstep<2>(sw, sw << 4, tab + kSgnOff, bu[2], accS);
+  accS = sign_kstep<3>(sw, sw << 4, tab + kSgnOff, bu[3], accS);
   // the hi column n plus the lo column G + n
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -186,15 +230,15 @@ __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const 
 
 // The workgroup's code tables in LDS (kTabBytes at the start of its LDS),
 // built from the codebooks:
-//  * 2-bit keys: entry x of the quad table (uint4 at 16x) holds the centroids
-//    of 4 consecutive coordinates whose plane-0 bits are x & 15 and plane-1
-//    bits x >> 4, as {hi(c0,c1), lo(c0,c1), hi(c2,c3), lo(c2,c3)} -- the
-//    order of a centroid K-step's slots;
-//  * other widths: pair tables khi[x] / klo[x] (uint32 at 4x and 1024 + 4x)
-//    with the fp16 hi / lo halves of the centroids of a coordinate pair whose
-//    2*KB-bit index is x (bit 2p: plane p of the lower coordinate, bit 2p+1:
-//    plane p of the upper);
-//  * at kS8Off, entry x (uint4): the +-1 values of 8 sign bits x, as fp16;
+//  * 2-bit keys: entry x of the pair table (uint2 at 16x) holds the
+//    centroids of 2 consecutive coordinates whose plane-0 bits are x & 3 and
+//    plane-1 bits x >> 2, as {hi(c0,c1), lo(c0,c1)} -- half of a centroid
+//    K-step's slots;
+//  * other widths: entry x of the pair table (uint2 at 8x) holds
+//    {hi(c0,c1), lo(c0,c1)} of the coordinate pair whose 2*KB-bit index is x
+//    (bit 2p: plane p of the lower coordinate, bit 2p+1: plane p of the upper);
+//  * at kSgnOff, entry x (uint2 at 16x) holds the +-1 values of 4 sign bits
+//    x (bit i -> slot i) as fp16;
 //  * at kVluOff (VB > 0), vlut[x]: the value centroids of the token pair
 //    whose fields are x & (2^VB - 1) and x >> VB.
 template <int KB, int VB>
@@ -205,17 +249,14 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const
     l = static_cast<_Float16>(c - static_cast<float>(h));
   };
   if constexpr (KB == 2) {
-    uint4* quad = reinterpret_cast<uint4*>(tab);
-    for (int e = tid; e < 256 * kKRep; e += nthreads) {
-      const int x = e / kKRep;
-      _Float16 h[4], l[4];
+    for (int x = tid; x < 16; x += nthreads) {
+      _Float16 h[2], l[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hilo(ck[((x >> i) & 1) | (((x >> (4 + i)) & 1) << 1)], h[i], l[i]);
-      quad[e] = make_uint4(h2u(h[0], h[1]), h2u(l[0], l[1]), h2u(h[2], h[3]), h2u(l[2], l[3]));
+      for (int i = 0; i < 2; ++i) hilo(ck[((x >> i) & 1) | (((x >> (2 + i)) & 1) << 1)], h[i], l[i]);
+      *reinterpret_cast<uint2*>(tab + 16 * x) = make_uint2(h2u(h[0], h[1]), h2u(l[0], l[1]));
     }
   } else {
-    uint32_t* khi = reinterpret_cast<uint32_t*>(tab);
-    uint32_t* klo = reinterpret_cast<uint32_t*>(tab + 1024);
+    uint2* pair = reinterpret_cast<uint2*>(tab);
     for (int x = tid; x < (1 << (2 * KB)); x += nthreads) {
       int ia = 0, ib = 0;
 #pragma unroll
@@ -226,19 +267,12 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const
       _Float16 ha, la, hb, lb;
       hilo(ck[ia], ha, la);
       hilo(ck[ib], hb, lb);
-      khi[x] = h2u(ha, hb);
-      klo[x] = h2u(la, lb);
+      pair[x] = make_uint2(h2u(ha, hb), h2u(la, lb));
     }
   }
-  uint4* s8 = reinterpret_cast<uint4*>(tab + kS8Off);
-  for (int e = tid; e < 256 * kSRep; e += nthreads) {
-    const int x = e / kSRep;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = h2u(static_cast<_Float16>(((x >> (2 * i)) & 1) ? 1.f : -1.f),
-                 static_cast<_Float16>(((x >> (2 * i + 1)) & 1) ? 1.f : -1.f));
-    s8[e] = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int x = tid; x < 16; x += nthreads) {
+    auto pm = [&](int i) { return static_cast<_Float16>(((x >> i) & 1) ? 1.f : -1.f); };
+    *reinterpret_cast<uint2*>(tab + kSgnOff + 16 * x) = make_uint2(h2u(pm(0), pm(1)), h2u(pm(2), pm(3)));
   }
   if constexpr (VB > 0) {
     uint32_t* vlut = reinterpret_cast<uint32_t*>(tab + kVluOff);
