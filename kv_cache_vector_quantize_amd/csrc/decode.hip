@@ -41,7 +41,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kDD = 128;
 constexpr int kDecThreads = 256;
-constexpr int kMaxSplit = 2048;   // tokens staged per workgroup (LDS)
+constexpr int kMaxSplit = 2048;      // logits: tokens staged per workgroup (LDS)
+constexpr int kDecMaxSplit = 8192;   // decode: tokens per workgroup (longer splits amortise its set-up)
 constexpr float kTau = 8.0f;      // raise the reference max when a block exceeds it by 2^8
 // LDS code tables (built by build_tables): key tables at 0, value table at
 // kVluOff.  Random lookups by 64 lanes are free of LDS bank conflicts only
@@ -483,16 +484,28 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
       for (int k = 0; k < 8; ++k)
         if (tb + 8 * g4 + k >= Ti) sv[k] = -INFINITY;
     }
+    // ||v|| of this lane group's 8 tokens, and their largest
     float nv[8];
+    uint32_t nvh[4];   // float16 norms: the 4 packed pairs as stored
+    float vm;
+    if constexpr (NV == 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(pk + P::kNV + 16 * g4);
+      nvh[0] = w.x; nvh[1] = w.y; nvh[2] = w.z; nvh[3] = w.w;
+      const half2_t m = __builtin_elementwise_max(
+          __builtin_elementwise_max(__builtin_bit_cast(half2_t, w.x), __builtin_bit_cast(half2_t, w.y)),
+          __builtin_elementwise_max(__builtin_bit_cast(half2_t, w.z), __builtin_bit_cast(half2_t, w.w)));
+      vm = static_cast<float>(m.x > m.y ? m.x : m.y);   // norms are finite and >= 0
+    } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) nv[k] = norm_at<NV>(pk + P::kNV, 8 * g4 + k);
+      for (int k = 0; k < 8; ++k) nv[k] = norm_at<NV>(pk + P::kNV, 8 * g4 + k);
+      vm = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])),
+                 fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
+    }
     // ---------------- raise the reference when a logit passes m + kTau or a
     // value norm passes sigma (rare after the first block)
     float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     bm = max_over_rows(bm);
-    const float vm = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])),
-                           fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
     if (__ballot(first || bm > lthr || vm > sig)) {
       sig = fmaxf(sig, max_over_rows(vm));
       const float ls = __builtin_amdgcn_logf(fmaxf(sig, 0x1p-90f));   // log2
@@ -518,16 +531,38 @@ __global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
     }
     // A = p'' ||v|| (float16, <= 2^kTau); B = c_V[idx] for tokens 8*g4 .. 8*g4+7
     half8 pa;
+    if constexpr (NV == 2) {
+      // p'' ||v|| rounded once to float16 straight from the stored float16
+      // norm: one mixed-precision fma per token
+      uint32_t pw[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float p = __builtin_amdgcn_exp2f(sv[k]);
-      lsum += p;
-      pa[k] = static_cast<_Float16>(p * nv[k]);
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[2 * i]), p1 = __builtin_amdgcn_exp2f(sv[2 * i + 1]);
+        lsum += p0 + p1;
+        pw[i] = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(pw[i]) : "v"(p0), "v"(nvh[i]));
+        asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+            : "+v"(pw[i]) : "v"(p1), "v"(nvh[i]));
+#endif
+      }
+      pa = u4_to_h8(pw[0], pw[1], pw[2], pw[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float p = __builtin_amdgcn_exp2f(sv[k]);
+        lsum += p;
+        pa[k] = static_cast<_Float16>(p * nv[k]);
+      }
     }
-    const uint32_t* vrec = reinterpret_cast<const uint32_t*>(pk + P::kVC) + n * VB + vwlo;
+    // two base addresses, so that every record word is an immediate offset
+    // of a paired 4-byte read (at most 255 words away)
+    const uint32_t* vrec0 = reinterpret_cast<const uint32_t*>(pk + P::kVC) + n * VB + vwlo;
+    const uint32_t* vrec1 = vrec0 + 64 * VB;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const uint32_t X = __builtin_amdgcn_alignbit(vrec[16 * nt * VB + 1], vrec[16 * nt * VB], vsh);
+      const uint32_t* vr = (nt < 4 ? vrec0 : vrec1) + 16 * (nt & 3) * VB;
+      const uint32_t X = __builtin_amdgcn_alignbit(vr[1], vr[0], vsh);
       uint32_t bw[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) bw[q] = vlut[(X >> (2 * VB * q)) & (VL - 1)];
@@ -732,18 +767,19 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
 }
 
 // Split length: enough workgroups for about two rounds of the chip at two
-// resident workgroups per CU (two waves per SIMD), in whole 32-token blocks,
-// at most kMaxSplit (the staged norms of a split live in LDS).
+// resident workgroups per CU, in whole 32-token blocks, at most `cap`
+// (logits: kMaxSplit, the staged norms of a split live in LDS; decode:
+// kDecMaxSplit).
 constexpr int kResidentPerCu = 2;
 
-static int split_length(int64_t nseq, int64_t T) {
+static int split_length(int64_t nseq, int64_t T, int cap) {
   const int64_t target = 2 * kResidentPerCu * 256;
   int64_t per_seq = (target + nseq - 1) / nseq;
   if (per_seq < 1) per_seq = 1;
   int64_t len = (T + per_seq - 1) / per_seq;
   len = ((len + 31) / 32) * 32;
   if (len < 128) len = 128;
-  if (len > kMaxSplit) len = kMaxSplit;
+  if (len > cap) len = cap;
   return static_cast<int>(len);
 }
 
@@ -753,7 +789,7 @@ DecodeWorkspace decode_workspace_layout(int B, int Hq, int Hkv, int64_t T, int d
   DecodeWorkspace w{};
   const size_t nh = static_cast<size_t>(B) * Hq;
   const int64_t nseq = static_cast<int64_t>(B) * Hkv;
-  const int64_t len = split_length(nseq > 0 ? nseq : 1, T);
+  const int64_t len = split_length(nseq > 0 ? nseq : 1, T, kDecMaxSplit);
   const size_t nsplit = static_cast<size_t>((T + len - 1) / len);
   w.qr = 0;
   w.u = a256(nh * d * sizeof(float));
@@ -812,7 +848,7 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
   if (B == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t nseq = static_cast<int64_t>(B) * Hkv;
-  const int len = split_length(nseq, k.T);
+  const int len = split_length(nseq, k.T, kDecMaxSplit);
   const int nsplit = static_cast<int>((k.T + len - 1) / len);
   // the softmax runs in base 2: the query fragments carry scale * log2(e),
   // the sign fragments also the QJL factor sqrt(pi/2) / m
@@ -856,7 +892,7 @@ hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float*
   if (B == 0 || k.T == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t nseq = static_cast<int64_t>(B) * Hkv;
-  const int len = split_length(nseq, k.T);
+  const int len = split_length(nseq, k.T, kMaxSplit);
   const int nsplit = static_cast<int>((k.T + len - 1) / len);
   switch (G) {
     case 1: return launch_logits_g<1>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
