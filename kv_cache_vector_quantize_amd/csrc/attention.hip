@@ -18,25 +18,54 @@ constexpr int kAD = 128;
 constexpr int kAM = 128;
 
 // ------------------------------------------------------------- query prep
+// One workgroup per query head: q' = Pi q, then (keys with a sketch) u = S q'.
+// Thread t owns half a row of each matrix (row t/2, columns 64 (t%2) ..
+// +63) in registers, loaded up front for both matrices so that the whole
+// kernel waits for memory once; the two halves of a row meet by a lane
+// shuffle.  The vectors are read from LDS as broadcasts.
+constexpr int kQThreadsP = 2 * kAD;
+
 template <typename QT>
-__global__ __launch_bounds__(kAD) void qprep_kernel(const float* __restrict__ rot,
-                                                    const float* __restrict__ sketch, int m,
-                                                    const QT* __restrict__ q,
-                                                    float* __restrict__ qr,
-                                                    float* __restrict__ u) {
-  __shared__ float qs[kAD], qrs[kAD];
-  const int h = blockIdx.x, j = threadIdx.x;
-  qs[j] = load_elem(q, static_cast<int64_t>(h) * kAD + j);
+__global__ __launch_bounds__(kQThreadsP) void qprep_kernel(const float* __restrict__ rot,
+                                                           const float* __restrict__ sketch, int m,
+                                                           const QT* __restrict__ q,
+                                                           float* __restrict__ qr,
+                                                           float* __restrict__ u) {
+  __shared__ float xs[kAD], ys[kAD];
+  const int64_t h = blockIdx.x;
+  const int tid = threadIdx.x, row = tid >> 1, c0 = 64 * (tid & 1);
+  const bool sk = m > 0;                    // m is 0 or kAM (checked on the host)
+  float4 pr[16], sr[16];
+  const float4* prow = reinterpret_cast<const float4*>(rot + row * kAD + c0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pr[i] = prow[i];
+  if (sk) {
+    const float4* srow = reinterpret_cast<const float4*>(sketch + row * kAD + c0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sr[i] = srow[i];
+  }
+  if (tid < kAD) xs[tid] = load_elem(q, h * kAD + tid);
   __syncthreads();
-  float a = 0.f;
-  for (int k = 0; k < kAD; ++k) a = fmaf(rot[j * kAD + k], qs[k], a);
-  qrs[j] = a;
-  qr[static_cast<int64_t>(h) * kAD + j] = a;
-  __syncthreads();
-  if (m > 0 && j < m) {
-    float b = 0.f;
-    for (int k = 0; k < kAD; ++k) b = fmaf(sketch[j * kAD + k], qrs[k], b);
-    u[static_cast<int64_t>(h) * m + j] = b;
+  auto dot64 = [&](const float4 (&w)[16], const float* v) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a = fmaf(w[i].x, v[c0 + 4 * i], a);
+      a = fmaf(w[i].y, v[c0 + 4 * i + 1], a);
+      a = fmaf(w[i].z, v[c0 + 4 * i + 2], a);
+      a = fmaf(w[i].w, v[c0 + 4 * i + 3], a);
+    }
+    return a + __shfl_xor(a, 1);
+  };
+  const float y = dot64(pr, xs);
+  if ((tid & 1) == 0) {
+    ys[row] = y;
+    qr[h * kAD + row] = y;
+  }
+  if (sk) {
+    __syncthreads();
+    const float z = dot64(sr, ys);
+    if ((tid & 1) == 0) u[h * kAM + row] = z;
   }
 }
 
@@ -44,11 +73,11 @@ hipError_t launch_qprep(const tq_tables& tk, const void* q, int q_dtype, int nh,
                         float* u, hipStream_t stream) {
   if (nh == 0) return hipSuccess;
   if (q_dtype == TQ_BF16)
-    hipLaunchKernelGGL(qprep_kernel<uint16_t>, dim3(nh), dim3(kAD), 0, stream, tk.rot, tk.sketch,
-                       tk.m, static_cast<const uint16_t*>(q), qr, u);
+    hipLaunchKernelGGL(qprep_kernel<uint16_t>, dim3(nh), dim3(kQThreadsP), 0, stream, tk.rot,
+                       tk.sketch, tk.m, static_cast<const uint16_t*>(q), qr, u);
   else
-    hipLaunchKernelGGL(qprep_kernel<float>, dim3(nh), dim3(kAD), 0, stream, tk.rot, tk.sketch,
-                       tk.m, static_cast<const float*>(q), qr, u);
+    hipLaunchKernelGGL(qprep_kernel<float>, dim3(nh), dim3(kQThreadsP), 0, stream, tk.rot,
+                       tk.sketch, tk.m, static_cast<const float*>(q), qr, u);
   return hipGetLastError();
 }
 

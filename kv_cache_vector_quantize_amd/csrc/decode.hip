@@ -1,721 +1,23 @@
-// Decode attention straight from the packed codes, on the matrix cores.
-//
-// Method (a2a-mcp.org page, Stage 2 closing paragraph; "How to implement",
-// item 1): the query is rotated once (q' = Pi q, u = S q'), every logit is
-//   l_t = ||k_t|| <q', c_K[idx_t]> + sqrt(pi/2)/m ||k_t|| ||r_t|| <u, 2 s_t - 1>,
-// a = softmax(scale * l), and the values are summed in the rotated domain,
-// acc = sum_t a_t ||v_t|| c_V[idxV_t]; out = Pi^T acc happens once, in the
-// combine kernel.  No pass dequantizes the cache to memory.
-//
-// Mapping onto gfx950 (wave64, v_mfma_f32_16x16x32_f16):
-//  * every workgroup lays the G rotated queries of its KV head out as
-//    matrix-core B fragments -- fp16 hi in columns [0,G), the fp16 residual
-//    in [G,2G) -- and builds its code tables in LDS from the codebooks.
-//  * one workgroup = 4 waves = one split of the context of one KV head;
-//    wave w owns 32-token blocks w, w+4, ... and keeps its own
-//    online-softmax state; the 4 states merge through LDS.
-//  * logits, per 16-token tile: A = centroid values of 16 tokens x 32
-//    coordinates, looked up from an LDS table by the 2b-bit index of a
-//    coordinate pair as an fp16 hi/lo pair; two MFMAs (A_hi, A_lo) against
-//    the query fragment give fp32-grade dots.  The 1-bit correction is the
-//    same contraction with A = +-1 and B = u.  The hi and lo columns are
-//    summed with one DPP row shift.
-//  * tile rows are ordered so that after the two tiles of a block, lane group
-//    g4 = lane/16 holds the logits of tokens 8*g4 .. 8*g4+7: exactly the
-//    K-slice those lanes feed to the value MFMA, so softmax weights never
-//    leave registers.
-//  * values: A = softmax weight times ||v|| / sigma (rows = heads, fp16;
-//    p <= 2^8 thanks to a lazily raised reference max, sigma = the split's
-//    largest value norm), B = value centroids of 32 tokens x 16 coordinates
-//    from a token-pair table; the merge multiplies sigma back in.
-#include <math.h>
-
-#include "common.h"
-#include "launch.h"
+// Split-K decode: the combine kernel, the split length, the workspace layout
+// and the entry launchers; the main kernels are in decode_kernels.h.
+#include "decode_kernels.h"
 
 namespace tq {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-constexpr int kDD = 128;
-constexpr int kDecThreads = 256;
-constexpr int kMaxSplit = 2048;      // logits: tokens staged per workgroup (LDS)
-constexpr int kDecMaxSplit = 8192;   // decode: tokens per workgroup (longer splits amortise its set-up)
-constexpr float kTau = 8.0f;      // raise the reference max when a block exceeds it by 2^8
-// LDS code tables (built by build_tables): key tables at 0, value table at
-// kVluOff.  Random lookups by 64 lanes are free of LDS bank conflicts only
-// while a table fits in the 64 banks (256 bytes; 128 for 4-byte reads): the
-// 2-bit key table is therefore indexed by coordinate pairs (16 entries)
-// rather than quads.
-constexpr int kSgnOff = 2048, kVluOff = 4096, kTabBytes = kVluOff + 1024;
-
-
-__device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-}
-
-__device__ __forceinline__ half8 u4_to_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 v = {a, b, c, d};
-  return __builtin_bit_cast(half8, v);
-}
-
-// value of lane (i + SH) within the lane's row of 16 (DPP row_shl); lanes
-// whose source falls off the row get 0
-template <int SH>
-__device__ __forceinline__ float row_shl(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                               0x100 + SH, 0xf, 0xf, false));
-}
-
-// max over the 4 rows of 16 lanes (lanes n, n+16, n+32, n+48), in every lane:
-// v_permlane16_swap / v_permlane32_swap exchange rows without LDS
-__device__ __forceinline__ float max_over_rows(float v) {
-  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-}
-
-// 2b-bit index of the coordinate pair (2m, 2m+1) of one 32-coordinate word:
-// bit 2p = plane p of the lower coordinate, bit 2p+1 = plane p of the upper.
-template <int KB>
-__device__ __forceinline__ uint32_t pair_index(const uint32_t* p, int m) {
-  uint32_t x = 0;
-#pragma unroll
-  for (int q = 0; q < KB; ++q) x |= ((p[q] >> (2 * m)) & 3u) << (2 * q);
-  return x;
-}
-
-// ------------------------------------------------------------ query operands
-// Per KV head s and lane (n = lane%16, g4 = lane/16), 12 B-fragments of 8 fp16:
-//  bq[0..7]: centroid K-steps c' = 0..7.  The K slots hold the coordinates
-//    32*g4 + 4c' + {0,1,0,1,2,3,2,3}: every coordinate twice, once against
-//    the hi and once against the lo half of its centroid.
-//  bu[0..3]: sign K-steps c = 0..3, coordinates 32*g4 + 8c + i.
-// Columns n < G carry the fp16 value, G <= n < 2G its fp16 residual, the
-// rest zero.
-
-
-// (x >> 8K) & 0xF0: the high nibble of byte K of x, as a 16-byte-stride
-// table offset, in one instruction (a byte-select operand for K > 0)
-template <int K>
-__device__ __forceinline__ uint32_t high_nibble16(uint32_t x) {
-  if constexpr (K == 0) {
-    return x & 0xF0u;
-  } else {
-    uint32_t r = 0;
-#if defined(__HIP_DEVICE_COMPILE__)
-    if constexpr (K == 1)
-      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
-          : "=v"(r) : "v"(x), "s"(0xF0u));
-    else if constexpr (K == 2)
-      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
-          : "=v"(r) : "v"(x), "s"(0xF0u));
-    else
-      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
-          : "=v"(r) : "v"(x), "s"(0xF0u));
-#endif
-    return r;
-  }
-}
-
-// centroid K-step C of a 2-bit tile (coordinates 4C .. 4C+3 = the pairs
-// (4C, 4C+1) and (4C+2, 4C+3)) from the pair table at `tab`
-template <int C>
-__device__ __forceinline__ floatx4 key2_kstep(uint32_t Q, uint32_t Q2, uint32_t Qs, uint32_t Q2s,
-                                              const char* tab, const half8& b, floatx4 acc) {
-  const uint32_t oa = high_nibble16<C / 2>((C & 1) ? Q : Qs);
-  const uint32_t ob = high_nibble16<C / 2>((C & 1) ? Q2 : Q2s);
-  const uint2 x = *reinterpret_cast<const uint2*>(tab + oa);
-  const uint2 y = *reinterpret_cast<const uint2*>(tab + ob);
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), b, acc, 0, 0, 0);
-}
-
-// sign K-step C: byte C of the sign word sw; sws = sw << 4
-template <int C>
-__device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const char* tab, const half8& b,
-                                              floatx4 acc) {
-  const uint2 x = *reinterpret_cast<const uint2*>(tab + high_nibble16<C>(sws));
-  const uint2 y = *reinterpret_cast<const uint2*>(tab + high_nibble16<C>(sw));
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), b, acc, 0, 0, 0);
-}
-
-// Centroid and sign dots of one 16-token tile (tile 0 or 1 of a 32-token
-// block) for this lane's query-head column: lane (g4, n) gets, for rows
-// 4*g4 + i, the centroid dot <q', c[idx]> (cen) and the sign dot
-// <u, 2s - 1> (qj) of head n (n < G; the other lanes hold partial sums).
-// pw: the tile token's KB plane words of coordinate word g4; sw: its sign
-// word; tab: the LDS tables of build_tables.
-template <int G, int KB>
-__device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
-                                            const half8 (&bu)[4], const char* tab, float (&cen)[4],
-                                            float (&qj)[4]) {
-  floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (KB == 2) {
-    // nibble j of Q / Q2: the pair-table index of coordinates (4j, 4j+1) /
-    // (4j+2, 4j+3): bits 0, 1 = plane 0 of the two, bits 2, 3 = plane 1.
-    // Qs / Q2s hold the same shifted up by 4, so that every nibble is the
-    // high nibble of some byte: x16 table offsets with one masked byte read.
-    const uint32_t Q = ((pw[1] << 2) & 0xCCCCCCCCu) | (pw[0] & 0x33333333u);
-    const uint32_t Q2 = (pw[1] & 0xCCCCCCCCu) | ((pw[0] >> 2) & 0x33333333u);
-    const uint32_t Qs = Q << 4, Q2s = Q2 << 4;
-    accC = key2_kstep<0>(Q, Q2, Qs, Q2s, tab, bq[0], accC);
-    accC = key2_kstep<1>(Q, Q2, Qs, Q2s, tab, bq[1], accC);
-    accC = key2_kstep<2>(Q, Q2, Qs, Q2s, tab, bq[2], accC);
-    accC = key2_kstep<3>(Q, Q2, Qs, Q2s, tab, bq[3], accC);
-    accC = key2_kstep<4>(Q, Q2, Qs, Q2s, tab, bq[4], accC);
-    accC = key2_kstep<5>(Q, Q2, Qs, Q2s, tab, bq[5], accC);
-    accC = key2_kstep<6>(Q, Q2, Qs, Q2s, tab, bq[6], accC);
-    accC = key2_kstep<7>(Q, Q2, Qs, Q2s, tab, bq[7], accC);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      // coordinates 4c .. 4c+3 of word g4: A = (hi, lo) of pair (4c, 4c+1), then of (4c+2, 4c+3)
-      const uint2 x = *reinterpret_cast<const uint2*>(tab + (pair_index<KB>(pw, 2 * c) << 3));
-      const uint2 y = *reinterpret_cast<const uint2*>(tab + (pair_index<KB>(pw, 2 * c + 1) << 3));
-      accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), bq[c], accC, 0, 0, 0);
-    }
-  }
-  // sign K-step c: coordinates 8c .. 8c+7 of word g4 = byte c of the sign
-  // word; its low / high nibble selects the +-1 quad of slots 0..3 / 4..7
-  accS = sign_kstep<0>(sw, sw << 4, tab + kSgnOff, bu[0], accS);
-  accS = sign_kstep<1>(sw, sw << 4, tab + kSgnOff, bu[1], accS);
-  accS = sign_kstep<2>(sw, sw << 4, tab + kSgnOff, bu[2], accS);
-  accS = sign_kstep<3>(sw, sw << 4, tab + kSgnOff, bu[3], accS);
-  // the hi column n plus the lo column G + n
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    cen[i] = accC[i] + row_shl<G>(accC[i]);
-    qj[i] = accS[i] + row_shl<G>(accS[i]);
-  }
-}
-
-// This lane's query fragments for KV head s, built from the rotated queries
-// (q' = Pi q, u = S q', one row of d floats per query head) times the
-// factors fq and fu, in the layout described above.
-template <int G>
-__device__ __forceinline__ void query_frags(const float* __restrict__ qr, const float* __restrict__ u,
-                                            int64_t s, int lane, float fq, float fu, half8 (&bq)[8],
-                                            half8 (&bu)[4]) {
-  const int n = lane & 15, g4 = lane >> 4;
-  const bool hi_col = n < G, lo_col = (n >= G) && (n < 2 * G);
-  const int g = hi_col ? n : (lo_col ? n - G : 0);
-  const float* qg = qr + (s * G + g) * kDD;
-  const float* ug = u + (s * G + g) * kDD;
-  auto part = [&](float x) -> _Float16 {
-    const _Float16 a = static_cast<_Float16>(x);
-    if (hi_col) return a;
-    if (lo_col) return static_cast<_Float16>(x - static_cast<float>(a));
-    return static_cast<_Float16>(0.f);
-  };
-  constexpr int kSlot[8] = {0, 1, 0, 1, 2, 3, 2, 3};
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    _Float16 h[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = part(fq * qg[32 * g4 + 4 * c + kSlot[i]]);
-    bq[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    _Float16 h[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = part(fu * ug[32 * g4 + 8 * c + i]);
-    bu[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
-  }
-}
-
-// The workgroup's code tables in LDS (kTabBytes at the start of its LDS),
-// built from the codebooks:
-//  * 2-bit keys: entry x of the pair table (uint2 at 16x) holds the
-//    centroids of 2 consecutive coordinates whose plane-0 bits are x & 3 and
-//    plane-1 bits x >> 2, as {hi(c0,c1), lo(c0,c1)} -- half of a centroid
-//    K-step's slots;
-//  * other widths: entry x of the pair table (uint2 at 8x) holds
-//    {hi(c0,c1), lo(c0,c1)} of the coordinate pair whose 2*KB-bit index is x
-//    (bit 2p: plane p of the lower coordinate, bit 2p+1: plane p of the upper);
-//  * at kSgnOff, entry x (uint2 at 16x) holds the +-1 values of 4 sign bits
-//    x (bit i -> slot i) as fp16;
-//  * at kVluOff (VB > 0), vlut[x]: the value centroids of the token pair
-//    whose fields are x & (2^VB - 1) and x >> VB.
-template <int KB, int VB>
-__device__ __forceinline__ void build_tables(const float* __restrict__ ck, const float* __restrict__ cv,
-                                             char* tab, int tid, int nthreads) {
-  auto hilo = [&](float c, _Float16& h, _Float16& l) {
-    h = static_cast<_Float16>(c);
-    l = static_cast<_Float16>(c - static_cast<float>(h));
-  };
-  if constexpr (KB == 2) {
-    for (int x = tid; x < 16; x += nthreads) {
-      _Float16 h[2], l[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) hilo(ck[((x >> i) & 1) | (((x >> (2 + i)) & 1) << 1)], h[i], l[i]);
-      *reinterpret_cast<uint2*>(tab + 16 * x) = make_uint2(h2u(h[0], h[1]), h2u(l[0], l[1]));
-    }
-  } else {
-    uint2* pair = reinterpret_cast<uint2*>(tab);
-    for (int x = tid; x < (1 << (2 * KB)); x += nthreads) {
-      int ia = 0, ib = 0;
-#pragma unroll
-      for (int p = 0; p < KB; ++p) {
-        ia |= ((x >> (2 * p)) & 1) << p;
-        ib |= ((x >> (2 * p + 1)) & 1) << p;
-      }
-      _Float16 ha, la, hb, lb;
-      hilo(ck[ia], ha, la);
-      hilo(ck[ib], hb, lb);
-      pair[x] = make_uint2(h2u(ha, hb), h2u(la, lb));
-    }
-  }
-  for (int x = tid; x < 16; x += nthreads) {
-    auto pm = [&](int i) { return static_cast<_Float16>(((x >> i) & 1) ? 1.f : -1.f); };
-    *reinterpret_cast<uint2*>(tab + kSgnOff + 16 * x) = make_uint2(h2u(pm(0), pm(1)), h2u(pm(2), pm(3)));
-  }
-  if constexpr (VB > 0) {
-    uint32_t* vlut = reinterpret_cast<uint32_t*>(tab + kVluOff);
-    for (int x = tid; x < (1 << (2 * VB)); x += nthreads)
-      vlut[x] = h2u(static_cast<_Float16>(cv[x & ((1 << VB) - 1)]), static_cast<_Float16>(cv[x >> VB]));
-  }
-}
-
-// ------------------------------------------------------------ the kernel
-// Every 32-token block a wave works on is streamed whole into the wave's
-// part of an LDS ring by LDS DMA (global_load_lds_dwordx4: 16 bytes per lane
-// straight into LDS, no registers), kRing blocks deep: while the wave
-// computes block j, blocks j+1 and j+2 are in flight.  A block's packet is
-// the concatenation of its key plane words, sign words, value records and
-// the three norm rows -- all contiguous, 16-byte aligned runs in the packed
-// streams, since every stream holds whole 32-token blocks.
-constexpr int kRing = 3;
-static_assert(kRing == 2 || kRing == 3, "the waits below cover rings of 2 or 3 blocks");
-
-// NK / NV: bytes per stored key / value norm (2: float16, 4: float32)
-template <int KB, int VB, int NK, int NV>
-struct Packet {
-  static constexpr int kKC = 0;                // key plane words [32 tokens][4][KB]
-  static constexpr int kSG = 512 * KB;         // sign words [32][4]
-  static constexpr int kVC = kSG + 512;        // value records [128 coordinates][VB]
-  static constexpr int kNK = kVC + 512 * VB;   // ||k|| [32]
-  static constexpr int kNR = kNK + 32 * NK;    // ||k|| ||r|| [32]
-  static constexpr int kNV = kNR + 32 * NK;    // ||v|| [32]
-  static constexpr int kBytes = kNV + 32 * NV;
-  static constexpr int kChunks = kBytes / 16;
-  static constexpr int kInstr = (kChunks + 63) / 64;   // DMA instructions per block
-  static constexpr int kTail = kChunks - 64 * (kInstr - 1);  // lanes of the last one
-};
-
-// LDS byte address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (const __attribute__((address_space(3))) char*)(p)));
-}
-
-// 16 bytes from global `src` (this lane's) to LDS at lds + 16 * lane; `lds`
-// is wave-uniform.  Issued as inline assembly so that the compiler does not
-// treat the ring as written by a load it tracks (it would then wait for every
-// DMA in flight before any LDS read); the waits are explicit instead.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-#endif
-}
-
-// wait until at most N vector-memory operations of this wave are in flight
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt vmcnt(%0)" : : "i"(N) : "memory");
-#endif
-}
-
-template <int NB>
-__device__ __forceinline__ float norm_at(const char* p, int i) {
-  if constexpr (NB == 2) return static_cast<float>(reinterpret_cast<const _Float16*>(p)[i]);
-  else return reinterpret_cast<const float*>(p)[i];
-}
-
-template <int G, int KB, int VB, int NK, int NV>
-__global__ __launch_bounds__(kDecThreads, 3) void decode_mfma_kernel(
-    const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
-    const float* __restrict__ cv, int64_t T, int split_len,
-    const uint32_t* __restrict__ kcodes, const uint32_t* __restrict__ ksigns, const void* knorm,
-    const void* krnorm, const uint32_t* __restrict__ vcodes, const void* vnorm, float fq, float fu,
-    int nsplit, float* __restrict__ partials) {
-  using P = Packet<KB, VB, NK, NV>;
-  constexpr int VL = 1 << (2 * VB);
-  constexpr int kSlot = 4 * P::kBytes;   // one ring slot: the 4 waves' packets
-  // code tables (build_tables); the ring; after the main loop the ring holds
-  // the four waves' softmax states for the merge
-  __shared__ __align__(16) char lds[kTabBytes];
-  constexpr int kMerge = (2 * 4 * 16 + 4 * G * kDD) * 4;
-  __shared__ __align__(16) char ring[kRing * kSlot > kMerge ? kRing * kSlot : kMerge];
-  const uint32_t* vlut = reinterpret_cast<const uint32_t*>(lds + kVluOff);
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g4 = lane >> 4;
-  const int split = blockIdx.x;
-  const int64_t s = blockIdx.y;
-  const int64_t h0 = s * G;
-  const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
-  const int Ti = static_cast<int>(T);
-  const int64_t Tp = (T + 31) / 32 * 32;             // padded tokens per sequence (streams)
-  const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
-  const int nb_split = (t1 - t0 + 31) / 32;
-  // this wave takes the split's blocks wave, wave + 4, ...
-  const int nbw = (nb_split > wave) ? (nb_split - wave + 3) / 4 : 0;
-
-  // DMA source of each of this lane's chunks for the wave's first block, and
-  // its advance per block of the wave (4 blocks of the split)
-  const char* src[P::kInstr];
-  int64_t step[P::kInstr];
-  {
-    const int64_t tok = s * Tp + t0 + 32 * wave;     // padded token index of the first block
-#pragma unroll
-    for (int i = 0; i < P::kInstr; ++i) {
-      const int c = 64 * i + lane;
-      const char* p = reinterpret_cast<const char*>(kcodes);
-      int64_t st = 0;
-      if (c < 32 * KB) {
-        p = reinterpret_cast<const char*>(kcodes) + tok * 16 * KB + 16 * c;
-        st = 4 * 32 * 16 * KB;
-      } else if (c < 32 * KB + 32) {
-        p = reinterpret_cast<const char*>(ksigns) + tok * 16 + 16 * (c - 32 * KB);
-        st = 4 * 32 * 16;
-      } else if (c < 32 * (KB + 1 + VB)) {
-        p = reinterpret_cast<const char*>(vcodes) + (tok / 32) * 512 * VB + 16 * (c - 32 * (KB + 1));
-        st = 4 * 512 * VB;
-      } else if (c < 32 * (KB + 1 + VB) + 4 * NK) {
-        const int e = c - 32 * (KB + 1 + VB);        // 2 NK chunks per key norm row
-        const int row = e / (2 * NK);
-        p = reinterpret_cast<const char*>(row == 0 ? knorm : krnorm) + tok * NK + 16 * (e - 2 * NK * row);
-        st = 4 * 32 * NK;
-      } else if (c < P::kChunks) {
-        const int e = c - 32 * (KB + 1 + VB) - 4 * NK;
-        p = reinterpret_cast<const char*>(vnorm) + tok * NV + 16 * e;
-        st = 4 * 32 * NV;
-      }
-      src[i] = p;
-      step[i] = st;
-    }
-  }
-  const uint32_t ring0 = lds_addr(ring) + wave * P::kBytes;
-  auto issue = [&](int j, int slot) {
-    const uint32_t l = ring0 + slot * kSlot;
-#pragma unroll
-    for (int i = 0; i < P::kInstr; ++i) {
-      const char* a = src[i] + j * step[i];
-      if (i + 1 < P::kInstr || lane < P::kTail) dma16(a, l + 1024 * i);
-    }
-  };
-#pragma unroll
-  for (int jj = 0; jj + 1 < kRing; ++jj)
-    if (jj < nbw) issue(jj, jj);
-
-  build_tables<KB, VB>(ck, cv, lds, tid, kDecThreads);  // visible after the barrier below
-  half8 bq[8], bu[4];
-  query_frags<G>(qr, u, s, lane, fq, fu, bq, bu);
-  __syncthreads();
-
-  floatx4 O[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // Online softmax in base 2, per head column n (every lane group of a
-  // column holds the same state).  Logits arrive as sv = l - r with the
-  // reference r = m + log2(sigma): m a lazily raised running max, sigma the
-  // running max of ||v||.  Then p'' = 2^sv = p / sigma and the value weight
-  // p'' ||v|| = p ||v|| / sigma stays <= 2^kTau, inside float16 range.
-  // lsum and O are both kept in units of 2^-r, so out = O / lsum.
-  float r_ref = 0.f, m_ref = -INFINITY, lsum = 0.f;
-  float sig = 0.f, lthr = 0.f;                         // sigma; kTau - log2(sigma)
-  bool first = true;
-  const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
-  const int vbit0 = 8 * VB * g4;                       // this lane group's 8 value fields
-  // the fields lie in record words vwlo and vwlo + 1 (the word after a
-  // record is the next record's first, or the first norm row: read, unused)
-  const int vwlo = vbit0 >> 5, vsh = vbit0 & 31;
-
-  int slot = 0;
-  for (int j = 0; j < nbw; ++j) {
-    // blocks j+1 .. j+kRing-1 stay in flight while block j is waited for
-    if (j + kRing - 1 < nbw) {
-      issue(j + kRing - 1, slot == 0 ? kRing - 1 : slot - 1);
-      wait_vm<(kRing - 1) * P::kInstr>();
-    } else if (kRing > 2 && j + 2 < nbw) {
-      wait_vm<(kRing > 2 ? 2 : 0) * P::kInstr>();
-    } else if (j + 1 < nbw) {
-      wait_vm<P::kInstr>();
-    } else {
-      wait_vm<0>();
-    }
-    const char* pk = ring + slot * kSlot + wave * P::kBytes;
-    slot = (slot == kRing - 1) ? 0 : slot + 1;
-    const int tb = t0 + 32 * (wave + 4 * j);           // first token of the block
-    const bool full = tb + 32 <= Ti;
-
-    // ---------------- logits of the block's 32 tokens
-    float sv[8];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const int row = rowtok + 4 * tile;
-      uint32_t kw[KB];
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(pk + P::kKC) + (row * 4 + g4) * KB;
-#pragma unroll
-      for (int q = 0; q < KB; ++q) kw[q] = kp[q];
-      const uint32_t sw = reinterpret_cast<const uint32_t*>(pk + P::kSG)[row * 4 + g4];
-      float cen[4], qj[4];
-      tile_logits<G, KB>(kw, sw, bq, bu, lds, cen, qj);
-      const int l0 = 8 * g4 + 4 * tile;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float nk = norm_at<NK>(pk + P::kNK, l0 + i), nr = norm_at<NK>(pk + P::kNR, l0 + i);
-        sv[4 * tile + i] = fmaf(nk, cen[i], fmaf(nr, qj[i], -r_ref));
-      }
-    }
-    if (!full) {  // the context's last, partial block: tokens past T get no weight
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (tb + 8 * g4 + k >= Ti) sv[k] = -INFINITY;
-    }
-    // ||v|| of this lane group's 8 tokens, and their largest
-    float nv[8];
-    uint32_t nvh[4];   // float16 norms: the 4 packed pairs as stored
-    float vm;
-    if constexpr (NV == 2) {
-      const uint4 w = *reinterpret_cast<const uint4*>(pk + P::kNV + 16 * g4);
-      nvh[0] = w.x; nvh[1] = w.y; nvh[2] = w.z; nvh[3] = w.w;
-      const half2_t m = __builtin_elementwise_max(
-          __builtin_elementwise_max(__builtin_bit_cast(half2_t, w.x), __builtin_bit_cast(half2_t, w.y)),
-          __builtin_elementwise_max(__builtin_bit_cast(half2_t, w.z), __builtin_bit_cast(half2_t, w.w)));
-      vm = static_cast<float>(m.x > m.y ? m.x : m.y);   // norms are finite and >= 0
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) nv[k] = norm_at<NV>(pk + P::kNV, 8 * g4 + k);
-      vm = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])),
-                 fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
-    }
-    // ---------------- raise the reference when a logit passes m + kTau or a
-    // value norm passes sigma (rare after the first block)
-    float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    bm = max_over_rows(bm);
-    if (__ballot(first || bm > lthr || vm > sig)) {
-      sig = fmaxf(sig, max_over_rows(vm));
-      const float ls = __builtin_amdgcn_logf(fmaxf(sig, 0x1p-90f));   // log2
-      const float m_new = fmaxf(m_ref, bm + r_ref);
-      const float r_new = m_new + ls;
-      const float delta = r_ref - r_new;
-      const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(delta);
-      first = false;
-      lsum *= alpha;
-      m_ref = m_new;
-      r_ref = r_new;
-      lthr = kTau - ls;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) sv[k] += delta;
-      float a4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g4 + i);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[nt][i] *= a4[i];
-      }
-    }
-    // A = p'' ||v|| (float16, <= 2^kTau); B = c_V[idx] for tokens 8*g4 .. 8*g4+7
-    half8 pa;
-    if constexpr (NV == 2) {
-      // p'' ||v|| rounded once to float16 straight from the stored float16
-      // norm: one mixed-precision fma per token
-      uint32_t pw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = __builtin_amdgcn_exp2f(sv[2 * i]), p1 = __builtin_amdgcn_exp2f(sv[2 * i + 1]);
-        lsum += p0 + p1;
-        pw[i] = 0;
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(pw[i]) : "v"(p0), "v"(nvh[i]));
-        asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
-            : "+v"(pw[i]) : "v"(p1), "v"(nvh[i]));
-#endif
-      }
-      pa = u4_to_h8(pw[0], pw[1], pw[2], pw[3]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float p = __builtin_amdgcn_exp2f(sv[k]);
-        lsum += p;
-        pa[k] = static_cast<_Float16>(p * nv[k]);
-      }
-    }
-    // two base addresses, so that every record word is an immediate offset
-    // of a paired 4-byte read (at most 255 words away)
-    const uint32_t* vrec0 = reinterpret_cast<const uint32_t*>(pk + P::kVC) + n * VB + vwlo;
-    const uint32_t* vrec1 = vrec0 + 64 * VB;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const uint32_t* vr = (nt < 4 ? vrec0 : vrec1) + 16 * (nt & 3) * VB;
-      const uint32_t X = __builtin_amdgcn_alignbit(vr[1], vr[0], vsh);
-      uint32_t bw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bw[q] = vlut[(X >> (2 * VB * q)) & (VL - 1)];
-      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, u4_to_h8(bw[0], bw[1], bw[2], bw[3]), O[nt], 0, 0, 0);
-    }
-  }
-
-  // ---------------- merge the 4 waves' states, write this split's partial
-  __syncthreads();  // every wave is done with the ring, which holds the merge area
-  float (*m_s)[16] = reinterpret_cast<float (*)[16]>(ring);
-  float (*l_s)[16] = reinterpret_cast<float (*)[16]>(ring + 4 * 16 * 4);
-  float (*o_s)[G][kDD] = reinterpret_cast<float (*)[G][kDD]>(ring + 2 * 4 * 16 * 4);
-  float ltot = lsum;
-  ltot += __shfl_xor(ltot, 16);
-  ltot += __shfl_xor(ltot, 32);
-  if (g4 == 0) {
-    m_s[wave][n] = (nbw > 0) ? r_ref : -INFINITY;    // a wave without blocks adds nothing
-    l_s[wave][n] = ltot;
-  }
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = 4 * g4 + i;
-      if (g < G) o_s[wave][g][16 * nt + n] = O[nt][i];
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < G * kDD; e += kDecThreads) {
-    const int g = e / kDD, jj = e % kDD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, m_s[w][g]);
-    float acc = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = (m_s[w][g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_s[w][g] - M);
-      acc += f * o_s[w][g][jj];
-      L += f * l_s[w][g];
-    }
-    float* out = partials + ((h0 + g) * nsplit + split) * (kDD + 2);
-    out[jj] = acc;
-    if (jj == 0) {
-      out[kDD] = M;
-      out[kDD + 1] = L;
-    }
-  }
-}
-
-// ------------------------------------------------------------ logits only
-// Raw logits of the G query heads sharing KV head s (same page, Stage 2
-// closing paragraph): l_t = ||k_t|| <q', c[idx_t]> + sqrt(pi/2)/m ||r_t|| <u, 2 s_t - 1>
-// with ||r_t|| the stored ||k|| ||r^||.  One workgroup per (split, KV head),
-// the same tiles as decode; out[(s*G + g) * T + t].
-template <int G, int KB>
-__global__ __launch_bounds__(kDecThreads, 2) void logits_mfma_kernel(
-    const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
-    int64_t T, int split_len, const uint32_t* __restrict__ kcodes,
-    const uint32_t* __restrict__ ksigns, const void* knorm, const void* krnorm, int knd,
-    float* __restrict__ out) {
-  constexpr int kStage = kTabBytes;
-  __shared__ __align__(16) char lds[kStage + 2 * kMaxSplit * 4];
-  float* nk_s = reinterpret_cast<float*>(lds + kStage);   // ||k||
-  float* rq_s = nk_s + kMaxSplit;                          // sqrt(pi/2)/m ||k|| ||r||
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g4 = lane >> 4;
-  const int split = blockIdx.x;
-  const int64_t s = blockIdx.y;
-  const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
-  const int Ti = static_cast<int>(T);
-  const int64_t Tp = (T + 31) / 32 * 32;             // padded tokens per sequence (streams)
-  const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
-  const int ntok = t1 - t0;
-  const float qjl = sqrtf(static_cast<float>(M_PI) / 2.f) / 128.f;
-
-  build_tables<KB, 0>(ck, nullptr, lds, tid, kDecThreads);
-  {
-    const int64_t rec0 = s * Tp + t0;
-    const int nst = (ntok + 31) & ~31;
-    for (int i = tid; i < nst; i += kDecThreads) {
-      float a = 0.f, b = 0.f;
-      if (i < ntok) {
-        a = load_norm(knorm, knd, rec0 + i);
-        b = load_norm(krnorm, knd, rec0 + i);
-      }
-      nk_s[i] = a;
-      rq_s[i] = qjl * b;
-    }
-  }
-  half8 bq[8], bu[4];
-  query_frags<G>(qr, u, s, lane, 1.f, 1.f, bq, bu);
-  __syncthreads();
-
-  const int nb_split = (ntok + 31) / 32;
-  const uint32_t* kc_seq = kcodes + s * Tp * 4 * KB;
-  const uint32_t* ks_seq = ksigns + s * Tp * 4;
-  const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
-  float* out_h = out + (s * G + (n < G ? n : 0)) * T;
-  const bool vec_ok = (Ti & 3) == 0;                  // 16-byte aligned output rows
-
-  uint32_t kw_n[2][KB], sw_n[2];
-  auto fetch = [&](int bb) {
-    const int tb = t0 + 32 * bb;
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      int t = tb + rowtok + 4 * tile;
-      t = (t < Ti) ? t : Ti - 1;                       // clamped: tail tokens are not stored
-      const uint32_t* kw = kc_seq + static_cast<uint32_t>(t * 4 + g4) * KB;
-#pragma unroll
-      for (int q = 0; q < KB; ++q) kw_n[tile][q] = kw[q];
-      sw_n[tile] = ks_seq[static_cast<uint32_t>(t * 4 + g4)];
-    }
-  };
-  if (wave < nb_split) fetch(wave);
-
-  for (int bb = wave; bb < nb_split; bb += 4) {
-    uint32_t kw_c[2][KB], sw_c[2];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-#pragma unroll
-      for (int q = 0; q < KB; ++q) kw_c[tile][q] = kw_n[tile][q];
-      sw_c[tile] = sw_n[tile];
-    }
-    if (bb + 4 < nb_split) fetch(bb + 4);              // in flight during this block
-    const int lb = 32 * bb;
-    const int tb = t0 + lb;
-    float lv[8];
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      float cen[4], qj[4];
-      tile_logits<G, KB>(kw_c[tile], sw_c[tile], bq, bu, lds, cen, qj);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int li = lb + 8 * g4 + 4 * tile + i;
-        lv[4 * tile + i] = nk_s[li] * cen[i] + rq_s[li] * qj[i];
-      }
-    }
-    // lane (g4, n < G): tokens tb + 8*g4 .. tb + 8*g4 + 7 of head n
-    if (n < G) {
-      const int tt = tb + 8 * g4;
-      if (vec_ok && tt + 8 <= Ti) {
-        float4* o4 = reinterpret_cast<float4*>(out_h + tt);
-        o4[0] = make_float4(lv[0], lv[1], lv[2], lv[3]);
-        o4[1] = make_float4(lv[4], lv[5], lv[6], lv[7]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (tt + k < Ti) out_h[tt + k] = lv[k];
-      }
-    }
-  }
-}
+// per-G launchers (decode_g<G>.hip)
+#define TQ_DECL_G(GV)                                                                              \
+  hipError_t decode_launch_g##GV(const tq_tables& tk, const tq_tables& tv, const float* qr,        \
+                                 const float* u, int64_t nseq, const tq_packed& k,                 \
+                                 const tq_packed& v, float fq, float fu, float* partials, int len, \
+                                 int nsplit, hipStream_t stream);                                  \
+  hipError_t logits_launch_g##GV(const tq_tables& tk, const float* qr, const float* u,             \
+                                 int64_t nseq, const tq_packed& k, int len, int nsplit,            \
+                                 float* out, hipStream_t stream);
+TQ_DECL_G(1)
+TQ_DECL_G(2)
+TQ_DECL_G(4)
+TQ_DECL_G(8)
+#undef TQ_DECL_G
 
 // Merge the splits of one query head by log-sum-exp (base 2), then rotate
 // back once: out = Pi^T (acc / L).  512 threads: 4 groups of splits x 128
@@ -768,8 +70,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(
 
 // Split length: enough workgroups for about two rounds of the chip at two
 // resident workgroups per CU, in whole 32-token blocks, at most `cap`
-// (logits: kMaxSplit, the staged norms of a split live in LDS; decode:
-// kDecMaxSplit).
+// (kLogMaxSplit, kDecMaxSplit).
 constexpr int kResidentPerCu = 2;
 
 static int split_length(int64_t nseq, int64_t T, int cap) {
@@ -798,49 +99,6 @@ DecodeWorkspace decode_workspace_layout(int B, int Hq, int Hkv, int64_t T, int d
   return w;
 }
 
-template <int G, int KB, int VB>
-static void launch_norms(dim3 grid, hipStream_t stream, const tq_tables& tk, const tq_tables& tv,
-                         const float* qr, const float* u, const tq_packed& k, const tq_packed& v,
-                         int len, float fq, float fu, int nsplit, float* partials) {
-#define TQ_DEC(NKB, NVB)                                                                       \
-  hipLaunchKernelGGL((decode_mfma_kernel<G, KB, VB, NKB, NVB>), grid, dim3(kDecThreads), 0,    \
-                     stream, qr, u, tk.centroids, tv.centroids, k.T, len, k.codes, k.signs,    \
-                     k.norm, k.rnorm, v.codes, v.norm, fq, fu, nsplit, partials)
-  const bool k16 = k.norm_dtype == TQ_F16, v16 = v.norm_dtype == TQ_F16;
-  if (k16 && v16) TQ_DEC(2, 2);
-  else if (k16) TQ_DEC(2, 4);
-  else if (v16) TQ_DEC(4, 2);
-  else TQ_DEC(4, 4);
-#undef TQ_DEC
-}
-
-template <int G, int KB>
-static void launch_vb(int vb, dim3 grid, hipStream_t stream, const tq_tables& tk,
-                      const tq_tables& tv, const float* qr, const float* u, const tq_packed& k,
-                      const tq_packed& v, int len, float fq, float fu, int nsplit, float* partials) {
-  switch (vb) {
-    case 1: launch_norms<G, KB, 1>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-    case 2: launch_norms<G, KB, 2>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-    case 3: launch_norms<G, KB, 3>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-    default: launch_norms<G, KB, 4>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-  }
-}
-
-template <int G>
-static hipError_t launch_g(const tq_tables& tk, const tq_tables& tv, const float* qr,
-                           const float* u, int64_t nseq, const tq_packed& k, const tq_packed& v,
-                           float fq, float fu, float* partials, int len, int nsplit,
-                           hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(nsplit), static_cast<unsigned>(nseq));
-  switch (tk.bits) {
-    case 1: launch_vb<G, 1>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-    case 2: launch_vb<G, 2>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-    case 3: launch_vb<G, 3>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-    default: launch_vb<G, 4>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* qr, const float* u,
                          int B, int Hq, int Hkv, const tq_packed& k, const tq_packed& v,
                          float scale, void* ws, const DecodeWorkspace& lay, float* out,
@@ -857,10 +115,10 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
   float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.partials);
   hipError_t e;
   switch (G) {
-    case 1: e = launch_g<1>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
-    case 2: e = launch_g<2>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
-    case 4: e = launch_g<4>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
-    case 8: e = launch_g<8>(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
+    case 1: e = decode_launch_g1(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
+    case 2: e = decode_launch_g2(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
+    case 4: e = decode_launch_g4(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
+    case 8: e = decode_launch_g8(tk, tv, qr, u, nseq, k, v, fq, fu, partials, len, nsplit, stream); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
@@ -869,36 +127,18 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
   return hipGetLastError();
 }
 
-template <int G>
-static hipError_t launch_logits_g(const tq_tables& tk, const float* qr, const float* u,
-                                  int64_t nseq, const tq_packed& k, int len, int nsplit, float* out,
-                                  hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(nsplit), static_cast<unsigned>(nseq));
-#define TQ_LOG(KBV)                                                                                \
-  hipLaunchKernelGGL((logits_mfma_kernel<G, KBV>), grid, dim3(kDecThreads), 0, stream, qr, u,     \
-                     tk.centroids, k.T, len, k.codes, k.signs, k.norm, k.rnorm, k.norm_dtype, out)
-  switch (tk.bits) {
-    case 1: TQ_LOG(1); break;
-    case 2: TQ_LOG(2); break;
-    case 3: TQ_LOG(3); break;
-    default: TQ_LOG(4); break;
-  }
-#undef TQ_LOG
-  return hipGetLastError();
-}
-
 hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
                               int Hkv, const tq_packed& k, float* logits, hipStream_t stream) {
   if (B == 0 || k.T == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t nseq = static_cast<int64_t>(B) * Hkv;
-  const int len = split_length(nseq, k.T, kMaxSplit);
+  const int len = split_length(nseq, k.T, kLogMaxSplit);
   const int nsplit = static_cast<int>((k.T + len - 1) / len);
   switch (G) {
-    case 1: return launch_logits_g<1>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
-    case 2: return launch_logits_g<2>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
-    case 4: return launch_logits_g<4>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
-    case 8: return launch_logits_g<8>(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 1: return logits_launch_g1(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 2: return logits_launch_g2(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 4: return logits_launch_g4(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 8: return logits_launch_g8(tk, qr, u, nseq, k, len, nsplit, logits, stream);
     default: return hipErrorInvalidValue;
   }
 }
