@@ -114,13 +114,16 @@ struct QTab {
 __device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
 
 // Index of y (x256 scale) = number of boundaries <= y.  Writes the lane masks
-// of the index bits into P (bit BITS-1 is the sign test y >= 0; the lower
-// bits are the magnitude cell, complemented for y < 0), returns the signed
-// centroid through C and the index through idx.
+// of the index bits into P (bit BITS-1 is the sign test: y's sign bit clear;
+// the lower bits are the magnitude cell, complemented for y < 0), returns the
+// signed centroid through C and the index through idx.  The sign test reads
+// the sign bit, so a -0.0 (only from a negative product that underflowed)
+// counts as negative, like the value it rounds.
 template <int BITS>
 __device__ __forceinline__ void quant_one(float y, const QTab<BITS>& tab, uint64_t* P, float& C,
                                           int& idx) {
-  const bool ms = y >= 0.f;
+  const int sgn = static_cast<int>(__float_as_uint(y)) >> 31;   // 0, or -1 for a set sign bit
+  const bool ms = sgn == 0;
   const float a = fabsf(y);
   const uint64_t Ms = __ballot(ms);
   float mag;
@@ -156,7 +159,7 @@ __device__ __forceinline__ void quant_one(float y, const QTab<BITS>& tab, uint64
   }
   constexpr int half = 1 << (BITS - 1);
   C = ms ? mag : -mag;
-  idx = cnt ^ (ms ? half : half - 1);  // half + cnt, or half - 1 - cnt
+  idx = (cnt ^ sgn) + half;  // half + cnt, or half - 1 - cnt
 }
 
 template <typename XT>
