@@ -72,15 +72,16 @@ def test_logits_group_sizes_ragged(G):
     assert ok, (nbad, mx)
 
 
-@pytest.mark.parametrize("bits,T", [(1, 100), (2, 2049), (4, 64)])
-def test_logits_code_widths_and_splits(bits, T):
-    """Every key width through the matrix-core logits; T = 2049 leaves a
-    one-token last split, T = 100 a partial 32-token block."""
-    say("logits bits", bits, "T", T)
+@pytest.mark.parametrize("bits,T,nd", [(1, 100, "f16"), (2, 2049, "f16"), (4, 64, "f16"), (3, 333, "f32"),
+                                       (2, 4096, "f32")])
+def test_logits_code_widths_and_splits(bits, T, nd):
+    """Every key width and both norm storages through the matrix-core logits;
+    T = 2049 leaves a one-token last split, T = 100 / 333 a partial block."""
+    say("logits bits", bits, "T", T, nd)
     B, Hkv, G = 1, 4, 4
     Hq = G * Hkv
     X = (torch.randn((B * Hkv, T, D), device="cuda") * 2).to(torch.bfloat16)
-    tk, p = _keys(X.contiguous(), bits, "f16")
+    tk, p = _keys(X.contiguous(), bits, nd)
     q = torch.randn((B, Hq, D), device="cuda")
     got = tq.tq_attn_logits(tk, q, p, B, Hq, Hkv)
     torch.cuda.synchronize()
