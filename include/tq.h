@@ -195,6 +195,12 @@ size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m);
  *   scale    softmax scale, > 0 (1/sqrt(d) for standard attention)
  *   out      out, [B][Hq][d] float32
  *   ws       workspace of at least tq_decode_workspace(B, Hq, Hkv, T, d, m) bytes
+ * Hq/Hkv must be 1, 2, 4 or 8, T < 2^28 and B*Hkv <= 65535 (else
+ * TQ_EUNSUPPORTED).  Key and value norms may be stored as float16 or float32
+ * independently.  Logits carry float32-grade accuracy (float16 hi/lo operand
+ * pairs, float32 accumulation); the value weights enter the value contraction
+ * as float16 (at most 2^8 relative to the running maximum), so out matches an
+ * exact evaluation to about 1e-4 relative.
  */
 tq_status tq_attn_decode(const tq_tables *tk, const tq_tables *tv, const void *q, int q_dtype,
                          int B, int Hq, int Hkv, const tq_packed *k, const tq_packed *v,
