@@ -11,26 +11,27 @@
 // combine kernel.  No pass dequantizes the cache to memory.
 //
 // Mapping onto gfx950 (wave64, v_mfma_f32_16x16x32_f16):
+//  * one workgroup = 4 waves = one split of the context of one KV head;
+//    wave w owns 32-token blocks w, w+4, ..., streams each whole block
+//    (key planes, signs, value records, norms) into its LDS ring by LDS DMA,
+//    and keeps its own online-softmax state; the 4 states merge through LDS.
 //  * every workgroup lays the G rotated queries of its KV head out as
 //    matrix-core B fragments -- fp16 hi in columns [0,G), the fp16 residual
 //    in [G,2G) -- and builds its code tables in LDS from the codebooks.
-//  * one workgroup = 4 waves = one split of the context of one KV head;
-//    wave w owns 32-token blocks w, w+4, ... and keeps its own
-//    online-softmax state; the 4 states merge through LDS.
-//  * logits, per 16-token tile: A = centroid values of 16 tokens x 32
-//    coordinates, looked up from an LDS table by the 2b-bit index of a
-//    coordinate pair as an fp16 hi/lo pair; two MFMAs (A_hi, A_lo) against
-//    the query fragment give fp32-grade dots.  The 1-bit correction is the
-//    same contraction with A = +-1 and B = u.  The hi and lo columns are
-//    summed with one DPP row shift.
+//  * logits, per 16-token tile: A = centroid values of 16 tokens x 4
+//    coordinates per K-step as fp16 hi/lo pairs, looked up from an LDS table
+//    by the index of a coordinate pair, against the query fragment: fp32-grade
+//    dots.  The 1-bit correction is the same contraction with A = +-1 (a
+//    table of sign nibbles) and B = u.  The hi and lo columns are summed with
+//    one DPP row shift.
 //  * tile rows are ordered so that after the two tiles of a block, lane group
 //    g4 = lane/16 holds the logits of tokens 8*g4 .. 8*g4+7: exactly the
 //    K-slice those lanes feed to the value MFMA, so softmax weights never
 //    leave registers.
-//  * values: A = softmax weight times ||v|| / sigma (rows = heads, fp16;
-//    p <= 2^8 thanks to a lazily raised reference max, sigma = the split's
-//    largest value norm), B = value centroids of 32 tokens x 16 coordinates
-//    from a token-pair table; the merge multiplies sigma back in.
+//  * values: A = softmax weight times ||v|| (rows = heads, fp16, at most 2^8
+//    thanks to a reference that tracks both the running logit max and the
+//    running largest ||v||), B = value centroids of 32 tokens x 16
+//    coordinates from a token-pair table.
 #pragma once
 
 #include <math.h>
