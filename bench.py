@@ -146,6 +146,56 @@ def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0):
     }
 
 
+def serve_leg(n, w, tk, tv, K, V, q, pk, pv, ws, out):
+    """The serving loop at the workload's shape: n steps of (append one new
+    key and value per sequence with tq_append, decode one query token per
+    (batch, query head)), the context growing from T-n+1 to T tokens.  The
+    streams end as they started (the appended tokens are the workload's own
+    last n tokens, re-quantized bit for bit)."""
+    import torch
+
+    from kv_cache_vector_quantize_amd import tq
+    T0 = w.T - n
+    # new tokens, one [nseq][1][d] slab per step
+    Kn = K[:, T0:].transpose(0, 1).contiguous().unsqueeze(2)
+    Vn = V[:, T0:].transpose(0, 1).contiguous().unsqueeze(2)
+    pk.capacity = pv.capacity = tq.padded_tokens(w.T)  # same buffers, now growable
+
+    def run(evs=None):
+        pk.T = pv.T = T0
+        for i in range(n):
+            if evs is not None:
+                evs[i][0].record()
+            tq.tq_append(tk, Kn[i], pk)
+            if evs is not None:
+                evs[i][1].record()
+            tq.tq_append(tv, Vn[i], pv)
+            if evs is not None:
+                evs[i][2].record()
+            tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv, ws=ws, out=out)
+            if evs is not None:
+                evs[i][3].record()
+
+    run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    run(evs)
+    torch.cuda.synchronize()
+    assert pk.T == pv.T == w.T
+    ak = sum(e[0].elapsed_time(e[1]) for e in evs) / n
+    av = sum(e[1].elapsed_time(e[2]) for e in evs) / n
+    dc = sum(e[2].elapsed_time(e[3]) for e in evs) / n
+    ms = evs[0][0].elapsed_time(evs[-1][3]) / n
+    log(f"serving: {n} steps, {ms:.3f} ms/step (append K {ak * 1e3:.1f} us, append V {av * 1e3:.1f} us, "
+        f"decode {dc * 1e3:.1f} us)")
+    del Kn, Vn
+    return {"steps": n, "context": [T0 + 1, w.T], "ms_per_step": round(ms, 4),
+            "append_k_us": round(ak * 1e3, 2), "append_v_us": round(av * 1e3, 2),
+            "decode_us": round(dc * 1e3, 2),
+            "new_tokens_per_s": round(w.B / (ms * 1e-3), 1),
+            "step": "tq_append(K), tq_append(V), tq_attn_decode"}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -164,6 +214,9 @@ def main():
     ap.add_argument("--config", type=int, default=3,
                     help="workload number 1-5 (default 3: batched quantize + decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serve-steps", type=int, default=32,
+                    help="decode workloads: also time this many serving steps (append one key "
+                         "and one value per sequence, then decode) ending at the full context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter scaling)")
     args = ap.parse_args()
@@ -275,6 +328,9 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
 
+    serving = serve_leg(args.serve_steps, w, tk, tv, K, V, q, pk, pv, ws, out) \
+        if w.decode and args.serve_steps > 0 else None
+
     step_bytes = sum(st["bytes"] for st in stages)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
@@ -321,6 +377,7 @@ def main():
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "stages": stage_report,
         "roofline": roofline,
+        "serving": serving,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -37,11 +37,12 @@
  *     little-endian.  No global mutable state: calls are thread-safe.
  *
  * Packed layout (bit k of a uint32 word is (word >> k) & 1).  Every stream
- * stores Tp = 32 * ceil(T / 32) tokens per sequence: the context is cut into
+ * stores Tp tokens per sequence, Tp = the stream's capacity (a multiple of 32,
+ * at least T) or, with capacity 0, 32 * ceil(T / 32): the context is cut into
  * 32-token blocks, so every block of every sequence starts 16-byte aligned
- * and can be streamed whole.  Tokens T .. Tp-1 are padding written by
- * tq_quantize (keys: the encoding of a zero vector; values: fields 0; norms
- * 0) and never contribute to a result.
+ * and can be streamed whole.  tq_quantize writes tokens T .. 32*ceil(T/32)-1
+ * as padding (keys: the encoding of a zero vector; values: fields 0; norms
+ * 0); tokens at or past T never contribute to a result.
  *   key stream   codes[s][Tp][d/32][bits] bit k of word (w,p) = bit p of idx[s][t][32w+k]
  *                signs[s][Tp][m/32]       bit k of word w     = [z[s][t][32w+k] >= 0]
  *                norm[s][Tp]  = ||k||,  rnorm[s][Tp] = ||k|| * ||r||
@@ -67,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 
 typedef enum {
   TQ_OK = 0,
@@ -106,7 +107,8 @@ typedef struct {
   void *norm;              /* [nseq][Tp] of norm_dtype                            */
   void *rnorm;             /* keys only, [nseq][Tp] of norm_dtype, else NULL      */
   int32_t norm_dtype;      /* TQ_F32 or TQ_F16                                    */
-  int32_t reserved;        /* must be 0                                           */
+  int32_t capacity;        /* tokens stored per sequence (Tp): 0, or a multiple   */
+                           /* of 32 that is >= T (a cache that grows by append)   */
 } tq_packed;
 
 /* Version of this ABI (TQ_ABI_VERSION of the built library). */
@@ -157,6 +159,28 @@ tq_status tq_rotation(int d, const double *G, double *rot64, float *rot32, hipSt
  */
 tq_status tq_quantize(const tq_tables *t, const void *x, int x_dtype, const tq_packed *out,
                       hipStream_t stream);
+
+/*
+ * tq_append -- quantize n new tokens per sequence onto the end of a stream:
+ * the cache update of every decode step, which quantizes each new key and
+ * value as it arrives.
+ * Cites: a2a-mcp.org page, "How to implement", item 1 (quantize on every
+ * cache update); "How it works" (online, data-independent: a token's record
+ * depends on that token alone).
+ *   t      tables of the stream
+ *   x      in, [out->nseq][n][d] of x_dtype (TQ_F32 or TQ_BF16)
+ *   n      new tokens per sequence, >= 0
+ *   out    a stream holding out->T tokens whose capacity is nonzero and at
+ *          least out->T + n (else TQ_EINVAL)
+ * Writes tokens T .. T+n-1 with the records tq_quantize gives them, and
+ * tokens T+n .. 32*ceil((T+n)/32)-1 as padding; the records of tokens below
+ * T are kept (the value record of the block holding token T is merged in
+ * place).  After the call the stream equals, bit for bit, tq_quantize of all
+ * T+n tokens at the same capacity.  out->T is the caller's to advance: pass
+ * T+n to later calls.  Calls that write one stream must not overlap.
+ */
+tq_status tq_append(const tq_tables *t, const void *x, int x_dtype, int64_t n, const tq_packed *out,
+                    hipStream_t stream);
 
 /* Workspace bytes for tq_attn_logits (the rotated queries). */
 size_t tq_logits_workspace(int B, int Hq, int d, int m);

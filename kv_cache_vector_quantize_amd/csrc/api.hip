@@ -34,7 +34,8 @@ tq_status check_tables(const tq_tables* t, bool key) {
 
 tq_status check_packed(const tq_packed* p, const tq_tables* t, int role) {
   if (p == nullptr) return TQ_EINVAL;
-  if (p->role != role || p->reserved != 0) return TQ_EINVAL;
+  if (p->role != role) return TQ_EINVAL;
+  if (p->capacity < 0 || p->capacity % 32 != 0 || (p->capacity != 0 && p->capacity < p->T)) return TQ_EINVAL;
   if (p->bits != t->bits || p->d != t->d || p->m != t->m) return TQ_EINVAL;
   if (p->nseq < 0 || p->T < 0) return TQ_EINVAL;
   if (p->norm_dtype != TQ_F32 && p->norm_dtype != TQ_F16) return TQ_EINVAL;
@@ -99,7 +100,24 @@ tq_status tq_quantize(const tq_tables* t, const void* x, int x_dtype, const tq_p
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
   if (out->nseq == 0 || out->T == 0) return TQ_OK;
   if (!ok_ptr(x)) return TQ_EINVAL;
-  return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, stream));
+  return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, 0, out->T, false, stream));
+}
+
+tq_status tq_append(const tq_tables* t, const void* x, int x_dtype, int64_t n, const tq_packed* out,
+                    hipStream_t stream) {
+  if (t == nullptr || out == nullptr) return TQ_EINVAL;
+  const bool key = out->role == TQ_KEY;
+  if (out->role != TQ_KEY && out->role != TQ_VALUE) return TQ_EINVAL;
+  tq_status st = check_tables(t, key);
+  if (st != TQ_OK) return st;
+  st = check_packed(out, t, out->role);
+  if (st != TQ_OK) return st;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
+  // the new tokens must fit the stream's storage
+  if (n < 0 || out->capacity == 0 || n > out->capacity - out->T) return TQ_EINVAL;
+  if (out->nseq == 0 || n == 0) return TQ_OK;
+  if (!ok_ptr(x)) return TQ_EINVAL;
+  return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, out->T, n, true, stream));
 }
 
 size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }

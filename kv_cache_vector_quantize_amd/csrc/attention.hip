@@ -131,7 +131,8 @@ constexpr int kLThreads = 256;
 template <int G>
 __global__ __launch_bounds__(kLThreads) void logits_kernel(
     const float* __restrict__ cent, int bits, int m, const float* __restrict__ qr,
-    const float* __restrict__ u, int Hq, int Hkv, int64_t T, const uint32_t* __restrict__ codes,
+    const float* __restrict__ u, int Hq, int Hkv, int64_t T, int64_t Tp,
+    const uint32_t* __restrict__ codes,
     const uint32_t* __restrict__ signs, const void* norm, const void* rnorm, int nd,
     float* __restrict__ logits) {
   __shared__ float qs[G][kAD];
@@ -149,7 +150,6 @@ __global__ __launch_bounds__(kLThreads) void logits_kernel(
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kLThreads + tid;
   if (t >= T) return;
   float l[G];
-  const int64_t Tp = (T + 31) / 32 * 32;  // padded tokens per sequence of the key stream
   key_logits_one<G>(codes, signs, norm, rnorm, nd, bits, m, s * Tp + t, qs, us, cs, qjl, l);
 #pragma unroll
   for (int g = 0; g < G; ++g) logits[(h0 + g) * T + t] = l[g];
@@ -163,7 +163,8 @@ hipError_t launch_logits(const tq_tables& tk, const float* qr, const float* u, i
             static_cast<unsigned>(B * Hkv));
 #define TQ_LLAUNCH(GV)                                                                          \
   hipLaunchKernelGGL(logits_kernel<GV>, grid, dim3(kLThreads), 0, stream, tk.centroids,        \
-                     tk.bits, tk.m, qr, u, Hq, Hkv, k.T, k.codes, k.signs, k.norm, k.rnorm,    \
+                     tk.bits, tk.m, qr, u, Hq, Hkv, k.T, stream_stride(k), k.codes, k.signs,   \
+                     k.norm, k.rnorm,                                                          \
                      k.norm_dtype, logits)
   switch (G) {
     case 1: TQ_LLAUNCH(1); break;

@@ -357,12 +357,14 @@ struct BlockStream {
   uint32_t ring0;   // LDS address of this wave's packet in slot 0
   int kslot;        // bytes per ring slot (the 4 waves' packets)
 
-  // tok: padded token index of the wave's first block; value segment and
-  // value norms are empty when P has VB = 0 / NV = 0
+  // tok / tokv: index of the wave's first token in the key / value stream
+  // (sequence * its stride + token); value segment and value norms are empty
+  // when P has VB = 0 / NV = 0
   template <int KB, int VB, int NK, int NV>
   __device__ __forceinline__ void init(const uint32_t* kcodes, const uint32_t* ksigns, const void* knorm,
                                        const void* krnorm, const uint32_t* vcodes, const void* vnorm,
-                                       int64_t tok, int lane, uint32_t ring_wave0, int slot_bytes) {
+                                       int64_t tok, int64_t tokv, int lane, uint32_t ring_wave0,
+                                       int slot_bytes) {
     ring0 = ring_wave0;
     kslot = slot_bytes;
 #pragma unroll
@@ -377,7 +379,7 @@ struct BlockStream {
         p = reinterpret_cast<const char*>(ksigns) + tok * 16 + 16 * (c - 32 * KB);
         st = 4 * 32 * 16;
       } else if (c < 32 * (KB + 1 + VB)) {
-        p = reinterpret_cast<const char*>(vcodes) + (tok / 32) * 512 * VB + 16 * (c - 32 * (KB + 1));
+        p = reinterpret_cast<const char*>(vcodes) + (tokv / 32) * 512 * VB + 16 * (c - 32 * (KB + 1));
         st = 4 * 512 * VB;
       } else if (c < 32 * (KB + 1 + VB) + 4 * NK) {
         const int e = c - 32 * (KB + 1 + VB);        // 2 NK chunks per key norm row
@@ -386,7 +388,7 @@ struct BlockStream {
         st = 4 * 32 * NK;
       } else if (c < P::kChunks) {
         const int e = c - 32 * (KB + 1 + VB) - 4 * NK;
-        p = reinterpret_cast<const char*>(vnorm) + tok * NV + 16 * e;
+        p = reinterpret_cast<const char*>(vnorm) + tokv * NV + 16 * e;
         st = 4 * 32 * NV;
       }
       src[i] = p;
@@ -436,7 +438,7 @@ constexpr int ring_occupancy() {
 template <int G, int KB, int VB, int NK, int NV>
 __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>>())) void decode_mfma_kernel(
     const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
-    const float* __restrict__ cv, int64_t T, int split_len,
+    const float* __restrict__ cv, int64_t T, int64_t TpK, int64_t TpV, int split_len,
     const uint32_t* __restrict__ kcodes, const uint32_t* __restrict__ ksigns, const void* knorm,
     const void* krnorm, const uint32_t* __restrict__ vcodes, const void* vnorm, float fq, float fu,
     int nsplit, float* __restrict__ partials) {
@@ -458,15 +460,14 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
   const int64_t h0 = s * G;
   const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
   const int Ti = static_cast<int>(T);
-  const int64_t Tp = (T + 31) / 32 * 32;             // padded tokens per sequence (streams)
   const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
   const int nb_split = (t1 - t0 + 31) / 32;
   // this wave takes the split's blocks wave, wave + 4, ...
   const int nbw = (nb_split > wave) ? (nb_split - wave + 3) / 4 : 0;
 
   BlockStream<P> st;
-  st.template init<KB, VB, NK, NV>(kcodes, ksigns, knorm, krnorm, vcodes, vnorm, s * Tp + t0 + 32 * wave, lane,
-                                   lds_addr(ring) + wave * P::kBytes, kSlot);
+  st.template init<KB, VB, NK, NV>(kcodes, ksigns, knorm, krnorm, vcodes, vnorm, s * TpK + t0 + 32 * wave,
+                                   s * TpV + t0 + 32 * wave, lane, lds_addr(ring) + wave * P::kBytes, kSlot);
 #pragma unroll
   for (int jj = 0; jj + 1 < kRing; ++jj)
     if (jj < nbw) st.issue(jj, jj, lane);
@@ -521,25 +522,36 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
         sv[4 * tile + i] = fmaf(nk, cen[i], fmaf(nr, qj[i], -r_ref));
       }
     }
-    if (!full) {  // the context's last, partial block: tokens past T get no weight
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (tb + 8 * g4 + k >= Ti) sv[k] = -INFINITY;
-    }
     // ||v|| of this lane group's 8 tokens, and their largest
     float nv[8];
     uint32_t nvh[4];   // float16 norms: the 4 packed pairs as stored
-    float vm;
     if constexpr (NV == 2) {
       const uint4 w = *reinterpret_cast<const uint4*>(pk + P::kNV + 16 * g4);
       nvh[0] = w.x; nvh[1] = w.y; nvh[2] = w.z; nvh[3] = w.w;
-      const half2_t m = __builtin_elementwise_max(
-          __builtin_elementwise_max(__builtin_bit_cast(half2_t, w.x), __builtin_bit_cast(half2_t, w.y)),
-          __builtin_elementwise_max(__builtin_bit_cast(half2_t, w.z), __builtin_bit_cast(half2_t, w.w)));
-      vm = static_cast<float>(m.x > m.y ? m.x : m.y);   // norms are finite and >= 0
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) nv[k] = norm_at<NV>(pk + P::kNV, 8 * g4 + k);
+    }
+    if (!full) {
+      // the context's last, partial block: tokens past T get no weight, and
+      // whatever their storage holds (padding, an append's leftovers) is
+      // never read as a number
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (tb + 8 * g4 + k >= Ti) {
+          sv[k] = -INFINITY;
+          if constexpr (NV == 2) nvh[k / 2] &= (k & 1) ? 0x0000FFFFu : 0u;
+          else nv[k] = 0.f;
+        }
+      }
+    }
+    float vm;
+    if constexpr (NV == 2) {
+      const half2_t m = __builtin_elementwise_max(
+          __builtin_elementwise_max(__builtin_bit_cast(half2_t, nvh[0]), __builtin_bit_cast(half2_t, nvh[1])),
+          __builtin_elementwise_max(__builtin_bit_cast(half2_t, nvh[2]), __builtin_bit_cast(half2_t, nvh[3])));
+      vm = static_cast<float>(m.x > m.y ? m.x : m.y);   // norms are finite and >= 0
+    } else {
       vm = fmaxf(fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])),
                  fmaxf(fmaxf(nv[4], nv[5]), fmaxf(nv[6], nv[7])));
     }
@@ -663,7 +675,7 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
 template <int G, int KB, int NK>
 __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>())) void logits_mfma_kernel(
     const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
-    int64_t T, int split_len, const uint32_t* __restrict__ kcodes,
+    int64_t T, int64_t TpK, int split_len, const uint32_t* __restrict__ kcodes,
     const uint32_t* __restrict__ ksigns, const void* knorm, const void* krnorm, float fu,
     float* __restrict__ out) {
   using P = Packet<KB, 0, NK, 0>;
@@ -678,13 +690,12 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>(
   const int64_t s = blockIdx.y;
   const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
   const int Ti = static_cast<int>(T);
-  const int64_t Tp = (T + 31) / 32 * 32;             // padded tokens per sequence (streams)
   const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
   const int nb_split = (t1 - t0 + 31) / 32;
   const int nbw = (nb_split > wave) ? (nb_split - wave + 3) / 4 : 0;
 
   BlockStream<P> st;
-  st.template init<KB, 0, NK, 0>(kcodes, ksigns, knorm, krnorm, nullptr, nullptr, s * Tp + t0 + 32 * wave,
+  st.template init<KB, 0, NK, 0>(kcodes, ksigns, knorm, krnorm, nullptr, nullptr, s * TpK + t0 + 32 * wave, 0,
                                  lane, lds_addr(ring) + wave * P::kBytes, kSlot);
 #pragma unroll
   for (int jj = 0; jj + 1 < kRing; ++jj)
@@ -742,7 +753,8 @@ static void launch_norms(dim3 grid, hipStream_t stream, const tq_tables& tk, con
                          int len, float fq, float fu, int nsplit, float* partials) {
 #define TQ_DEC(NKB, NVB)                                                                       \
   hipLaunchKernelGGL((decode_mfma_kernel<G, KB, VB, NKB, NVB>), grid, dim3(kDecThreads), 0,    \
-                     stream, qr, u, tk.centroids, tv.centroids, k.T, len, k.codes, k.signs,    \
+                     stream, qr, u, tk.centroids, tv.centroids, k.T, stream_stride(k),         \
+                     stream_stride(v), len, k.codes, k.signs,                                  \
                      k.norm, k.rnorm, v.codes, v.norm, fq, fu, nsplit, partials)
   const bool k16 = k.norm_dtype == TQ_F16, v16 = v.norm_dtype == TQ_F16;
   if (k16 && v16) TQ_DEC(2, 2);
@@ -789,10 +801,12 @@ static hipError_t launch_logits_g(const tq_tables& tk, const float* qr, const fl
   do {                                                                                             \
     if (k.norm_dtype == TQ_F16)                                                                    \
       hipLaunchKernelGGL((logits_mfma_kernel<G, KBV, 2>), grid, dim3(kDecThreads), 0, stream, qr,  \
-                         u, tk.centroids, k.T, len, k.codes, k.signs, k.norm, k.rnorm, fu, out);   \
+                         u, tk.centroids, k.T, stream_stride(k), len, k.codes, k.signs, k.norm,    \
+                         k.rnorm, fu, out);                                                        \
     else                                                                                           \
       hipLaunchKernelGGL((logits_mfma_kernel<G, KBV, 4>), grid, dim3(kDecThreads), 0, stream, qr,  \
-                         u, tk.centroids, k.T, len, k.codes, k.signs, k.norm, k.rnorm, fu, out);   \
+                         u, tk.centroids, k.T, stream_stride(k), len, k.codes, k.signs, k.norm,    \
+                         k.rnorm, fu, out);                                                        \
   } while (0)
   switch (tk.bits) {
     case 1: TQ_LOG(1); break;

@@ -8,13 +8,21 @@
 
 namespace tq {
 
+// Tokens stored per sequence in a packed stream (its row stride).
+inline int64_t stream_stride(const tq_packed& p) {
+  return p.capacity != 0 ? static_cast<int64_t>(p.capacity) : (p.T + 31) / 32 * 32;
+}
+
 hipError_t launch_codebook(int d, int bits, double* c64, double* b64, float* c32, float* b32,
                            hipStream_t stream);
 
 hipError_t launch_rotation(int d, const double* G, double* Q, float* Q32, hipStream_t stream);
 
+// Quantizes tokens pos .. pos+n-1 of every sequence (x holds n tokens per
+// sequence) into `out`.  append = false: the whole stream (pos = 0, n = T);
+// append = true: tokens below pos are kept.
 hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,
-                           hipStream_t stream);
+                           int64_t pos, int64_t n, bool append, hipStream_t stream);
 
 // Pre-rotated queries: qr[h][d] = Pi q, u[h][m] = S qr, for nh = B*Hq heads.
 hipError_t launch_qprep(const tq_tables& tk, const void* q, int q_dtype, int nh, float* qr,

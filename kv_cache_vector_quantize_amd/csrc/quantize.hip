@@ -237,11 +237,14 @@ __device__ __forceinline__ float sumsq16(const RawX<XT>& r, const float* xv) {
   return ss;
 }
 
-template <typename XT, bool KEY, int BITS>
+// APPEND: the stream already holds tokens below pos (a separate instance, so
+// that the whole-stream launches carry none of the merge code)
+template <typename XT, bool KEY, int BITS, bool APPEND>
 __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     const float* __restrict__ rot, const float* __restrict__ sketch,
     const float* __restrict__ cent, const float* __restrict__ bnd, const XT* __restrict__ x,
-    int64_t nseq, int64_t T, uint32_t* __restrict__ codes, uint32_t* __restrict__ signs,
+    int64_t nseq, int64_t pos_arg, int64_t T, int64_t Tp, uint32_t* __restrict__ codes,
+    uint32_t* __restrict__ signs,
     void* __restrict__ norm, void* __restrict__ rnorm, int norm_dtype) {
   constexpr bool kSplitX = sizeof(XT) == 4;  // fp32 input: stage hi and lo
   constexpr int kXP = kSplitX ? 2 : 1;
@@ -279,8 +282,13 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     }
   }
 
-  const int64_t nblk = (T + kUnit - 1) / kUnit;
-  const int64_t Tp = nblk * kUnit;  // padded tokens per sequence in the packed streams
+  // x holds tokens pos .. T-1 of every sequence; the blocks that hold them are
+  // blk0 .. blk0+nblk-1 (Tp: tokens stored per sequence).  Tokens below pos
+  // keep their records, tokens from T to the block's end become padding.
+  const int64_t pos = APPEND ? pos_arg : 0;
+  const int64_t nx = T - pos;
+  const int64_t blk0 = pos / kUnit;
+  const int64_t nblk = (T + kUnit - 1) / kUnit - blk0;
   const int64_t units = nseq * nblk;
   // A-row c32 of a 32x32 tile holds token atok
   const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
@@ -291,9 +299,9 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   int64_t s = blockIdx.x / nblk, blk = blockIdx.x % nblk;
 
   auto load_raw = [&](int64_t us, int64_t ub, RawX<XT>& raw) {
-    const int64_t t0 = ub * kUnit;
-    if (us < nseq && t0 + sv < T) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + ((us * T + t0 + sv) * kD + 16 * sq));
+    const int64_t t = (blk0 + ub) * kUnit + sv;
+    if (us < nseq && t >= pos && t < T) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + ((us * nx + t - pos) * kD + 16 * sq));
 #pragma unroll
       for (int r = 0; r < RawX<XT>::kWords; ++r) raw.w[r] = src[r];
     } else {
@@ -325,9 +333,9 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   // keys: the norms of a unit are stored after the next unit's first barrier
   // (they need every wave's share of ||r||^2)
   int64_t pend_base = 0;
-  int pend_n = 0;
+  int pend_lo = 0, pend_n = 0;
   auto store_key_norms = [&](int pp) {
-    if (tid < pend_n) {  // every token of the unit, padding included
+    if (tid >= pend_lo && tid < pend_n) {  // the unit's new tokens, padding included
       const float rho2 = rho_s[pp][0][tid] + rho_s[pp][1][tid] + rho_s[pp][2][tid] + rho_s[pp][3][tid];
       const float nx = n_s[pp][tid];
       store_norm(norm, norm_dtype, pend_base + tid, nx);
@@ -338,8 +346,9 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   int par = 0;
   for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x, par ^= 1) {
     const int xb = KEY ? 0 : par;
-    const int64_t t0 = blk * kUnit;
+    const int64_t t0 = (blk0 + blk) * kUnit;
     const int nvalid = static_cast<int>((T - t0 < kUnit) ? T - t0 : kUnit);
+    const int lo = pos > t0 ? static_cast<int>(pos - t0) : 0;  // tokens t0 .. t0+lo-1 are kept
 
     // ---------------- stage: norms, power-of-two range scale, fp16 copy
     {
@@ -483,7 +492,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     if constexpr (KEY) {
       {
         const int tk = lane & 31, p = lane >> 5;
-        if (p < BITS) {  // padding tokens get the zero-vector encoding
+        if (p < BITS && tk >= lo) {  // padding tokens get the zero-vector encoding
           uint32_t* dst = codes + ((s * Tp + t0 + tk) * 4 + wave) * BITS;
           dst[p] = cw0;
           if (p + 2 < BITS) dst[p + 2] = cw1;
@@ -527,7 +536,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         sw = writelane(static_cast<uint32_t>(Z), v, sw);
         sw = writelane(static_cast<uint32_t>(Z >> 32), 16 + v, sw);
       }
-      if (lane < kUnit) {
+      if (lane >= lo && lane < kUnit) {
         // a zero vector (padding included) has every sign bit set
         if (n_s[par][lane] == 0.f) sw = 0xFFFFFFFFu;
         signs[(s * Tp + t0 + lane) * 4 + wave] = sw;
@@ -544,28 +553,39 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       }
       // lane half h holds record bits [16*BITS*h, 16*BITS*(h+1))
       const int j = 32 * wave + c32;
-      uint32_t* dst = codes + ((s * nblk + blk) * kD + j) * BITS;
+      uint32_t* dst = codes + ((s * (Tp / kUnit) + blk0 + blk) * kD + j) * BITS;
+      // record word q; its bits below BITS*lo belong to kept tokens and are
+      // merged from the stored record (only in a block that an append resumes)
+      auto put = [&](int q, uint32_t w) {
+        const int kb = BITS * lo - 32 * q;
+        if (kb > 0) {
+          const uint32_t keep = kb >= 32 ? 0xFFFFFFFFu : (1u << kb) - 1u;
+          w = (dst[q] & keep) | (w & ~keep);
+        }
+        dst[q] = w;
+      };
       if constexpr (BITS == 1) {
         const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
-        if (h == 0) dst[0] = vlo | (other << 16);
+        if (h == 0) put(0, vlo | (other << 16));
       } else if constexpr (BITS == 2) {
-        dst[h] = vlo;
+        put(h, vlo);
       } else if constexpr (BITS == 3) {
         const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
         if (h == 0) {
-          dst[0] = vlo;
-          dst[1] = vhi | (other << 16);
+          put(0, vlo);
+          put(1, vhi | (other << 16));
         } else {
-          dst[2] = (vlo >> 16) | (vhi << 16);
+          put(2, (vlo >> 16) | (vhi << 16));
         }
       } else {
-        dst[2 * h] = vlo;
-        dst[2 * h + 1] = vhi;
+        put(2 * h, vlo);
+        put(2 * h + 1, vhi);
       }
-      if (tid < kUnit) store_norm(norm, norm_dtype, s * Tp + t0 + tid, n_s[par][tid]);
+      if (tid >= lo && tid < kUnit) store_norm(norm, norm_dtype, s * Tp + t0 + tid, n_s[par][tid]);
     }
     if constexpr (KEY) {
       pend_base = s * Tp + t0;
+      pend_lo = lo;
       pend_n = kUnit;
     }
     s = s1;
@@ -588,13 +608,14 @@ static int device_cus() {
   return cus;
 }
 
-template <typename XT, bool KEY>
+template <typename XT, bool KEY, bool APPEND>
 static void launch_bits(dim3 grid, hipStream_t stream, const tq_tables& t, const void* x,
-                        const tq_packed& out) {
+                        const tq_packed& out, int64_t pos, int64_t n) {
 #define TQ_QL(B)                                                                                    \
-  hipLaunchKernelGGL((quantize_mfma_kernel<XT, KEY, B>), grid, dim3(kQThreads), 0, stream, t.rot,  \
-                     t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), out.nseq, out.T,  \
-                     out.codes, out.signs, out.norm, out.rnorm, out.norm_dtype)
+  hipLaunchKernelGGL((quantize_mfma_kernel<XT, KEY, B, APPEND>), grid, dim3(kQThreads), 0, stream, t.rot,  \
+                     t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), out.nseq, pos,    \
+                     pos + n, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,       \
+                     out.norm_dtype)
   switch (t.bits) {
     case 1: TQ_QL(1); break;
     case 2: TQ_QL(2); break;
@@ -604,21 +625,28 @@ static void launch_bits(dim3 grid, hipStream_t stream, const tq_tables& t, const
 #undef TQ_QL
 }
 
+template <bool APPEND>
+static void launch_dtypes(dim3 grid, hipStream_t stream, const tq_tables& t, const void* x, int x_dtype,
+                          const tq_packed& out, int64_t pos, int64_t n) {
+  const bool key = out.role == TQ_KEY;
+  if (x_dtype == TQ_BF16) {
+    if (key) launch_bits<uint16_t, true, APPEND>(grid, stream, t, x, out, pos, n);
+    else launch_bits<uint16_t, false, APPEND>(grid, stream, t, x, out, pos, n);
+  } else {
+    if (key) launch_bits<float, true, APPEND>(grid, stream, t, x, out, pos, n);
+    else launch_bits<float, false, APPEND>(grid, stream, t, x, out, pos, n);
+  }
+}
+
 hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,
-                           hipStream_t stream) {
-  const int64_t nblk = (out.T + kUnit - 1) / kUnit;
+                           int64_t pos, int64_t n, bool append, hipStream_t stream) {
+  const int64_t nblk = (pos + n + kUnit - 1) / kUnit - pos / kUnit;
   const int64_t units = out.nseq * nblk;
   if (units == 0) return hipSuccess;
-  const bool key = out.role == TQ_KEY;
-  const int64_t cap = (key ? 2 : 3) * static_cast<int64_t>(device_cus());
+  const int64_t cap = (out.role == TQ_KEY ? 2 : 3) * static_cast<int64_t>(device_cus());
   const dim3 grid(static_cast<unsigned>(units < cap ? units : cap));
-  if (x_dtype == TQ_BF16) {
-    if (key) launch_bits<uint16_t, true>(grid, stream, t, x, out);
-    else launch_bits<uint16_t, false>(grid, stream, t, x, out);
-  } else {
-    if (key) launch_bits<float, true>(grid, stream, t, x, out);
-    else launch_bits<float, false>(grid, stream, t, x, out);
-  }
+  if (append) launch_dtypes<true>(grid, stream, t, x, x_dtype, out, pos, n);
+  else launch_dtypes<false>(grid, stream, t, x, x_dtype, out, 0, n);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ class Packed(ctypes.Structure):
                 ("m", ctypes.c_int32), ("nseq", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("signs", ctypes.c_void_p),
                 ("norm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p),
-                ("norm_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("norm_dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 _lib = None
@@ -64,6 +64,8 @@ def lib():
     L.tq_rotation.argtypes = [i32, vp, vp, vp, vp]
     L.tq_quantize.restype = i32
     L.tq_quantize.argtypes = [ctypes.POINTER(Tables), vp, i32, ctypes.POINTER(Packed), vp]
+    L.tq_append.restype = i32
+    L.tq_append.argtypes = [ctypes.POINTER(Tables), vp, i32, i64, ctypes.POINTER(Packed), vp]
     L.tq_logits_workspace.restype = sz
     L.tq_logits_workspace.argtypes = [i32, i32, i32, i32]
     L.tq_attn_logits.restype = i32
@@ -161,9 +163,10 @@ def make_tables(G, S, bits, device="cuda"):
 
 @dataclass
 class PackedStream:
-    """A packed key or value stream.  The device buffers (``buf_*``) hold Tp =
-    32 * ceil(T / 32) tokens per sequence; ``codes``/``signs``/``norm``/``rnorm``
-    are views of the first T tokens (value codes are block records already)."""
+    """A packed key or value stream.  The device buffers (``buf_*``) hold Tp
+    tokens per sequence: the capacity, or with capacity 0, 32 * ceil(T / 32).
+    ``codes``/``signs``/``norm``/``rnorm`` are views of the first T tokens
+    (value codes are block records already)."""
     role: int
     bits: int
     d: int
@@ -175,10 +178,11 @@ class PackedStream:
     buf_norm: torch.Tensor
     buf_rnorm: Optional[torch.Tensor]
     norm_dtype: int
+    capacity: int = 0
 
     @property
     def Tp(self):
-        return padded_tokens(self.T)
+        return self.capacity if self.capacity else padded_tokens(self.T)
 
     @property
     def codes(self):
@@ -199,7 +203,7 @@ class PackedStream:
     def c_struct(self):
         return Packed(self.role, self.bits, self.d, self.m, self.nseq, self.T,
                       self.buf_codes.data_ptr(), _dp(self.buf_signs), self.buf_norm.data_ptr(),
-                      _dp(self.buf_rnorm), self.norm_dtype, 0)
+                      _dp(self.buf_rnorm), self.norm_dtype, self.capacity)
 
 
 def padded_tokens(T):
@@ -211,12 +215,16 @@ def _dp(t):
     return None if t is None else t.data_ptr()
 
 
-def alloc_packed(role, tables, nseq, T, norm_dtype="f16", device="cuda"):
-    """Allocate a packed stream in the canonical layout (see include/tq.h)."""
+def alloc_packed(role, tables, nseq, T, norm_dtype="f16", device="cuda", capacity=0):
+    """Allocate a packed stream in the canonical layout (see include/tq.h) of
+    T tokens; a nonzero capacity (a multiple of 32, >= T) sizes it for
+    tokens appended later by tq_append."""
     nd = TQ_F16 if norm_dtype == "f16" else TQ_F32
     tdt = torch.float16 if norm_dtype == "f16" else torch.float32
     d, m, bits = tables.d, tables.m, tables.bits
-    Tp = padded_tokens(T)
+    if capacity and (capacity % 32 or capacity < T):
+        raise ValueError(f"capacity {capacity} must be a multiple of 32 and >= T = {T}")
+    Tp = capacity if capacity else padded_tokens(T)
     if role == TQ_KEY:
         codes = torch.zeros((nseq, Tp, d // 32, bits), dtype=torch.int32, device=device)
         signs = torch.zeros((nseq, Tp, m // 32), dtype=torch.int32, device=device)
@@ -226,7 +234,7 @@ def alloc_packed(role, tables, nseq, T, norm_dtype="f16", device="cuda"):
         signs, rnorm = None, None
     norm = torch.zeros((nseq, Tp), dtype=tdt, device=device)
     return PackedStream(role, bits, d, m if role == TQ_KEY else 0, nseq, T, codes, signs, norm,
-                        rnorm, nd)
+                        rnorm, nd, capacity)
 
 
 # ------------------------------------------------------------ hot-path calls
@@ -236,6 +244,18 @@ def tq_quantize(tables, x, out):
     t, p = tables.c_struct(), out.c_struct()
     _check(lib().tq_quantize(ctypes.byref(t), _ptr(x), _dtype_code(x), ctypes.byref(p),
                              _stream(x.device)), "tq_quantize")
+    return out
+
+
+def tq_append(tables, x, out):
+    """Quantize x: [nseq, n, d] (float32 / bfloat16, on the device) onto the
+    end of ``out`` (which needs a capacity of at least T + n), then advance
+    ``out.T`` by n."""
+    assert x.is_contiguous() and x.dim() == 3 and x.shape[0] == out.nseq
+    t, p = tables.c_struct(), out.c_struct()
+    _check(lib().tq_append(ctypes.byref(t), _ptr(x), _dtype_code(x), x.shape[1], ctypes.byref(p),
+                           _stream(x.device)), "tq_append")
+    out.T += x.shape[1]
     return out
 
 

@@ -30,10 +30,10 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
-    assert L.tq_abi_version() == 2
+    assert L.tq_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -69,10 +69,10 @@ def _tables(tq, d=128, m=128, bits=2, reserved=0, sketch=True):
     return tq.Tables(d, m, bits, reserved, FAKE, FAKE if sketch else None, FAKE, FAKE)
 
 
-def _packed(tq, role=0, bits=2, d=128, m=128, nseq=1, T=4, nd=2):
+def _packed(tq, role=0, bits=2, d=128, m=128, nseq=1, T=4, nd=2, cap=0):
     key = role == 0
     return tq.Packed(role, bits, d, m, nseq, T, FAKE, FAKE if key else None, FAKE,
-                     FAKE if key else None, nd, 0)
+                     FAKE if key else None, nd, cap)
 
 
 @needs_no_gpu
@@ -102,6 +102,9 @@ def test_quantize_validation(L):
         (_tables(tq, m=0, sketch=False), _packed(tq, role=1, m=0, nd=7), -1),  # bad norm dtype
         (_tables(tq), _packed(tq, role=3), -1),
         (_tables(tq), _packed(tq, T=-1), -1),
+        (_tables(tq), _packed(tq, T=4, cap=48), -1),           # capacity not a multiple of 32
+        (_tables(tq), _packed(tq, T=70, cap=64), -1),          # capacity below T
+        (_tables(tq), _packed(tq, T=4, cap=-32), -1),
     ]
     for t, p, want in cases:
         assert L.tq_quantize(by(t), x, 1, by(p), None) == want, (want,)
@@ -111,6 +114,27 @@ def test_quantize_validation(L):
     assert L.tq_quantize(by(_tables(tq)), None, 1, by(_packed(tq)), None) == -1
     # empty stream: nothing to do, OK without touching any pointer
     assert L.tq_quantize(by(_tables(tq)), None, 1, by(_packed(tq, nseq=0)), None) == 0
+
+
+@needs_no_gpu
+def test_append_validation(L):
+    from kv_cache_vector_quantize_amd import tq
+    by = ctypes.byref
+    x = ctypes.c_void_p(FAKE)
+    t = _tables(tq)
+    # no capacity (a stream sized for its T only) cannot grow
+    assert L.tq_append(by(t), x, 1, 1, by(_packed(tq, T=4)), None) == -1
+    # past the capacity, or a negative count
+    assert L.tq_append(by(t), x, 1, 61, by(_packed(tq, T=4, cap=64)), None) == -1
+    assert L.tq_append(by(t), x, 1, -1, by(_packed(tq, T=4, cap=64)), None) == -1
+    assert L.tq_append(by(t), x, 1, (1 << 62), by(_packed(tq, T=4, cap=64)), None) == -1
+    # bad dtype, null input, role mismatch with the tables
+    assert L.tq_append(by(t), x, 2, 1, by(_packed(tq, T=4, cap=64)), None) == -1
+    assert L.tq_append(by(t), None, 1, 1, by(_packed(tq, T=4, cap=64)), None) == -1
+    assert L.tq_append(by(t), x, 1, 1, by(_packed(tq, T=4, cap=64, bits=3)), None) == -1
+    # nothing to do: OK without touching any pointer
+    assert L.tq_append(by(t), None, 1, 0, by(_packed(tq, T=4, cap=64)), None) == 0
+    assert L.tq_append(by(t), None, 1, 5, by(_packed(tq, nseq=0, T=4, cap=64)), None) == 0
 
 
 @needs_no_gpu

@@ -1,0 +1,247 @@
+"""GPU parity of tq_append (quantize-on-append, the cache update of each
+decode step) against the oracle and against tq_quantize of the whole stream,
+and of decode over streams that grow by append."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_vector_quantize_amd import inputs, tq
+
+from gpu_common import gpu_tables, key_records, oracle_tables, say, to64, value_records
+from parity import check_key_stream, check_value_stream, decode_close
+
+pytestmark = pytest.mark.gpu
+D = M = 128
+
+# chunk sizes of successive appends: single tokens, a block boundary crossed
+# mid-chunk, whole blocks, a chunk that ends exactly on a boundary
+CHUNKS = [1, 1, 30, 1, 32, 64, 5, 3, 63]
+
+
+def _stream(role, bits, nseq, T, nd, cap):
+    tabs = gpu_tables(D, M if role == tq.TQ_KEY else 0, bits)
+    return tabs, tq.alloc_packed(role, tabs, nseq, T, nd, capacity=cap)
+
+
+def _bufs(p):
+    return [b for b in (p.buf_codes, p.buf_signs, p.buf_norm, p.buf_rnorm) if b is not None]
+
+
+@pytest.mark.parametrize("role,bits,xdt,nd", [
+    (tq.TQ_KEY, 1, torch.bfloat16, "f16"), (tq.TQ_KEY, 2, torch.float32, "f32"),
+    (tq.TQ_KEY, 3, torch.bfloat16, "f32"), (tq.TQ_KEY, 4, torch.bfloat16, "f16"),
+    (tq.TQ_VALUE, 1, torch.bfloat16, "f16"), (tq.TQ_VALUE, 2, torch.float32, "f16"),
+    (tq.TQ_VALUE, 3, torch.bfloat16, "f32"), (tq.TQ_VALUE, 4, torch.float32, "f32")])
+def test_appends_equal_bulk_quantize(role, bits, xdt, nd):
+    """A stream built by successive appends is bit for bit the stream that
+    one tq_quantize of all its tokens writes (at the same capacity), and its
+    records match the oracle."""
+    say("append vs bulk", role, bits, xdt, nd)
+    nseq, cap = 3, 256
+    T = sum(CHUNKS)
+    g = torch.Generator().manual_seed(100 + 10 * role + bits)
+    X = (torch.randn((nseq, T, D), generator=g) * 2.0).to(xdt).cuda().contiguous()
+    tabs, bulk = _stream(role, bits, nseq, T, nd, cap)
+    tq.tq_quantize(tabs, X, bulk)
+    _, grown = _stream(role, bits, nseq, 0, nd, cap)
+    t0 = 0
+    for n in CHUNKS:
+        tq.tq_append(tabs, X[:, t0:t0 + n].contiguous(), grown)
+        t0 += n
+    torch.cuda.synchronize()
+    assert grown.T == T
+    for a, b in zip(_bufs(grown), _bufs(bulk)):
+        assert torch.equal(a, b)
+    Pi, S, c, t = oracle_tables(D, M if role == tq.TQ_KEY else 0, bits)
+    x = to64(X).reshape(-1, D)
+    if role == tq.TQ_KEY:
+        idx, sg, n_, rn = key_records(grown)
+        rep = check_key_stream(x, idx.reshape(-1, D), sg.reshape(-1, M), n_.reshape(-1),
+                               rn.reshape(-1), Pi, S, c, t, nd)
+    else:
+        idx, n_ = value_records(grown)
+        rep = check_value_stream(x, idx.reshape(-1, D), n_.reshape(-1), Pi, c, t, nd)
+    assert rep["ok"], rep
+
+
+def test_append_keeps_earlier_records_and_storage_past_the_block():
+    """An append touches only its own tokens and the padding of its last
+    block: earlier records, and storage past that block, keep their bytes."""
+    say("append locality")
+    nseq, cap, T0 = 2, 160, 45
+    g = torch.Generator().manual_seed(7)
+    X = torch.randn((nseq, T0 + 20, D), generator=g).cuda().contiguous()
+    for role, bits in ((tq.TQ_KEY, 3), (tq.TQ_VALUE, 3)):
+        tabs, p = _stream(role, bits, nseq, T0, "f16", cap)
+        tq.tq_quantize(tabs, X[:, :T0].contiguous(), p)
+        # sentinel bytes past the first two blocks
+        for b in _bufs(p):
+            if role == tq.TQ_VALUE and b is p.buf_codes:
+                b[:, 2:].fill_(0x5A5A5A5A)
+            else:
+                b[:, 64:].view(torch.int16 if b.element_size() == 2 else torch.int32).fill_(0x2A2A)
+        before = [b.clone() for b in _bufs(p)]
+        tq.tq_append(tabs, X[:, T0:T0 + 19].contiguous(), p)  # tokens 45 .. 63
+        torch.cuda.synchronize()
+        for a, b in zip(_bufs(p), before):
+            if role == tq.TQ_VALUE and a is p.buf_codes:
+                assert torch.equal(a[:, 2:], b[:, 2:]) and torch.equal(a[:, 0], b[:, 0])
+            else:
+                assert torch.equal(a[:, :T0], b[:, :T0]) and torch.equal(a[:, 64:], b[:, 64:])
+        # the block that the append resumed holds the old tokens' fields
+        ref_tabs, ref = _stream(role, bits, nseq, T0 + 19, "f16", cap)
+        tq.tq_quantize(ref_tabs, X[:, :T0 + 19].contiguous(), ref)
+        torch.cuda.synchronize()
+        for a, b in zip(_bufs(p), _bufs(ref)):
+            if role == tq.TQ_VALUE and a is p.buf_codes:
+                assert torch.equal(a[:, :2], b[:, :2])
+            else:
+                assert torch.equal(a[:, :64], b[:, :64])
+
+
+def _oracle_decode(q, pk, pv, kbits, vbits, B, Hq, Hkv):
+    Pi, S, ck, _ = oracle_tables(D, M, kbits)
+    _, _, cv, _ = oracle_tables(D, 0, vbits)
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            s = b * Hkv + h // G
+            kc = pk.codes[s].cpu().numpy().view(np.uint32)
+            ks = pk.signs[s].cpu().numpy().view(np.uint32)
+            vc = pv.codes[s].cpu().numpy().view(np.uint32)
+            out[b, h] = oracle.decode_from_records(
+                q[b:b + 1, h:h + 1], kc[None, None], ks[None, None],
+                pk.norm[s].cpu().numpy().astype(np.float64)[None, None],
+                pk.rnorm[s].cpu().numpy().astype(np.float64)[None, None], vc[None, None],
+                pv.norm[s].cpu().numpy().astype(np.float64)[None, None], pk.T, Pi, S, ck, cv)[0, 0]
+    return out
+
+
+def test_serving_loop_append_then_decode():
+    """Prefill, then steps of (append one key and one value per sequence,
+    decode one query per head) across block boundaries; every step's output
+    matches the oracle evaluated on the step's records."""
+    say("serving loop")
+    B, Hkv, G, T0, steps, cap = 2, 2, 4, 45, 40, 96
+    Hq = G * Hkv
+    nseq = B * Hkv
+    g = torch.Generator().manual_seed(21)
+    K = (torch.randn((nseq, T0 + steps, D), generator=g) * 1.5).to(torch.bfloat16).cuda()
+    V = torch.randn((nseq, T0 + steps, D), generator=g).to(torch.bfloat16).cuda()
+    Q = torch.randn((steps, B, Hq, D), generator=g).to(torch.bfloat16).cuda()
+    tk, pk = _stream(tq.TQ_KEY, 2, nseq, T0, "f16", cap)
+    tv, pv = _stream(tq.TQ_VALUE, 3, nseq, T0, "f16", cap)
+    tq.tq_quantize(tk, K[:, :T0].contiguous(), pk)
+    tq.tq_quantize(tv, V[:, :T0].contiguous(), pv)
+    for i in range(steps):
+        t = T0 + i
+        tq.tq_append(tk, K[:, t:t + 1].contiguous(), pk)
+        tq.tq_append(tv, V[:, t:t + 1].contiguous(), pv)
+        assert pk.T == pv.T == t + 1
+        got = tq.tq_attn_decode(tk, tv, Q[i], pk, pv, B, Hq, Hkv)
+        if i % 6 == 0 or t + 1 in (64, 65, 85):
+            ref = _oracle_decode(to64(Q[i]), pk, pv, 2, 3, B, Hq, Hkv)
+            ok, rel = decode_close(got.cpu().numpy().reshape(-1, D), ref.reshape(-1, D))
+            assert ok, (t + 1, rel)
+
+
+@pytest.mark.parametrize("knd,vnd", [("f16", "f16"), ("f32", "f32")])
+def test_decode_ignores_storage_past_T(knd, vnd):
+    """Whatever the storage of tokens at or past T holds (here: random code
+    bits, NaN and infinite norms) leaves decode and logits unchanged."""
+    say("decode past T", knd, vnd)
+    B, Hkv, G, T, cap = 1, 2, 2, 77, 128
+    Hq = G * Hkv
+    g = torch.Generator().manual_seed(3)
+    K = torch.randn((B * Hkv, T, D), generator=g).cuda().contiguous()
+    V = torch.randn((B * Hkv, T, D), generator=g).cuda().contiguous()
+    q = torch.randn((B, Hq, D), generator=g).cuda()
+    tk, pk = _stream(tq.TQ_KEY, 2, B * Hkv, T, knd, cap)
+    tv, pv = _stream(tq.TQ_VALUE, 2, B * Hkv, T, vnd, cap)
+    tq.tq_quantize(tk, K, pk)
+    tq.tq_quantize(tv, V, pv)
+    clean = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv)
+    clean_l = tq.tq_attn_logits(tk, q, pk, B, Hq, Hkv)
+    torch.cuda.synchronize()
+    clean, clean_l = clean.clone(), clean_l.clone()
+    rnd = torch.Generator(device="cuda").manual_seed(9)
+    for b in (pk.buf_codes, pk.buf_signs):
+        b[:, T:].random_(-2 ** 31, 2 ** 31 - 1, generator=rnd)
+    # value block 2 holds tokens 64 .. 95: randomize the fields of 77 .. 95
+    words = pv.buf_codes[:, 2]  # [nseq][d][2]: a 64-bit record per coordinate
+    junk = torch.randint(-2 ** 31, 2 ** 31 - 1, words.shape, device="cuda", dtype=torch.int32)
+    keep_bits = 2 * (T - 64)  # 2-bit fields of tokens 64 .. 76 in the first word
+    mask = torch.tensor((1 << keep_bits) - 1, dtype=torch.int64).to(torch.int32).cuda()
+    words[..., 0] = (words[..., 0] & mask) | (junk[..., 0] & ~mask)
+    words[..., 1] = junk[..., 1]
+    for b in (pk.buf_norm, pk.buf_rnorm, pv.buf_norm):
+        b[:, T:T + 8] = float("nan")
+        b[:, T + 8:] = float("inf")
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv)
+    got_l = tq.tq_attn_logits(tk, q, pk, B, Hq, Hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(got, clean)
+    assert torch.equal(got_l, clean_l)
+    ref = _oracle_decode(to64(q), pk, pv, 2, 2, B, Hq, Hkv)
+    ok, rel = decode_close(got.cpu().numpy().reshape(-1, D), ref.reshape(-1, D))
+    assert ok, rel
+
+
+def test_append_empty_and_capacity_errors():
+    say("append errors")
+    tabs, p = _stream(tq.TQ_KEY, 2, 2, 30, "f16", 32)
+    x = torch.randn((2, 3, D), device="cuda")
+    with pytest.raises(tq.TQError):
+        tq.tq_append(tabs, x, p)          # 30 + 3 > capacity 32
+    assert p.T == 30
+    tq.tq_append(tabs, x[:, :0].contiguous(), p)  # nothing to do
+    assert p.T == 30
+    tabs0, p0 = _stream(tq.TQ_KEY, 2, 2, 30, "f16", 0)
+    with pytest.raises(tq.TQError):
+        tq.tq_append(tabs0, x[:, :1].contiguous(), p0)  # no capacity to grow into
+
+
+def test_full_size_append_one_token():
+    """Decode-step cache updates at the full batched decode shape (16 x 8 kv
+    heads, 131072 cached tokens): the last 32 tokens arrive one per call.
+    Every appended key matches the oracle (32 x 128 vectors, so that the
+    parity rule's mismatch fraction is meaningful), the tokens before them
+    are untouched, and the value block they fill equals the bulk one."""
+    w = inputs.WORKLOADS[3]
+    say("full-size append", w.name)
+    n = 32
+    T0, cap = w.T - n, w.T + 32 * 32
+    K = inputs.keys(w, device="cuda").reshape(w.nseq, w.T, D)
+    Kn = K[:, T0:].transpose(0, 1).contiguous().unsqueeze(2)  # [n][nseq][1][d]
+    tabs, p = _stream(tq.TQ_KEY, w.k_bits, w.nseq, T0, w.norm_dtype, cap)
+    tq.tq_quantize(tabs, K[:, :T0].contiguous(), p)
+    torch.cuda.synchronize()
+    last = p.buf_codes[:, T0 - 32:T0].clone()
+    for i in range(n):
+        tq.tq_append(tabs, Kn[i], p)
+    torch.cuda.synchronize()
+    assert p.T == w.T
+    assert torch.equal(p.buf_codes[:, T0 - 32:T0], last)
+    Pi, S, c, t = oracle_tables(D, M, w.k_bits)
+    idx = oracle.unpack_key_codes(p.buf_codes[:, T0:w.T].cpu().numpy().view(np.uint32), D)
+    sg = oracle.unpack_signs(p.buf_signs[:, T0:w.T].cpu().numpy().view(np.uint32), M)
+    rep = check_key_stream(to64(K[:, T0:]).reshape(-1, D), idx.reshape(-1, D), sg.reshape(-1, M),
+                           p.buf_norm[:, T0:w.T].cpu().numpy().reshape(-1),
+                           p.buf_rnorm[:, T0:w.T].cpu().numpy().reshape(-1), Pi, S, c, t,
+                           w.norm_dtype)
+    assert rep["ok"], rep
+    del K, Kn
+    V = inputs.values(w, device="cuda").reshape(w.nseq, w.T, D)
+    Vn = V[:, T0:].transpose(0, 1).contiguous().unsqueeze(2)
+    tv, pv = _stream(tq.TQ_VALUE, w.v_bits, w.nseq, T0, w.norm_dtype, cap)
+    tq.tq_quantize(tv, V[:, :T0].contiguous(), pv)
+    for i in range(n):
+        tq.tq_append(tv, Vn[i], pv)
+    ref_t, ref = _stream(tq.TQ_VALUE, w.v_bits, w.nseq, w.T, w.norm_dtype, cap)
+    tq.tq_quantize(ref_t, V, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(pv.buf_codes, ref.buf_codes)
+    assert torch.equal(pv.buf_norm, ref.buf_norm)
