@@ -31,6 +31,16 @@ def table_gaussians(d=128, m=128, seed=TABLE_SEED):
     return G, S
 
 
+HADAMARD_SEED = 43
+
+
+def hadamard_signs(d=128, seed=HADAMARD_SEED):
+    """The d random signs (+-1, float64) of a randomized Walsh-Hadamard
+    rotation, from a numpy PCG64 stream of their own."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 2, size=d).astype(np.float64) * 2.0 - 1.0
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str

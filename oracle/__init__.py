@@ -28,7 +28,7 @@ invariants, brute force).  No function here is "parity unpinned".
 
 from .codebook import (beta_density, bin_mass, bin_first_moment, lloyd_max,
                        codebook_mse)
-from .rotation import rotation_from_gaussian
+from .rotation import rotation_from_gaussian, hadamard_matrix, randomized_hadamard
 from .quantize import quantize_keys, quantize_values, residual_and_sketch
 from .packing import (pack_key_codes, unpack_key_codes, pack_signs, unpack_signs,
                       pack_value_codes, unpack_value_codes, round_norms)
@@ -37,7 +37,7 @@ from .attention import (query_prep, key_logits, key_logits_from_records,
 
 __all__ = [
     "beta_density", "bin_mass", "bin_first_moment", "lloyd_max", "codebook_mse",
-    "rotation_from_gaussian", "quantize_keys", "quantize_values",
+    "rotation_from_gaussian", "hadamard_matrix", "randomized_hadamard", "quantize_keys", "quantize_values",
     "residual_and_sketch", "pack_key_codes", "unpack_key_codes", "pack_signs",
     "unpack_signs", "pack_value_codes", "unpack_value_codes", "round_norms",
     "query_prep", "key_logits", "key_logits_from_records", "decode",

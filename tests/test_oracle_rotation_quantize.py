@@ -39,6 +39,50 @@ def test_rotated_coordinate_follows_beta_law():
         assert p > 1e-3, (j, p)
 
 
+# ------------------------------------------- randomized Walsh-Hadamard variant
+def test_hadamard_sylvester_equals_closed_form():
+    # H_d[j][k] = (-1)^popcount(j & k), and H H^T = d I in exact arithmetic
+    for d in (1, 2, 4, 8, 64, 256):
+        H = oracle.hadamard_matrix(d)
+        j, k = np.indices((d, d))
+        pc = np.vectorize(lambda v: bin(int(v)).count("1"))(j & k)
+        assert np.array_equal(H, (-1.0) ** pc)
+        assert np.array_equal(H @ H.T, d * np.eye(d))
+    with pytest.raises(ValueError):
+        oracle.hadamard_matrix(96)
+
+
+def test_hadamard_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hadamard_worked_example.json")))
+    assert np.array_equal(oracle.hadamard_matrix(4), np.array(g["H4"], dtype=float))
+    assert np.array_equal(oracle.hadamard_matrix(4) @ np.array(g["x"], float), np.array(g["H4_x"], float))
+    P = oracle.randomized_hadamard(np.array(g["signs"], float))
+    assert np.allclose(P @ np.array(g["x"], float), np.array(g["PiH_x"], float), rtol=0, atol=1e-15)
+
+
+def test_randomized_hadamard_orthogonal_and_second_moment():
+    P = oracle.randomized_hadamard(inputs.hadamard_signs(128))
+    assert np.max(np.abs(P @ P.T - np.eye(128))) < 1e-14
+    # over random signs, y_j = sum_k H_jk s_k x_k / sqrt(d) has mean 0 and
+    # E[y_j^2] = ||x||^2 / d exactly (the cross terms vanish)
+    d, n = 16, 40000
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(d)
+    ys = np.stack([oracle.randomized_hadamard(rng.integers(0, 2, d) * 2.0 - 1.0) @ x for _ in range(n)])
+    var = np.sum(x * x) / d
+    # the sample mean of y_j^2 has standard deviation below sqrt(3) var / sqrt(n)
+    assert np.all(np.abs(np.mean(ys ** 2, axis=0) - var) < 5 * np.sqrt(3.0) * var / np.sqrt(n))
+    assert np.all(np.abs(np.mean(ys, axis=0)) < 5 * np.sqrt(var / n))
+    with pytest.raises(ValueError):
+        oracle.randomized_hadamard(np.array([1.0, 0.5]))
+
+
+def test_hadamard_signs_input():
+    s = inputs.hadamard_signs(128)
+    assert s.shape == (128,) and set(np.unique(s)) == {-1.0, 1.0}
+    assert np.array_equal(s, inputs.hadamard_signs(128))
+
+
 # ---------------------------------------------------------------- quantizer
 def _tables(d, m, bits, seed=42):
     G, S = inputs.table_gaussians(d, m, seed=seed)
