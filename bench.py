@@ -59,7 +59,7 @@ def traffic_from_profiles(kernel_src, kernel_name):
         return None
 
 
-def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0):
+def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0, hadamard=False):
     """The oracle, untouched, on a bounded sample of the same workload.  Each
     timed stage of the step gets a share of `budget_s`: quantize + pack chunks
     of 32768 vectors, logits of one KV head's query group over chunks of its
@@ -78,7 +78,8 @@ def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0):
     share = budget_s / len(stages)
     notes, cpu_s = [], 0.0
     with threadpool_limits(limits=1):
-        Pi = oracle.rotation_from_gaussian(G)
+        Pi = (oracle.randomized_hadamard(inputs.hadamard_signs(d)) if hadamard
+              else oracle.rotation_from_gaussian(G))
         ck, tk = oracle.lloyd_max(d, w.k_bits)
         cv, tv = (oracle.lloyd_max(d, w.v_bits) if w.v_bits else (None, None))
         for st in stages:
@@ -214,6 +215,9 @@ def main():
     ap.add_argument("--config", type=int, default=3,
                     help="workload number 1-5 (default 3: batched quantize + decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotation", choices=["qr", "hadamard"], default="qr",
+                    help="qr: Pi = Q of a seeded Gaussian (the method as described); hadamard: the "
+                         "randomized Walsh-Hadamard variant H diag(s) / sqrt(d)")
     ap.add_argument("--serve-steps", type=int, default=32,
                     help="decode workloads: also time this many serving steps (append one key "
                          "and one value per sequence, then decode) ending at the full context")
@@ -241,8 +245,11 @@ def main():
     xb = 2 if w.x_dtype == "bf16" else 4
     log("workload", w.name)
     G, S = inputs.table_gaussians(d, m)
-    tk = tq.make_tables(G, S, w.k_bits, dev)
-    tv = tq.make_tables(G, None, w.v_bits, dev) if w.v_bits else None
+    had = args.rotation == "hadamard"
+    hs = inputs.hadamard_signs(d) if had else None
+    tk = tq.make_tables(G, S, w.k_bits, dev, hadamard_signs=hs)
+    tv = tq.make_tables(G, None, w.v_bits, dev, hadamard_signs=hs) if w.v_bits else None
+    rtag = ", hadamard" if had else ""
     t0 = time.perf_counter()
     K = inputs.keys(w, device=dev).reshape(w.nseq, w.T, d)
     V = inputs.values(w, device=dev).reshape(w.nseq, w.T, d) if w.v_bits else None
@@ -260,12 +267,12 @@ def main():
     if w.quantize_timed:
         stages.append({"name": "quantize_k", "bytes": nvec * (d * xb + kb), "units": nvec,
                        "fn": lambda: tq.tq_quantize(tk, K, pk),
-                       "kernel": f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}>",
+                       "kernel": f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>",
                        "flop_per_unit": 2 * d * d + 2 * m * d})
         if w.v_bits:
             stages.append({"name": "quantize_v", "bytes": nvec * (d * xb + vb), "units": nvec,
                            "fn": lambda: tq.tq_quantize(tv, V, pv),
-                           "kernel": f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}>",
+                           "kernel": f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}{rtag}>",
                            "flop_per_unit": 2 * d * d})
     else:
         tq.tq_quantize(tk, K, pk)
@@ -372,7 +379,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "d": d,
                    "k_bits": w.k_bits, "qjl_m": m, "v_bits": w.v_bits, "norms": w.norm_dtype,
-                   "inputs": inputs_desc, "step": [st["name"] for st in stages],
+                   "inputs": inputs_desc, "rotation": args.rotation,
+                   "step": [st["name"] for st in stages],
                    "parallelism": "1 GPU"},
         "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
         "stages": stage_report,
@@ -382,7 +390,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded CPU sample")
-        res["cpu_baseline"] = cpu_baseline(w, stages, K, V, pk, pv, q)
+        res["cpu_baseline"] = cpu_baseline(w, stages, K, V, pk, pv, q, hadamard=had)
     print(json.dumps(res), flush=True)
 
 

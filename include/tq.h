@@ -82,12 +82,18 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 typedef enum { TQ_KEY = 0, TQ_VALUE = 1 } tq_role;
 
+/* What `rot` of a tq_tables holds. */
+typedef enum {
+  TQ_ROT_DENSE = 0,     /* any orthogonal Pi (tq_rotation: QR of a Gaussian)       */
+  TQ_ROT_HADAMARD = 1   /* H_d diag(s) / sqrt(d) as written by tq_hadamard_rotation */
+} tq_rotation_kind;
+
 /* Data-independent tables of one stream (device memory, caller-owned). */
 typedef struct {
   int32_t d;               /* head dimension; the hot-path kernels support 128   */
   int32_t m;               /* sketch rows: 128 for keys, 0 for values             */
   int32_t bits;            /* code width, 1..4                                    */
-  int32_t reserved;        /* must be 0                                           */
+  int32_t rot_kind;        /* tq_rotation_kind of rot                             */
   const float *rot;        /* Pi, d x d row-major; y = Pi x                       */
   const float *sketch;     /* S, m x d row-major, iid N(0,1); NULL when m == 0    */
   const float *centroids;  /* 2^bits ascending, unit-sphere scale                 */
@@ -147,6 +153,21 @@ tq_status tq_codebook(int d, int bits, double *centroids64, double *bounds64,
  *   rot32  out, d x d row-major floats (round to nearest), or NULL
  */
 tq_status tq_rotation(int d, const double *G, double *rot64, float *rot32, hipStream_t stream);
+
+/*
+ * tq_hadamard_rotation -- the randomized Walsh-Hadamard rotation
+ * Pi_H = H_d diag(s) / sqrt(d), H_d Sylvester's Hadamard matrix
+ * (H_d[j][k] = (-1)^popcount(j & k)), s a vector of d random signs.
+ * Cites: qiita page, "What you hit when you try it" (implementations that
+ * stand a Walsh-Hadamard transform in for the rotation).  Setup helper;
+ * tables with rot_kind TQ_ROT_HADAMARD must hold its output.  Since
+ * sqrt(d) Pi_H has entries +-1, exact in float16, quantization rotates with
+ * one matrix-core product instead of the hi + lo pair a general Pi needs.
+ *   d      power of two, 2..4096
+ *   signs  in, d floats; s_k = -1 where the sign bit of signs[k] is set, else +1
+ *   rot32  out, d x d row-major floats: +-(1/sqrt(d)) rounded to nearest
+ */
+tq_status tq_hadamard_rotation(int d, const float *signs, float *rot32, hipStream_t stream);
 
 /*
  * tq_quantize -- online quantization of key or value vectors.

@@ -22,7 +22,8 @@ tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
 // Tables of a stream as the hot-path kernels need them.
 tq_status check_tables(const tq_tables* t, bool key) {
   if (t == nullptr) return TQ_EINVAL;
-  if (t->reserved != 0 || t->bits < 1 || t->bits > 4 || t->d <= 0 || t->d % 32 != 0) return TQ_EINVAL;
+  if (t->rot_kind != TQ_ROT_DENSE && t->rot_kind != TQ_ROT_HADAMARD) return TQ_EINVAL;
+  if (t->bits < 1 || t->bits > 4 || t->d <= 0 || t->d % 32 != 0) return TQ_EINVAL;
   if (t->m < 0 || t->m % 32 != 0) return TQ_EINVAL;
   if (key ? t->m == 0 : t->m != 0) return TQ_EINVAL;
   if (!ok_ptr(t->rot) || !ok_ptr(t->centroids) || !ok_ptr(t->bounds)) return TQ_EINVAL;
@@ -86,6 +87,11 @@ tq_status tq_codebook(int d, int bits, double* centroids64, double* bounds64, fl
 tq_status tq_rotation(int d, const double* G, double* rot64, float* rot32, hipStream_t stream) {
   if (d < 2 || d > 128 || !ok_ptr(G) || !ok_ptr(rot64) || !ok_opt(rot32)) return TQ_EINVAL;
   return from_hip(tq::launch_rotation(d, G, rot64, rot32, stream));
+}
+
+tq_status tq_hadamard_rotation(int d, const float* signs, float* rot32, hipStream_t stream) {
+  if (d < 2 || d > 4096 || (d & (d - 1)) != 0 || !ok_ptr(signs) || !ok_ptr(rot32)) return TQ_EINVAL;
+  return from_hip(tq::launch_hadamard_rotation(d, signs, rot32, stream));
 }
 
 tq_status tq_quantize(const tq_tables* t, const void* x, int x_dtype, const tq_packed* out,
@@ -166,7 +172,7 @@ tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q
   if (st != TQ_OK) return st;
   st = check_tables(tv, false);
   if (st != TQ_OK) return st;
-  if (tv->d != tk->d) return TQ_EINVAL;
+  if (tv->d != tk->d || tv->rot_kind != tk->rot_kind) return TQ_EINVAL;
   st = check_packed(k, tk, TQ_KEY);
   if (st != TQ_OK) return st;
   st = check_packed(v, tv, TQ_VALUE);

@@ -18,6 +18,8 @@ hipError_t launch_codebook(int d, int bits, double* c64, double* b64, float* c32
 
 hipError_t launch_rotation(int d, const double* G, double* Q, float* Q32, hipStream_t stream);
 
+hipError_t launch_hadamard_rotation(int d, const float* signs, float* rot32, hipStream_t stream);
+
 // Quantizes tokens pos .. pos+n-1 of every sequence (x holds n tokens per
 // sequence) into `out`.  append = false: the whole stream (pos = 0, n = T);
 // append = true: tokens below pos are kept.

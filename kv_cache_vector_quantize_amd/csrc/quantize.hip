@@ -82,6 +82,19 @@ __device__ __forceinline__ void split_frag(const float* p, float sc, qhalf8& hi,
   lo = qu4(l[0], l[1], l[2], l[3]);
 }
 
+// B fragment of a Walsh-Hadamard rotation: the signs of 8 entries of Pi_H
+// (+-1/sqrt(d)) as fp16 +-1, exact, so one product replaces the hi + lo pair
+__device__ __forceinline__ void sign_frag(const float* p, qhalf8& hi) {
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = (__float_as_uint(p[2 * i]) >> 16) & 0x8000u;
+    const uint32_t b = (__float_as_uint(p[2 * i + 1]) >> 16) & 0x8000u;
+    h[i] = (a | 0x3C00u) | ((b | 0x3C00u) << 16);   // fp16 1.0 = 0x3C00
+  }
+  hi = qu4(h[0], h[1], h[2], h[3]);
+}
+
 // fp16(a - hi.x), fp16(b - hi.y): the lo halves of an fp16 hi + lo split,
 // each from one mixed-precision fma (hi read as fp16, a and b as fp32)
 __device__ __forceinline__ qhalf2 split_lo(qhalf2 hi, float a, float b) {
@@ -238,8 +251,10 @@ __device__ __forceinline__ float sumsq16(const RawX<XT>& r, const float* xv) {
 }
 
 // APPEND: the stream already holds tokens below pos (a separate instance, so
-// that the whole-stream launches carry none of the merge code)
-template <typename XT, bool KEY, int BITS, bool APPEND>
+// that the whole-stream launches carry none of the merge code).  HAD: Pi is
+// a randomized Walsh-Hadamard rotation, whose sqrt(d) Pi has entries +-1:
+// one fp16 product rotates exactly, where a general Pi needs hi + lo.
+template <typename XT, bool KEY, int BITS, bool APPEND, bool HAD>
 __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     const float* __restrict__ rot, const float* __restrict__ sketch,
     const float* __restrict__ cent, const float* __restrict__ bnd, const XT* __restrict__ x,
@@ -253,7 +268,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   constexpr int kXB = KEY ? 1 : 2;
   __shared__ __align__(16) _Float16 xs[kXB][kXP][kUnit][kRowH];
   __shared__ __align__(16) _Float16 rs[KEY ? 2 : 1][KEY ? kUnit : 1][KEY ? kRowH : 8];
-  __shared__ __align__(16) float rinv_s[2][kUnit];  // kResScale / (kPiScale * ||scaled x||); 0 for x = 0
+  __shared__ __align__(16) float rinv_s[2][kUnit];  // kResScale / (rotation scale * ||scaled x||); 0 for x = 0
   __shared__ float n_s[2][kUnit];                 // ||x||, by unit parity
   __shared__ float rho_s[2][4][KEY ? kUnit : 1];  // per-wave sums of the residual squares (x256^2)
 
@@ -270,12 +285,15 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
 
   // B fragments: Pi^T for coordinates j = 32*wave + c32 and (keys) S^T for
   // sketch rows i = 32*wave + c32; K-step c covers input index 16c + 8h + e.
-  qhalf8 bph[8], bpl[8];
+  qhalf8 bph[8], bpl[HAD ? 1 : 8];
   qhalf8 bsh[KEY ? 8 : 1], bsl[KEY ? 8 : 1];
   {
     const int j = 32 * wave + c32;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) split_frag(rot + j * kD + 16 * c + 8 * h, kPiScale, bph[c], bpl[c]);
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (HAD) sign_frag(rot + j * kD + 16 * c + 8 * h, bph[c]);
+      else split_frag(rot + j * kD + 16 * c + 8 * h, kPiScale, bph[c], bpl[c]);
+    }
     if constexpr (KEY) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) split_frag(sketch + j * kD + 16 * c + 8 * h, 1.f, bsh[c], bsl[c]);
@@ -388,7 +406,10 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       if (sq == 0) {
         const float nr = sqrtf(ss);
         n_s[par][sv] = ldexpf(nr, -sh);
-        rinv_s[par][sv] = (ss > 0.f) ? (kResScale / kPiScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
+        // the rotation product is kPiScale Pi x (dense) or sqrt(d) Pi_H x (HAD)
+        static_assert(kD == 128, "sqrt(kD) below");
+        constexpr float kRotScale = HAD ? 11.313708498984761f : kPiScale;
+        rinv_s[par][sv] = (ss > 0.f) ? (kResScale / kRotScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
       }
       uint32_t wh[8], wl[8];
 #pragma unroll
@@ -427,7 +448,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     for (int c = 0; c < 8; ++c) {
       const qhalf8 ah = *reinterpret_cast<const qhalf8*>(&xs[xb][0][atok][16 * c + 8 * h]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bph[c], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bpl[c], acc, 0, 0, 0);
+      if constexpr (!HAD) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bpl[c], acc, 0, 0, 0);
       if constexpr (kSplitX) {
         const qhalf8 al = *reinterpret_cast<const qhalf8*>(&xs[xb][kXP - 1][atok][16 * c + 8 * h]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bph[c], acc, 0, 0, 0);
@@ -608,11 +629,11 @@ static int device_cus() {
   return cus;
 }
 
-template <typename XT, bool KEY, bool APPEND>
+template <typename XT, bool KEY, bool APPEND, bool HAD>
 static void launch_bits(dim3 grid, hipStream_t stream, const tq_tables& t, const void* x,
                         const tq_packed& out, int64_t pos, int64_t n) {
 #define TQ_QL(B)                                                                                    \
-  hipLaunchKernelGGL((quantize_mfma_kernel<XT, KEY, B, APPEND>), grid, dim3(kQThreads), 0, stream, t.rot,  \
+  hipLaunchKernelGGL((quantize_mfma_kernel<XT, KEY, B, APPEND, HAD>), grid, dim3(kQThreads), 0, stream, t.rot,  \
                      t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), out.nseq, pos,    \
                      pos + n, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,       \
                      out.norm_dtype)
@@ -625,16 +646,16 @@ static void launch_bits(dim3 grid, hipStream_t stream, const tq_tables& t, const
 #undef TQ_QL
 }
 
-template <bool APPEND>
+template <bool APPEND, bool HAD>
 static void launch_dtypes(dim3 grid, hipStream_t stream, const tq_tables& t, const void* x, int x_dtype,
                           const tq_packed& out, int64_t pos, int64_t n) {
   const bool key = out.role == TQ_KEY;
   if (x_dtype == TQ_BF16) {
-    if (key) launch_bits<uint16_t, true, APPEND>(grid, stream, t, x, out, pos, n);
-    else launch_bits<uint16_t, false, APPEND>(grid, stream, t, x, out, pos, n);
+    if (key) launch_bits<uint16_t, true, APPEND, HAD>(grid, stream, t, x, out, pos, n);
+    else launch_bits<uint16_t, false, APPEND, HAD>(grid, stream, t, x, out, pos, n);
   } else {
-    if (key) launch_bits<float, true, APPEND>(grid, stream, t, x, out, pos, n);
-    else launch_bits<float, false, APPEND>(grid, stream, t, x, out, pos, n);
+    if (key) launch_bits<float, true, APPEND, HAD>(grid, stream, t, x, out, pos, n);
+    else launch_bits<float, false, APPEND, HAD>(grid, stream, t, x, out, pos, n);
   }
 }
 
@@ -645,8 +666,14 @@ hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const
   if (units == 0) return hipSuccess;
   const int64_t cap = (out.role == TQ_KEY ? 2 : 3) * static_cast<int64_t>(device_cus());
   const dim3 grid(static_cast<unsigned>(units < cap ? units : cap));
-  if (append) launch_dtypes<true>(grid, stream, t, x, x_dtype, out, pos, n);
-  else launch_dtypes<false>(grid, stream, t, x, x_dtype, out, 0, n);
+  const bool had = t.rot_kind == TQ_ROT_HADAMARD;
+  if (append) {
+    if (had) launch_dtypes<true, true>(grid, stream, t, x, x_dtype, out, pos, n);
+    else launch_dtypes<true, false>(grid, stream, t, x, x_dtype, out, pos, n);
+  } else {
+    if (had) launch_dtypes<false, true>(grid, stream, t, x, x_dtype, out, 0, n);
+    else launch_dtypes<false, false>(grid, stream, t, x, x_dtype, out, 0, n);
+  }
   return hipGetLastError();
 }
 

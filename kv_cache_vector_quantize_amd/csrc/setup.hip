@@ -209,4 +209,23 @@ hipError_t launch_rotation(int d, const double* G, double* Q, float* Q32, hipStr
   return hipGetLastError();
 }
 
+// Randomized Walsh-Hadamard rotation (qiita page, "What you hit when you try
+// it"): entry (j, k) = (-1)^popcount(j & k) * s_k / sqrt(d), one thread per
+// entry; 1/sqrt(d) in float64, then rounded once to float32.
+__global__ void hadamard_rotation_kernel(int d, const float* __restrict__ signs, float* __restrict__ rot) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= static_cast<int64_t>(d) * d) return;
+  const int j = static_cast<int>(e / d), k = static_cast<int>(e % d);
+  const bool neg = (__popc(static_cast<unsigned>(j & k)) & 1) != (signbit(signs[k]) != 0);
+  const double v = 1.0 / sqrt(static_cast<double>(d));
+  rot[e] = static_cast<float>(neg ? -v : v);
+}
+
+hipError_t launch_hadamard_rotation(int d, const float* signs, float* rot32, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(d) * d;
+  hipLaunchKernelGGL(hadamard_rotation_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     stream, d, signs, rot32);
+  return hipGetLastError();
+}
+
 }  // namespace tq

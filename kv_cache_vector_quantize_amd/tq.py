@@ -19,6 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2, -3, -4
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 TQ_KEY, TQ_VALUE = 0, 1
+TQ_ROT_DENSE, TQ_ROT_HADAMARD = 0, 1
 
 
 class TQError(RuntimeError):
@@ -29,7 +30,7 @@ class TQError(RuntimeError):
 
 class Tables(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("m", ctypes.c_int32), ("bits", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("rot", ctypes.c_void_p),
+                ("rot_kind", ctypes.c_int32), ("rot", ctypes.c_void_p),
                 ("sketch", ctypes.c_void_p), ("centroids", ctypes.c_void_p),
                 ("bounds", ctypes.c_void_p)]
 
@@ -62,6 +63,8 @@ def lib():
     L.tq_codebook.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     L.tq_rotation.restype = i32
     L.tq_rotation.argtypes = [i32, vp, vp, vp, vp]
+    L.tq_hadamard_rotation.restype = i32
+    L.tq_hadamard_rotation.argtypes = [i32, vp, vp, vp]
     L.tq_quantize.restype = i32
     L.tq_quantize.argtypes = [ctypes.POINTER(Tables), vp, i32, ctypes.POINTER(Packed), vp]
     L.tq_append.restype = i32
@@ -131,6 +134,15 @@ def tq_rotation(G):
     return r64, r32
 
 
+def tq_hadamard_rotation(signs):
+    """signs: device float32 [d] (+-1).  Returns rot32 = H_d diag(signs) / sqrt(d)."""
+    signs = signs.contiguous()
+    d = signs.shape[0]
+    r32 = torch.empty((d, d), dtype=torch.float32, device=signs.device)
+    _check(lib().tq_hadamard_rotation(d, _ptr(signs), _ptr(r32), _stream()), "tq_hadamard_rotation")
+    return r32
+
+
 @dataclass
 class StreamTables:
     """Device tables of one stream (tensors kept alive here)."""
@@ -141,24 +153,30 @@ class StreamTables:
     sketch: Optional[torch.Tensor]
     centroids: torch.Tensor
     bounds: torch.Tensor
+    rot_kind: int = TQ_ROT_DENSE
 
     def c_struct(self):
-        return Tables(self.d, self.m, self.bits, 0, self.rot.data_ptr(),
+        return Tables(self.d, self.m, self.bits, self.rot_kind, self.rot.data_ptr(),
                       None if self.sketch is None else self.sketch.data_ptr(),
                       self.centroids.data_ptr(), self.bounds.data_ptr())
 
 
-def make_tables(G, S, bits, device="cuda"):
-    """Rotation from the Gaussian G (numpy/torch float64 [d, d]), sketch S
-    (float64 [m, d] or None) and the Lloyd-Max codebook, all built on the
-    device by the library."""
-    G = torch.as_tensor(G, dtype=torch.float64).to(device)
-    _, rot32 = tq_rotation(G)
-    d = G.shape[0]
+def make_tables(G, S, bits, device="cuda", hadamard_signs=None):
+    """Rotation from the Gaussian G (numpy/torch float64 [d, d]) -- or, given
+    hadamard_signs (d values +-1), the randomized Walsh-Hadamard rotation
+    from them (G is then unused) -- sketch S (float64 [m, d] or None) and the
+    Lloyd-Max codebook, all built on the device by the library."""
+    if hadamard_signs is not None:
+        sg = torch.as_tensor(hadamard_signs, dtype=torch.float32).to(device)
+        rot32, kind = tq_hadamard_rotation(sg), TQ_ROT_HADAMARD
+    else:
+        _, rot32 = tq_rotation(torch.as_tensor(G, dtype=torch.float64).to(device))
+        kind = TQ_ROT_DENSE
+    d = rot32.shape[0]
     sk = None if S is None else torch.as_tensor(S, dtype=torch.float64).to(device).float().contiguous()
     _, _, c32, b32 = tq_codebook(d, bits, device)
     b32 = b32.clone() if b32.numel() else torch.zeros(1, dtype=torch.float32, device=device)
-    return StreamTables(d, 0 if sk is None else sk.shape[0], bits, rot32, sk, c32, b32)
+    return StreamTables(d, 0 if sk is None else sk.shape[0], bits, rot32, sk, c32, b32, kind)
 
 
 @dataclass

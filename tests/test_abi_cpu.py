@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert L.tq_abi_version() == 3
@@ -65,8 +65,8 @@ needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                                   reason="fake device pointers are only used without a GPU")
 
 
-def _tables(tq, d=128, m=128, bits=2, reserved=0, sketch=True):
-    return tq.Tables(d, m, bits, reserved, FAKE, FAKE if sketch else None, FAKE, FAKE)
+def _tables(tq, d=128, m=128, bits=2, rot_kind=0, sketch=True):
+    return tq.Tables(d, m, bits, rot_kind, FAKE, FAKE if sketch else None, FAKE, FAKE)
 
 
 def _packed(tq, role=0, bits=2, d=128, m=128, nseq=1, T=4, nd=2, cap=0):
@@ -85,6 +85,10 @@ def test_codebook_and_rotation_validation(L):
     assert L.tq_codebook(128, 2, None, None, vp(FAKE + 4), vp(FAKE), None) == -1  # misaligned
     assert L.tq_rotation(129, vp(FAKE), vp(FAKE), None, None) == -1
     assert L.tq_rotation(128, None, vp(FAKE), None, None) == -1
+    assert L.tq_hadamard_rotation(96, vp(FAKE), vp(FAKE), None) == -1     # not a power of two
+    assert L.tq_hadamard_rotation(8192, vp(FAKE), vp(FAKE), None) == -1
+    assert L.tq_hadamard_rotation(128, None, vp(FAKE), None) == -1
+    assert L.tq_hadamard_rotation(128, vp(FAKE), vp(FAKE + 4), None) == -1  # misaligned
 
 
 @needs_no_gpu
@@ -93,7 +97,7 @@ def test_quantize_validation(L):
     by = ctypes.byref
     x = ctypes.c_void_p(FAKE)
     cases = [
-        (_tables(tq, reserved=1), _packed(tq), -1),
+        (_tables(tq, rot_kind=2), _packed(tq), -1),            # unknown rotation kind
         (_tables(tq, bits=5), _packed(tq, bits=5), -1),
         (_tables(tq, d=96), _packed(tq, d=96), -2),            # valid, unsupported d
         (_tables(tq, m=64), _packed(tq, m=64), -2),            # unsupported sketch size
@@ -163,6 +167,10 @@ def test_attention_validation(L):
     assert L.tq_attn_decode(*args(float("nan"), pk, pv, ws)) == -1
     assert L.tq_attn_decode(*args(0.1, pk, _packed(tq, role=1, m=0, bits=3, nseq=16, T=65), ws)) == -1
     assert L.tq_attn_decode(*args(0.1, pk, pv, ws - 1)) == -3
+    # keys and values rotated differently (dense vs Walsh-Hadamard)
+    tvh = _tables(tq, m=0, sketch=False, bits=3, rot_kind=1)
+    assert L.tq_attn_decode(by(tk), by(tvh), q, 1, 2, 32, 8, by(pk), by(pv), 0.1, vp(FAKE), vp(FAKE),
+                            ws, None) == -1
     assert L.tq_attn_decode(*args(0.1, _packed(tq, nseq=16, T=0),
                                   _packed(tq, role=1, m=0, bits=3, nseq=16, T=0), ws)) == -1
     # 16 query heads per kv head: fine for logits, unsupported for decode
