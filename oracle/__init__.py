@@ -16,7 +16,8 @@ Quantization with Near-optimal Distortion Rate"):
 * a2a-mcp.org/blog/what-is-turboquant-ja ("P3") -- "How it works",
   Stage 1 (random rotation, Beta((d-1)/2,(d-1)/2) law, Lloyd-Max) and
   Stage 2 (1-bit QJL on the residual); "How to implement", item 1
-  (precomputed codebook, pre-rotated query, dots straight from indices).
+  (precomputed codebook, pre-rotated query, dots straight from indices);
+  "Benchmarks" (vector search judged by top-k recall).
 
 Every function is written in the order the pages give the steps; the
 readings taken where the pages are silent are listed in each docstring.
@@ -34,6 +35,7 @@ from .packing import (pack_key_codes, unpack_key_codes, pack_signs, unpack_signs
                       pack_value_codes, unpack_value_codes, round_norms)
 from .attention import (query_prep, key_logits, key_logits_from_records,
                         decode, decode_from_records, qjl_scale)
+from .search import topk, search_from_records
 
 __all__ = [
     "beta_density", "bin_mass", "bin_first_moment", "lloyd_max", "codebook_mse",
@@ -41,5 +43,5 @@ __all__ = [
     "residual_and_sketch", "pack_key_codes", "unpack_key_codes", "pack_signs",
     "unpack_signs", "pack_value_codes", "unpack_value_codes", "round_norms",
     "query_prep", "key_logits", "key_logits_from_records", "decode",
-    "decode_from_records", "qjl_scale",
+    "decode_from_records", "qjl_scale", "topk", "search_from_records",
 ]
