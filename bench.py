@@ -59,7 +59,7 @@ def traffic_from_profiles(kernel_src, kernel_name):
         return None
 
 
-def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0, hadamard=False):
+def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0, hadamard=False, logits=None):
     """The oracle, untouched, on a bounded sample of the same workload.  Each
     timed stage of the step gets a share of `budget_s`: quantize + pack chunks
     of 32768 vectors, logits of one KV head's query group over chunks of its
@@ -103,6 +103,13 @@ def cpu_baseline(w, stages, K, V, pk, pv, q, budget_s=12.0, hadamard=False):
                     n += chunk
                 sample_bytes = n * st["bytes"] / st["units"]
                 notes.append(f"{name}: {n} vectors in {t_s:.1f} s ({n / t_s / 1e6:.3f} Mvec/s)")
+            elif name == "topk":   # one row of the GPU's scores through the oracle's top-k
+                row = logits.view(-1, w.T)[0:1].double().cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.topk(row, w.topk)
+                t_s = time.perf_counter() - t0
+                sample_bytes = st["bytes"] / (w.B * w.Hq)
+                notes.append(f"topk: one row of {w.T} scores in {t_s:.2f} s")
             elif name == "logits":
                 G_ = w.Hq // w.Hkv
                 chunk, n, t_s = 4096, 0, 0.0
@@ -283,9 +290,21 @@ def main():
         lws = torch.empty(max(tq.logits_workspace_bytes(w.B, w.Hq, d, m), 256), dtype=torch.uint8,
                           device=dev)
         stages.append({"name": "logits", "bytes": nvec * kb + w.B * w.Hq * w.T * 4 + qbytes,
-                       "units": nvec, "kernel": f"logits_kernel<{w.Hq // w.Hkv}>",
+                       "units": nvec,
+                       "kernel": (f"logits_mfma_kernel<{w.Hq // w.Hkv}, {w.k_bits}, {nb}>" if w.Hq // w.Hkv <= 8
+                                  else f"logits_kernel<{w.Hq // w.Hkv}>"),
                        "fn": lambda: tq.tq_attn_logits(tk, q, pk, w.B, w.Hq, w.Hkv, ws=lws, out=logits),
                        "flop_per_unit": 2 * (w.Hq // w.Hkv) * (d + m)})
+    if w.topk:
+        rows = w.B * w.Hq
+        scores2d = logits.view(rows, w.T)
+        tws = torch.empty(tq.topk_workspace_bytes(rows, w.T, w.topk), dtype=torch.uint8, device=dev)
+        t_idx = torch.empty((rows, w.topk), dtype=torch.int32, device=dev)
+        t_val = torch.empty((rows, w.topk), dtype=torch.float32, device=dev)
+        stages.append({"name": "topk", "bytes": rows * w.T * 4 + rows * w.topk * 8, "units": rows * w.T,
+                       "kernel": "topk_chunk_kernel<16>",
+                       "fn": lambda: tq.tq_topk(scores2d, w.topk, ws=tws, idx=t_idx, val=t_val),
+                       "flop_per_unit": 0})
     if w.decode:
         ws = torch.empty(tq.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.T, d, m), dtype=torch.uint8,
                          device=dev)
@@ -348,7 +367,7 @@ def main():
     # the fp16 matrix-core peak all of them are bandwidth-bound.
     dom = max(stages, key=lambda st: st["ms"])
     src = {"quantize_k": "quantize.hip", "quantize_v": "quantize.hip", "logits": "attention.hip",
-           "decode": "decode.hip"}[dom["name"]]
+           "decode": "decode.hip", "topk": "topk.hip"}[dom["name"]]
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
     roofline = {
         "kernel": dom["kernel"],
@@ -369,6 +388,8 @@ def main():
     for st in stages:
         if st["name"].startswith("quantize"):
             stage_report[st["name"]]["mvec_s"] = round(nvec / (st["ms"] * 1e-3) / 1e6, 2)
+        elif st["name"] == "topk":
+            stage_report[st["name"]]["scores_per_s"] = round(st["units"] / (st["ms"] * 1e-3), 1)
         else:
             stage_report[st["name"]]["qhead_tokens_per_s"] = round(w.B * w.Hq * w.T / (st["ms"] * 1e-3), 1)
     inputs_desc = ("fp32" if w.x_dtype == "f32" else "bf16") + " K" + (", V" if w.v_bits else "") + ", Q"
@@ -388,9 +409,16 @@ def main():
         "serving": serving,
         "cpu_baseline": None,
     }
+    if w.topk:
+        call_ms = sum(st["ms"] for st in stages if st["name"] in ("logits", "topk"))
+        res["search"] = {"database_keys": w.T, "queries_per_call": w.B * w.Hq, "k": w.topk,
+                         "ms_per_call": round(call_ms, 4),
+                         "queries_per_s": round(w.B * w.Hq / (call_ms * 1e-3), 1),
+                         "step": "tq_attn_logits (scores of every key), tq_topk"}
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded CPU sample")
-        res["cpu_baseline"] = cpu_baseline(w, stages, K, V, pk, pv, q, hadamard=had)
+        res["cpu_baseline"] = cpu_baseline(w, stages, K, V, pk, pv, q, hadamard=had,
+                                           logits=logits if w.logits else None)
     print(json.dumps(res), flush=True)
 
 

@@ -251,6 +251,29 @@ tq_status tq_attn_decode(const tq_tables *tk, const tq_tables *tv, const void *q
                          int B, int Hq, int Hkv, const tq_packed *k, const tq_packed *v,
                          float scale, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes for tq_topk (0 for invalid sizes). */
+size_t tq_topk_workspace(int64_t rows, int64_t n, int k);
+
+/*
+ * tq_topk -- the k largest entries of every row of a score matrix: the
+ * selection step of inner-product search over packed keys, whose scores are
+ * the tq_attn_logits estimates.
+ * Cites: a2a-mcp.org page, "Benchmarks" (vector search judged by top-k
+ * recall); "How it works" (inner products estimated straight from codes).
+ * An entry ranks above another if its score is larger, or the scores are
+ * equal (-0 equals +0) and its column is smaller; each row's result is in
+ * that order.
+ *   scores   in, [rows][n] float32, no NaN
+ *   rows     0..65535
+ *   n        1..2^31-1 columns
+ *   k        1..32, k <= n
+ *   idx      out, [rows][k] int32 column indices
+ *   val      out, [rows][k] float32 scores (as stored, -0 returned as +0)
+ *   ws       workspace of at least tq_topk_workspace(rows, n, k) bytes
+ */
+tq_status tq_topk(const float *scores, int64_t rows, int64_t n, int k, int32_t *idx, float *val,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -198,4 +198,19 @@ tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q
   return from_hip(tq::launch_decode(*tk, *tv, qr, u, B, Hq, Hkv, *k, *v, scale, ws, lay, out, stream));
 }
 
+size_t tq_topk_workspace(int64_t rows, int64_t n, int k) {
+  if (rows < 0 || rows > 65535 || n < 1 || n > INT32_MAX || k < 1 || k > 32 || k > n) return 0;
+  return tq::topk_workspace(rows, n, k);
+}
+
+tq_status tq_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* idx, float* val, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  if (rows < 0 || n < 1 || n > INT32_MAX || k < 1 || k > 32 || k > n) return TQ_EINVAL;
+  if (rows > 65535) return TQ_EUNSUPPORTED;  // one grid row per score row
+  if (rows == 0) return TQ_OK;
+  if (!ok_ptr(scores) || !ok_ptr(idx) || !ok_ptr(val) || !ok_ptr(ws)) return TQ_EINVAL;
+  if (ws_bytes < tq::topk_workspace(rows, n, k)) return TQ_EWORKSPACE;
+  return from_hip(tq::launch_topk(scores, rows, n, k, idx, val, ws, stream));
+}
+
 }  // extern "C"

@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
     float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     bm = max_over_rows(bm);
-    if (__ballot(first || bm > lthr || vm > sig)) {
+    if (__builtin_amdgcn_ballot_w64(first || bm > lthr || vm > sig) != 0) {
       sig = fmaxf(sig, max_over_rows(vm));
       const float ls = __builtin_amdgcn_logf(fmaxf(sig, 0x1p-90f));   // log2
       const float m_new = fmaxf(m_ref, bm + r_ref);

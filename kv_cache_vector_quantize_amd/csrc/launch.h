@@ -49,4 +49,10 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
 hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
                               int Hkv, const tq_packed& k, float* logits, hipStream_t stream);
 
+// Top-k of each score row (k <= 32): chunk lists in ws, then one merge per row.
+int64_t topk_chunks(int64_t n);
+size_t topk_workspace(int64_t rows, int64_t n, int k);
+hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* idx, float* val, void* ws,
+                       hipStream_t stream);
+
 }  // namespace tq

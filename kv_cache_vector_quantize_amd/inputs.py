@@ -60,6 +60,7 @@ class Workload:
     decode: bool = False       # whole decode (softmax + values) is part of it
     logits: bool = False       # logits only
     quantize_timed: bool = True
+    topk: int = 0              # search: the k best keys per query after the logits
 
     @property
     def nseq(self):
@@ -78,6 +79,12 @@ WORKLOADS = {
     5: Workload("70b_long_decode_64q8kv_T524288", 5, B=1, Hq=64, Hkv=8, T=524288,
                 k_bits=2, v_bits=3, k_law="student_t_outliers", v_sigma=1.0, decode=True,
                 quantize_timed=False),
+    # Inner-product search (the pages' second workload: GloVe vectors, d = 200,
+    # judged by top-k recall), as a synthetic stand-in at the head dimension
+    # the kernels are built for: one database of 2^20 keys (3 bits: 2-bit
+    # codes + QJL), 8 queries per call, top 10.
+    6: Workload("search_d128_N1M_q8_top10", 6, B=1, Hq=8, Hkv=1, T=1048576, k_bits=3,
+                logits=True, quantize_timed=False, topk=10),
 }
 
 # Channels scaled x20 in the "normal with outliers" key law (tiny workload).

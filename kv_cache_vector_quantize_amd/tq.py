@@ -67,6 +67,10 @@ def lib():
     L.tq_hadamard_rotation.argtypes = [i32, vp, vp, vp]
     L.tq_quantize.restype = i32
     L.tq_quantize.argtypes = [ctypes.POINTER(Tables), vp, i32, ctypes.POINTER(Packed), vp]
+    L.tq_topk_workspace.restype = sz
+    L.tq_topk_workspace.argtypes = [i64, i64, i32]
+    L.tq_topk.restype = i32
+    L.tq_topk.argtypes = [vp, i64, i64, i32, vp, vp, vp, sz, vp]
     L.tq_append.restype = i32
     L.tq_append.argtypes = [ctypes.POINTER(Tables), vp, i32, i64, ctypes.POINTER(Packed), vp]
     L.tq_logits_workspace.restype = sz
@@ -317,3 +321,26 @@ def tq_attn_decode(tk, tv, q, k, v, B, Hq, Hkv, scale=None, ws=None, out=None):
                             Hkv, ctypes.byref(p1), ctypes.byref(p2), float(scale), _ptr(out),
                             _ptr(ws), ws.numel(), _stream(q.device)), "tq_attn_decode")
     return out
+
+
+def topk_workspace_bytes(rows, n, k):
+    return lib().tq_topk_workspace(rows, n, k)
+
+
+def tq_topk(scores, k, ws=None, idx=None, val=None):
+    """scores: [rows, n] float32 on the device.  Returns (idx int32 [rows, k],
+    val float32 [rows, k]): each row's k largest scores, larger first, ties
+    to the smaller column."""
+    assert scores.dtype == torch.float32 and scores.is_contiguous() and scores.dim() == 2
+    rows, n = scores.shape
+    need = lib().tq_topk_workspace(rows, n, k)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=scores.device)
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    if val is None:
+        val = torch.empty((rows, k), dtype=torch.float32, device=scores.device)
+    _check(lib().tq_topk(_ptr(scores), rows, n, k, _ptr(idx), _ptr(val), _ptr(ws), ws.numel(),
+                         _stream(scores.device)), "tq_topk")
+    return idx, val
+

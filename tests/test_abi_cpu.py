@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
     assert L.tq_abi_version() == 3
@@ -118,6 +118,31 @@ def test_quantize_validation(L):
     assert L.tq_quantize(by(_tables(tq)), None, 1, by(_packed(tq)), None) == -1
     # empty stream: nothing to do, OK without touching any pointer
     assert L.tq_quantize(by(_tables(tq)), None, 1, by(_packed(tq, nseq=0)), None) == 0
+
+
+def test_topk_workspace_sizes(L):
+    # one sorted list of 16 (k <= 16) or 32 keys of 8 bytes per 16384-column chunk and row
+    assert L.tq_topk_workspace(8, 1 << 20, 10) == 8 * 64 * 16 * 8
+    assert L.tq_topk_workspace(3, 16385, 17) == 3 * 2 * 32 * 8
+    assert L.tq_topk_workspace(1, 5, 6) == 0          # k > n
+    assert L.tq_topk_workspace(1, 100, 33) == 0       # k > 32
+    assert L.tq_topk_workspace(70000, 100, 3) == 0
+
+
+@needs_no_gpu
+def test_topk_validation(L):
+    vp = ctypes.c_void_p
+    f = vp(FAKE)
+    ws = L.tq_topk_workspace(4, 1000, 10)
+    assert L.tq_topk(f, 4, 1000, 0, f, f, f, ws, None) == -1          # k < 1
+    assert L.tq_topk(f, 4, 1000, 33, f, f, f, ws, None) == -1         # k > 32
+    assert L.tq_topk(f, 4, 5, 6, f, f, f, ws, None) == -1             # k > n
+    assert L.tq_topk(f, 4, 1 << 31, 6, f, f, f, ws, None) == -1       # n too large
+    assert L.tq_topk(None, 4, 1000, 10, f, f, f, ws, None) == -1
+    assert L.tq_topk(f, 4, 1000, 10, vp(FAKE + 4), f, f, ws, None) == -1
+    assert L.tq_topk(f, 4, 1000, 10, f, f, f, ws - 1, None) == -3
+    assert L.tq_topk(f, 70000, 1000, 10, f, f, f, 1 << 40, None) == -2
+    assert L.tq_topk(None, 0, 1000, 10, None, None, None, 0, None) == 0   # no rows
 
 
 @needs_no_gpu
