@@ -14,6 +14,11 @@
 //     largest keys sorted in registers (an unrolled insertion that runs only
 //     when the key beats the thread's current K-th); the workgroup then
 //     merges its 256 lists pairwise through LDS and writes its K best.
+//     The scan goes in 4 rounds; after each of the first three the
+//     workgroup takes tau = the largest of its threads' k-th best keys.
+//     At least k keys of the chunk are >= tau, so a key below tau is not in
+//     the chunk's top k and is dropped without an insertion: after the first
+//     round almost every key is rejected by one comparison.
 //  2. topk_merge_kernel: one workgroup per row merges the rows' chunk lists
 //     the same way and writes the k best as (index, score).
 // The scan is a single pass over the scores (HBM-bound for long rows); the
@@ -52,39 +57,76 @@ __device__ __forceinline__ void topk_insert(uint64_t (&a)[K], uint64_t x) {
   }
 }
 
-// Merge the 256 sorted lists L[t][0..K) in LDS into L[0] (every thread of
-// the workgroup calls this; L is overwritten).
+// a <- the K largest of a and b (both sorted descending), sorted
+// descending, in registers: max(a[i], b[K-1-i]) holds exactly those K and
+// is bitonic (falls, then rises), which log2(K) half-cleaner stages sort.
 template <int K>
-__device__ __forceinline__ void topk_tree_merge(uint64_t (*L)[K], int tid) {
-  for (int step = kTkThreads / 2; step >= 1; step >>= 1) {
-    __syncthreads();
-    uint64_t out[K];
-    if (tid < step) {
-      const uint64_t* A = L[tid];
-      const uint64_t* B = L[tid + step];
-      int p = 0, q = 0;
+__device__ __forceinline__ void topk_merge_into(uint64_t (&a)[K], const uint64_t (&b)[K]) {
 #pragma unroll
-      for (int o = 0; o < K; ++o) {
-        const uint64_t x = A[p], y = B[q];     // p, q < K: at most K are taken in total
-        const bool ta = x >= y;
-        out[o] = ta ? x : y;
-        p += ta ? 1 : 0;
-        q += ta ? 0 : 1;
+  for (int i = 0; i < K; ++i) a[i] = a[i] > b[K - 1 - i] ? a[i] : b[K - 1 - i];
+#pragma unroll
+  for (int j = K / 2; j >= 1; j >>= 1) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if ((i & j) == 0) {
+        const uint64_t hi = a[i] > a[i + j] ? a[i] : a[i + j];
+        const uint64_t lo = a[i] > a[i + j] ? a[i + j] : a[i];
+        a[i] = hi;
+        a[i + j] = lo;
       }
     }
+  }
+}
+
+// Merge the 256 sorted lists, thread t's in a (registers), into the list of
+// thread 0 (every thread of the workgroup calls this).  L: LDS exchange area.
+template <int K>
+__device__ __forceinline__ void topk_tree_merge(uint64_t (&a)[K], uint64_t (*L)[K], int tid) {
+  for (int step = kTkThreads / 2; step >= 1; step >>= 1) {
+    __syncthreads();   // the previous round's readers are done with L
+    if (tid >= step && tid < 2 * step) {
+#pragma unroll
+      for (int i = 0; i < K; i += 2)
+        *reinterpret_cast<uint4*>(&L[tid - step][i]) =
+            make_uint4(static_cast<uint32_t>(a[i]), static_cast<uint32_t>(a[i] >> 32),
+                       static_cast<uint32_t>(a[i + 1]), static_cast<uint32_t>(a[i + 1] >> 32));
+    }
     __syncthreads();
     if (tid < step) {
+      uint64_t b[K];
 #pragma unroll
-      for (int o = 0; o < K; ++o) L[tid][o] = out[o];
+      for (int i = 0; i < K; i += 2) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&L[tid][i]);
+        b[i] = (static_cast<uint64_t>(w.y) << 32) | w.x;
+        b[i + 1] = (static_cast<uint64_t>(w.w) << 32) | w.z;
+      }
+      topk_merge_into<K>(a, b);
     }
   }
+}
+
+// the largest of the workgroup's `mine` values (all threads call it)
+__device__ __forceinline__ uint64_t topk_block_max(uint64_t mine, uint64_t* red, int tid) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t other = __shfl_xor(mine, o, 64);
+    mine = other > mine ? other : mine;
+  }
+  __syncthreads();                 // the previous round's readers are done with red
+  if ((tid & 63) == 0) red[tid >> 6] = mine;
   __syncthreads();
+  uint64_t m = red[0];
+#pragma unroll
+  for (int w = 1; w < kTkThreads / 64; ++w) m = red[w] > m ? red[w] : m;
+  return m;
 }
 
 template <int K>
 __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(const float* __restrict__ scores, int64_t n,
-                                                                 int64_t nchunks, uint64_t* __restrict__ cand) {
-  __shared__ uint64_t L[kTkThreads][K];
+                                                                 int64_t nchunks, int k,
+                                                                 uint64_t* __restrict__ cand) {
+  __shared__ uint64_t L[kTkThreads / 2][K];   // tree-merge exchange area
+  __shared__ uint64_t red[kTkThreads / 64];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.y, chunk = blockIdx.x;
   const float* s = scores + row * n;
@@ -95,31 +137,57 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(const float* __r
   // 4 consecutive columns per thread and step: 16-byte loads where the row
   // is 16-byte aligned and whole
   const bool vec = (n % 4 == 0);
-  for (int e = 0; e < kTkPer / 4; ++e) {
+  uint64_t tau = 0;
+  auto take = [&](uint64_t x) {
+    if (x > tau) topk_insert<K>(a, x);
+  };
+  constexpr int kSteps4 = kTkPer / 4, kRounds = 4, kSteps = kSteps4 / kRounds;
+  // every load of the thread is issued before the first key is ranked: one
+  // memory latency per workgroup instead of one per step
+  float4 v[kSteps4];
+#pragma unroll
+  for (int e = 0; e < kSteps4; ++e) {
     const int64_t c0 = base + 4 * (static_cast<int64_t>(e) * kTkThreads + tid);
     if (vec && c0 + 3 < n) {
-      const float4 v = *reinterpret_cast<const float4*>(s + c0);
-      topk_insert<K>(a, topk_key(v.x, c0));
-      topk_insert<K>(a, topk_key(v.y, c0 + 1));
-      topk_insert<K>(a, topk_key(v.z, c0 + 2));
-      topk_insert<K>(a, topk_key(v.w, c0 + 3));
+      v[e] = *reinterpret_cast<const float4*>(s + c0);
     } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (c0 + u < n) topk_insert<K>(a, topk_key(s[c0 + u], c0 + u));
+      v[e].x = c0 < n ? s[c0] : 0.f;
+      v[e].y = c0 + 1 < n ? s[c0 + 1] : 0.f;
+      v[e].z = c0 + 2 < n ? s[c0 + 2] : 0.f;
+      v[e].w = c0 + 3 < n ? s[c0 + 3] : 0.f;
     }
   }
 #pragma unroll
-  for (int i = 0; i < K; ++i) L[tid][i] = a[i];
-  topk_tree_merge<K>(L, tid);
-  if (tid < K) cand[(row * nchunks + chunk) * K + tid] = L[0][tid];
+  for (int round = 0; round < kRounds; ++round) {
+#pragma unroll
+    for (int e = round * kSteps; e < (round + 1) * kSteps; ++e) {
+      const int64_t c0 = base + 4 * (static_cast<int64_t>(e) * kTkThreads + tid);
+      if (c0 < n) take(topk_key(v[e].x, c0));
+      if (c0 + 1 < n) take(topk_key(v[e].y, c0 + 1));
+      if (c0 + 2 < n) take(topk_key(v[e].z, c0 + 2));
+      if (c0 + 3 < n) take(topk_key(v[e].w, c0 + 3));
+    }
+    if (round + 1 < kRounds) {
+      uint64_t kth = 0;   // this thread's k-th best so far (0: fewer than k)
+#pragma unroll
+      for (int i = 0; i < K; ++i) kth = (i == k - 1) ? a[i] : kth;
+      const uint64_t t = topk_block_max(kth, red, tid);
+      tau = t > tau ? t : tau;
+    }
+  }
+  topk_tree_merge<K>(a, L, tid);
+  if (tid == 0) {
+    uint64_t* dst = cand + (row * nchunks + chunk) * K;
+#pragma unroll
+    for (int i = 0; i < K; ++i) dst[i] = a[i];
+  }
 }
 
 template <int K>
 __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const uint64_t* __restrict__ cand, int64_t nchunks,
                                                                 int k, int32_t* __restrict__ idx,
                                                                 float* __restrict__ val) {
-  __shared__ uint64_t L[kTkThreads][K];
+  __shared__ uint64_t L[kTkThreads / 2][K];   // tree-merge exchange area
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   uint64_t a[K];
@@ -128,19 +196,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const uint64_t* 
   // thread t folds the chunk lists t, t + 256, ... into its own
   for (int64_t c = tid; c < nchunks; c += kTkThreads) {
     const uint64_t* src = cand + (row * nchunks + c) * K;
-    for (int i = 0; i < K; ++i) {
-      const uint64_t x = src[i];
-      if (x <= a[K - 1]) break;               // the list is sorted: nothing after it beats a[K-1]
-      topk_insert<K>(a, x);
-    }
-  }
+    uint64_t b[K];
 #pragma unroll
-  for (int i = 0; i < K; ++i) L[tid][i] = a[i];
-  topk_tree_merge<K>(L, tid);
-  if (tid < k) {
-    const uint64_t key = L[0][tid];
-    idx[row * k + tid] = static_cast<int32_t>(~static_cast<uint32_t>(key));
-    val[row * k + tid] = topk_score(key);
+    for (int i = 0; i < K; i += 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src + i);
+      b[i] = (static_cast<uint64_t>(w.y) << 32) | w.x;
+      b[i + 1] = (static_cast<uint64_t>(w.w) << 32) | w.z;
+    }
+    topk_merge_into<K>(a, b);
+  }
+  topk_tree_merge<K>(a, L, tid);
+  if (tid == 0) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (i < k) {
+        idx[row * k + i] = static_cast<int32_t>(~static_cast<uint32_t>(a[i]));
+        val[row * k + i] = topk_score(a[i]);
+      }
+    }
   }
 }
 
@@ -151,7 +224,7 @@ static hipError_t launch_topk_k(const float* scores, int64_t rows, int64_t n, in
                                 uint64_t* cand, hipStream_t stream) {
   const int64_t nchunks = topk_chunks(n);
   hipLaunchKernelGGL(topk_chunk_kernel<K>, dim3(static_cast<unsigned>(nchunks), static_cast<unsigned>(rows)),
-                     dim3(kTkThreads), 0, stream, scores, n, nchunks, cand);
+                     dim3(kTkThreads), 0, stream, scores, n, nchunks, k, cand);
   hipLaunchKernelGGL(topk_merge_kernel<K>, dim3(static_cast<unsigned>(rows)), dim3(kTkThreads), 0, stream, cand,
                      nchunks, k, idx, val);
   return hipGetLastError();
