@@ -10,17 +10,19 @@
 //
 // Two launches:
 //  1. topk_chunk_kernel: one workgroup per (chunk of kChunk columns, row).
-//     Every thread scans kPer columns with 16-byte loads, keeping its K
-//     largest keys sorted in registers (an unrolled insertion that runs only
-//     when the key beats the thread's current K-th); the workgroup then
-//     merges its 256 lists pairwise through LDS and writes its K best.
-//     The scan goes in 4 rounds; after each of the first three the
-//     workgroup takes tau = the largest of its threads' k-th best keys.
-//     At least k keys of the chunk are >= tau, so a key below tau is not in
-//     the chunk's top k and is dropped without an insertion: after the first
-//     round almost every key is rejected by one comparison.
-//  2. topk_merge_kernel: one workgroup per row merges the rows' chunk lists
-//     the same way and writes the k best as (index, score).
+//     Every thread loads its kPer columns with 16-byte loads.  A threshold
+//     tau with at least k keys of the chunk at or above it comes from the
+//     threads' maxima (the k-th largest maximum of each wave, sorted across
+//     the lanes); the keys that reach it -- a few dozen on ordinary data --
+//     are appended to an LDS buffer and placed by counting, for each, the
+//     candidates above it.  When too many keys reach tau (rows with long
+//     runs of equal top scores, sorted rows), each thread instead keeps its
+//     K best candidates in registers and the workgroup merges its 256 lists
+//     pairwise.  The chunk's K best (at least its exact top k) are written.
+//  2. topk_merge_kernel: one workgroup per row.  tau = the largest k-th
+//     entry of its chunk lists; the list entries that reach it are ranked
+//     by counting as above (or, if too many, merged pairwise), and the k
+//     best are written as (index, score).
 // The scan is a single pass over the scores (HBM-bound for long rows); the
 // merges touch K keys per chunk.
 #include <hip/hip_runtime.h>
@@ -105,45 +107,40 @@ __device__ __forceinline__ void topk_tree_merge(uint64_t (&a)[K], uint64_t (*L)[
   }
 }
 
-// the largest of the workgroup's `mine` values (all threads call it)
-__device__ __forceinline__ uint64_t topk_block_max(uint64_t mine, uint64_t* red, int tid) {
+// descending sort of one u32 per lane across the wave (bitonic network on
+// lane shuffles): lane i returns the i-th largest
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t other = __shfl_xor(mine, o, 64);
-    mine = other > mine ? other : mine;
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), stride, 64));
+      const bool desc = (lane & size) == 0;      // this block's direction (all descending at 64)
+      const bool lower = (lane & stride) == 0;
+      v = (lower == desc) ? (v > o ? v : o) : (v > o ? o : v);
+    }
   }
-  __syncthreads();                 // the previous round's readers are done with red
-  if ((tid & 63) == 0) red[tid >> 6] = mine;
-  __syncthreads();
-  uint64_t m = red[0];
-#pragma unroll
-  for (int w = 1; w < kTkThreads / 64; ++w) m = red[w] > m ? red[w] : m;
-  return m;
+  return v;
 }
+
+constexpr int kTkCap = 512;   // candidates a workgroup selects from by rank counting
 
 template <int K>
 __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(const float* __restrict__ scores, int64_t n,
                                                                  int64_t nchunks, int k,
                                                                  uint64_t* __restrict__ cand) {
-  __shared__ uint64_t L[kTkThreads / 2][K];   // tree-merge exchange area
-  __shared__ uint64_t red[kTkThreads / 64];
-  const int tid = threadIdx.x;
+  __shared__ uint64_t L[kTkThreads / 2][K];   // tree-merge exchange area (fallback)
+  __shared__ uint64_t cbuf[kTkCap];           // candidate keys
+  __shared__ uint64_t best[K];
+  __shared__ uint32_t red[kTkThreads / 64];
+  __shared__ int ccount;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t row = blockIdx.y, chunk = blockIdx.x;
   const float* s = scores + row * n;
-  uint64_t a[K];
-#pragma unroll
-  for (int i = 0; i < K; ++i) a[i] = 0;
   const int64_t base = chunk * kTkChunk;
-  // 4 consecutive columns per thread and step: 16-byte loads where the row
-  // is 16-byte aligned and whole
+  constexpr int kSteps4 = kTkPer / 4;
+  // every load of the thread is issued before the first key is ranked
   const bool vec = (n % 4 == 0);
-  uint64_t tau = 0;
-  auto take = [&](uint64_t x) {
-    if (x > tau) topk_insert<K>(a, x);
-  };
-  constexpr int kSteps4 = kTkPer / 4, kRounds = 4, kSteps = kSteps4 / kRounds;
-  // every load of the thread is issued before the first key is ranked: one
-  // memory latency per workgroup instead of one per step
   float4 v[kSteps4];
 #pragma unroll
   for (int e = 0; e < kSteps4; ++e) {
@@ -157,24 +154,77 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(const float* __r
       v[e].w = c0 + 3 < n ? s[c0 + 3] : 0.f;
     }
   }
+  auto col = [&](int e, int u) { return base + 4 * (static_cast<int64_t>(e) * kTkThreads + tid) + u; };
+  auto comp = [&](int e, int u) {
+    return u == 0 ? v[e].x : (u == 1 ? v[e].y : (u == 2 ? v[e].z : v[e].w));
+  };
+  // Threshold: the k-th largest of a wave's 64 per-thread maxima (score
+  // bits of the key) is reached by k distinct columns, so at least k keys
+  // of the chunk have score bits >= it; tau, the largest over the waves,
+  // keeps that property.  A key whose score bits are below tau is not in
+  // the chunk's top k.
+  uint32_t mx = 0;   // below every real key's score bits
 #pragma unroll
-  for (int round = 0; round < kRounds; ++round) {
+  for (int e = 0; e < kSteps4; ++e)
 #pragma unroll
-    for (int e = round * kSteps; e < (round + 1) * kSteps; ++e) {
-      const int64_t c0 = base + 4 * (static_cast<int64_t>(e) * kTkThreads + tid);
-      if (c0 < n) take(topk_key(v[e].x, c0));
-      if (c0 + 1 < n) take(topk_key(v[e].y, c0 + 1));
-      if (c0 + 2 < n) take(topk_key(v[e].z, c0 + 2));
-      if (c0 + 3 < n) take(topk_key(v[e].w, c0 + 3));
+    for (int u = 0; u < 4; ++u)
+      if (col(e, u) < n) {
+        const uint32_t h = static_cast<uint32_t>(topk_key(comp(e, u), 0) >> 32);
+        mx = h > mx ? h : mx;
+      }
+  const uint32_t srt = wave_sort_desc(mx, lane);
+  const uint32_t tw = static_cast<uint32_t>(__shfl(static_cast<int>(srt), k - 1, 64));
+  if (tid == 0) ccount = 0;
+  if (lane == 0) red[tid >> 6] = tw;
+  __syncthreads();
+  uint32_t tau = red[0];
+#pragma unroll
+  for (int w = 1; w < kTkThreads / 64; ++w) tau = red[w] > tau ? red[w] : tau;
+  // candidates: every key whose score bits reach tau (at least k of them)
+#pragma unroll
+  for (int e = 0; e < kSteps4; ++e)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = col(e, u);
+      if (c < n) {
+        const uint64_t key = topk_key(comp(e, u), c);
+        if (static_cast<uint32_t>(key >> 32) >= tau) {
+          const int p = atomicAdd(&ccount, 1);
+          if (p < kTkCap) cbuf[p] = key;
+        }
+      }
     }
-    if (round + 1 < kRounds) {
-      uint64_t kth = 0;   // this thread's k-th best so far (0: fewer than k)
-#pragma unroll
-      for (int i = 0; i < K; ++i) kth = (i == k - 1) ? a[i] : kth;
-      const uint64_t t = topk_block_max(kth, red, tid);
-      tau = t > tau ? t : tau;
+  __syncthreads();
+  const int cnt = ccount;   // uniform: both paths below are taken by the whole workgroup
+  if (cnt <= kTkCap) {
+    // rank of each candidate among the candidates: its place in the list
+    if (tid < K) best[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += kTkThreads) {
+      const uint64_t key = cbuf[i];
+      int rank = 0;
+      for (int j = 0; j < cnt; ++j) rank += cbuf[j] > key ? 1 : 0;
+      if (rank < K) best[rank] = key;
     }
+    __syncthreads();
+    if (tid < K) cand[(row * nchunks + chunk) * K + tid] = best[tid];
+    return;
   }
+  // many keys share the top score bits (e.g. sorted or constant rows):
+  // every thread keeps its K best of the candidates, then the lists merge
+  uint64_t a[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) a[i] = 0;
+#pragma unroll
+  for (int e = 0; e < kSteps4; ++e)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = col(e, u);
+      if (c < n) {
+        const uint64_t key = topk_key(comp(e, u), c);
+        if (static_cast<uint32_t>(key >> 32) >= tau) topk_insert<K>(a, key);
+      }
+    }
   topk_tree_merge<K>(a, L, tid);
   if (tid == 0) {
     uint64_t* dst = cand + (row * nchunks + chunk) * K;
@@ -187,9 +237,75 @@ template <int K>
 __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(const uint64_t* __restrict__ cand, int64_t nchunks,
                                                                 int k, int32_t* __restrict__ idx,
                                                                 float* __restrict__ val) {
-  __shared__ uint64_t L[kTkThreads / 2][K];   // tree-merge exchange area
-  const int tid = threadIdx.x;
+  __shared__ uint64_t L[kTkThreads / 2][K];   // tree-merge exchange area (fallback)
+  __shared__ uint64_t cbuf[kTkCap];
+  __shared__ uint64_t red[kTkThreads / 64];
+  __shared__ int ccount;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t row = blockIdx.x;
+  const uint64_t* lists = cand + row * nchunks * K;
+  // tau: the largest k-th entry of the chunk lists.  That list holds k keys
+  // >= tau, so the row's top k are all >= tau, and each of them is in its
+  // chunk's list.  (tau > 0: the first chunk has at least k columns.)
+  // a thread's first list stays in registers (one round of 16-byte loads)
+  uint64_t b0[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) b0[i] = 0;
+  if (tid < nchunks) {
+#pragma unroll
+    for (int i = 0; i < K; i += 2) {
+      const uint4 w = *reinterpret_cast<const uint4*>(lists + tid * K + i);
+      b0[i] = (static_cast<uint64_t>(w.y) << 32) | w.x;
+      b0[i + 1] = (static_cast<uint64_t>(w.w) << 32) | w.z;
+    }
+  }
+  uint64_t t = 0;
+#pragma unroll
+  for (int i = 0; i < K; ++i) t = (i == k - 1) ? b0[i] : t;
+  for (int64_t c = tid + kTkThreads; c < nchunks; c += kTkThreads) {
+    const uint64_t x = lists[c * K + (k - 1)];
+    t = x > t ? x : t;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t x = __shfl_xor(t, o, 64);
+    t = x > t ? x : t;
+  }
+  if (tid == 0) ccount = 0;
+  if (lane == 0) red[tid >> 6] = t;
+  __syncthreads();
+  uint64_t tau = red[0];
+#pragma unroll
+  for (int w = 1; w < kTkThreads / 64; ++w) tau = red[w] > tau ? red[w] : tau;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (b0[i] >= tau) {
+      const int p = atomicAdd(&ccount, 1);
+      if (p < kTkCap) cbuf[p] = b0[i];
+    }
+  }
+  for (int64_t c = tid + kTkThreads; c < nchunks; c += kTkThreads) {
+    for (int i = 0; i < K; ++i) {
+      const uint64_t x = lists[c * K + i];
+      if (x < tau) break;                     // the list is sorted descending
+      const int p = atomicAdd(&ccount, 1);
+      if (p < kTkCap) cbuf[p] = x;
+    }
+  }
+  __syncthreads();
+  const int cnt = ccount;
+  if (cnt <= kTkCap) {
+    for (int i = tid; i < cnt; i += kTkThreads) {
+      const uint64_t key = cbuf[i];
+      int rank = 0;
+      for (int j = 0; j < cnt; ++j) rank += cbuf[j] > key ? 1 : 0;
+      if (rank < k) {
+        idx[row * k + rank] = static_cast<int32_t>(~static_cast<uint32_t>(key));
+        val[row * k + rank] = topk_score(key);
+      }
+    }
+    return;
+  }
   uint64_t a[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) a[i] = 0;
