@@ -366,7 +366,8 @@ def main():
     # 32768, decode 102 B per (token, KV head) against 2G(2d+m) flop, so at
     # the fp16 matrix-core peak all of them are bandwidth-bound.
     dom = max(stages, key=lambda st: st["ms"])
-    src = {"quantize_k": "quantize.hip", "quantize_v": "quantize.hip", "logits": "attention.hip",
+    src = {"quantize_k": "quantize.hip", "quantize_v": "quantize.hip",
+           "logits": "decode_kernels.h" if w.Hq // w.Hkv <= 8 else "attention.hip",
            "decode": "decode.hip", "topk": "topk.hip"}[dom["name"]]
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
     roofline = {
