@@ -43,16 +43,17 @@ def value_record_bytes(bits, d=128, norm_bytes=2):
     return (d // 32) * bits * 4 + norm_bytes
 
 
-def traffic_from_profiles(kernel_src, kernel_name):
+def traffic_from_profiles(kernel_src, kernel_name, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when it is missing or the kernel source changed since."""
+    None when it is missing, was taken on another workload, or the kernel
+    source changed since."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         t = json.load(open(p))
         e = t.get(kernel_name)
-        if e is None or e.get("source_sha256") != _sha(kernel_src):
+        if e is None or e.get("workload") != workload or e.get("source_sha256") != _sha(kernel_src):
             return None
         return e["hbm_bytes_per_launch"]
     except Exception:
@@ -375,7 +376,7 @@ def main():
         "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic_from_profiles(os.path.join(ROOT, "kv_cache_vector_quantize_amd", "csrc", src),
-                                         dom["kernel"]),
+                                         dom["kernel"], w.name),
         "algorithmic": {"bytes_per_unit": round(dom["bytes"] / dom["units"], 2), "units_per_launch": dom["units"],
                         "unit": "vector" if dom["name"].startswith("quantize") else "token of one KV head",
                         "flop_per_unit": dom["flop_per_unit"],
