@@ -235,7 +235,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; every input lives on one MI355X and "
+        print("bench.py measures one GPU only: every input lives on one MI355X and "
               "nothing is sharded (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

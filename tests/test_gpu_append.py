@@ -245,3 +245,31 @@ def test_full_size_append_one_token():
     torch.cuda.synchronize()
     assert torch.equal(pv.buf_codes, ref.buf_codes)
     assert torch.equal(pv.buf_norm, ref.buf_norm)
+
+
+@pytest.mark.parametrize("G", [1, 8, 16])
+def test_capacity_stride_gives_same_results(G):
+    """Streams stored with spare capacity (a longer row stride) give logits
+    and decode outputs bit for bit equal to the same streams stored tight,
+    for the matrix-core paths (1 and 8 heads per KV head) and the vector
+    path of logits (16)."""
+    say("capacity stride", G)
+    B, Hkv, T = 2, 2, 333
+    Hq = G * Hkv
+    g = torch.Generator().manual_seed(40 + G)
+    K = torch.randn((B * Hkv, T, D), generator=g).to(torch.bfloat16).cuda().contiguous()
+    V = torch.randn((B * Hkv, T, D), generator=g).to(torch.bfloat16).cuda().contiguous()
+    q = torch.randn((B, Hq, D), generator=g).to(torch.bfloat16).cuda()
+    res = []
+    for cap in (0, 32 * 20):
+        tk, pk = _stream(tq.TQ_KEY, 3, B * Hkv, T, "f16", cap)
+        tv, pv = _stream(tq.TQ_VALUE, 2, B * Hkv, T, "f32", cap)
+        tq.tq_quantize(tk, K, pk)
+        tq.tq_quantize(tv, V, pv)
+        lg = tq.tq_attn_logits(tk, q, pk, B, Hq, Hkv)
+        dc = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv) if G <= 8 else None
+        torch.cuda.synchronize()
+        res.append((lg.clone(), None if dc is None else dc.clone()))
+    assert torch.equal(res[0][0], res[1][0])
+    if G <= 8:
+        assert torch.equal(res[0][1], res[1][1])
