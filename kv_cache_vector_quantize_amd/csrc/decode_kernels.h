@@ -313,6 +313,7 @@ struct Packet {
   static constexpr int kInstr = (kChunks + 63) / 64;   // DMA instructions per block
   static constexpr int kTail = kChunks - 64 * (kInstr - 1);  // lanes of the last one
 };
+static_assert(Packet<3, 4, 4, 2>::kBytes == 512 * 3 + 512 + 512 * 4 + 64 * 4 + 32 * 2, "packet layout");
 
 // LDS byte address of a __shared__ object
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -429,10 +430,20 @@ __device__ __forceinline__ float norm_at(const char* p, int i) {
   else return reinterpret_cast<const float*>(p)[i];
 }
 
-// workgroups per CU that the LDS of a workgroup (tables + ring) allows, at most 3
+// workgroups per CU that the LDS of a workgroup (tables + ring of packets of
+// `bytes`) allows, at most 3; the host sizes decode splits by it
+constexpr int ring_occupancy_bytes(int bytes) {
+  return (kTabBytes + kRing * 4 * bytes) * 3 <= 160 * 1024 ? 3 : 2;
+}
+
+// bytes of one block's packet (Packet<KB, VB, NK, NV>::kBytes)
+constexpr int packet_bytes(int kb, int vb, int nk, int nv) {
+  return 512 * kb + 512 + 512 * vb + 64 * nk + 32 * nv;
+}
+
 template <typename P>
 constexpr int ring_occupancy() {
-  return (kTabBytes + kRing * 4 * P::kBytes) * 3 <= 160 * 1024 ? 3 : 2;
+  return ring_occupancy_bytes(P::kBytes);
 }
 
 template <int G, int KB, int VB, int NK, int NV>

@@ -47,10 +47,11 @@ def test_workspace_sizes(L):
     assert L.tq_logits_workspace(1, 1, 128, 0) == 512
     # rotated queries (q', u: 2 x 64 heads x 128 floats) and one (d + 2)-float
     # partial per query head per split; T = 524288 over 8 KV heads is cut into
-    # 128 splits of 4096 tokens (about 1024 workgroups), 131072 tokens over
-    # 128 sequences into 16 splits of 8192 (the longest decode split).
+    # 96 splits of 5472 tokens (768 workgroups: one round of the chip at 3 per
+    # CU), 131072 tokens over 128 sequences into 16 splits of 8192 (the
+    # longest decode split).
     ws = L.tq_decode_workspace(1, 64, 8, 524288, 128, 128)
-    assert ws == 2 * 64 * 128 * 4 + 64 * 128 * 130 * 4
+    assert ws == 2 * 64 * 128 * 4 + 64 * 96 * 130 * 4
     ws = L.tq_decode_workspace(16, 32, 8, 131072, 128, 128)
     assert ws == 2 * 512 * 128 * 4 + 512 * 16 * 130 * 4
     assert L.tq_decode_workspace(-1, 1, 1, 1, 128, 128) == 0
