@@ -23,8 +23,8 @@
 //     entry of its chunk lists; the list entries that reach it are ranked
 //     by counting as above (or, if too many, merged pairwise), and the k
 //     best are written as (index, score).
-// The scan is a single pass over the scores (HBM-bound for long rows); the
-// merges touch K keys per chunk.
+// Every score is read once, by one 16-byte load; the merges touch K keys
+// per chunk.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"

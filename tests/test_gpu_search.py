@@ -35,7 +35,8 @@ def _check_topk(s, k):
 
 @pytest.mark.parametrize("rows,n,k", [
     (1, 1, 1), (3, 5, 5), (2, 100, 10), (4, 16383, 16), (4, 16384, 17), (5, 16385, 32),
-    (2, 100003, 10), (40, 3000, 7), (3, 4 * 16384 * 5 + 3, 32)])
+    (2, 100003, 10), (40, 3000, 7), (3, 4 * 16384 * 5 + 3, 32),
+    (1, 300 * 16384 + 5, 7)])   # more chunk lists than the row merge has threads
 def test_topk_exact(rows, n, k):
     say("topk", rows, n, k)
     _check_topk(_scores(rows, n, seed=rows * 1000 + k), k)
