@@ -21,7 +21,8 @@
 //  * logits, per 16-token tile: A = centroid values of 16 tokens x 4
 //    coordinates per K-step as fp16 hi/lo pairs, looked up from an LDS table
 //    by the index of a coordinate pair, against the query fragment: fp32-grade
-//    dots.  The 1-bit correction is the same contraction with A = +-1 (a
+//    dots.  Decode with 2-bit keys uses exact float16 levels instead (one
+//    K-slot per coordinate, 8 coordinates per K-step; exact_levels2).  The 1-bit correction is the same contraction with A = +-1 (a
 //    table of sign nibbles) and B = u.  The hi and lo columns are summed with
 //    one DPP row shift.
 //  * tile rows are ordered so that after the two tiles of a block, lane group
@@ -100,7 +101,9 @@ __device__ __forceinline__ uint32_t pair_index(const uint32_t* p, int m) {
 // Per KV head s and lane (n = lane%16, g4 = lane/16), 12 B-fragments of 8 fp16:
 //  bq[0..7]: centroid K-steps c' = 0..7.  The K slots hold the coordinates
 //    32*g4 + 4c' + {0,1,0,1,2,3,2,3}: every coordinate twice, once against
-//    the hi and once against the lo half of its centroid.
+//    the hi and once against the lo half of its centroid.  With exact
+//    float16 levels (X2, 2-bit keys in decode) only bq[0..3] are used, slot
+//    i of K-step c' holding coordinate 32*g4 + 8c' + i once.
 //  bu[0..3]: sign K-steps c = 0..3, coordinates 32*g4 + 8c + i.
 // Columns n < G carry the fp16 value, G <= n < 2G its fp16 residual, the
 // rest zero.
@@ -141,6 +144,45 @@ __device__ __forceinline__ floatx4 key2_kstep(uint32_t Q, uint32_t Q2, uint32_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), b, acc, 0, 0, 0);
 }
 
+// (x >> 8K) & 0x78 in one instruction: with x = Q << 3 it is the low nibble
+// of byte K of Q times 8, with x = Q >> 1 its high nibble times 8
+template <int K>
+__device__ __forceinline__ uint32_t byte_x8(uint32_t x) {
+  if constexpr (K == 0) {
+    return x & 0x78u;
+  } else {
+    uint32_t r = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (K == 1)
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+          : "=v"(r) : "v"(x), "s"(0x78u));
+    else if constexpr (K == 2)
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 src1_sel:DWORD"
+          : "=v"(r) : "v"(x), "s"(0x78u));
+    else
+      asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 src1_sel:DWORD"
+          : "=v"(r) : "v"(x), "s"(0x78u));
+#endif
+    return r;
+  }
+}
+
+// centroid K-step C of a 2-bit tile on exact float16 levels (build_tables
+// with X2): coordinates 8C .. 8C+7 are the pairs (8C, 8C+1) = nibble 2C of
+// Q, (8C+2, 8C+3) = nibble 2C of Q2, (8C+4, 8C+5) = nibble 2C+1 of Q and
+// (8C+6, 8C+7) = nibble 2C+1 of Q2.  Each pair entry is 4 bytes at an
+// 8-byte stride: 4-byte reads by 64 lanes stay free of bank conflicts only
+// within a 128-byte table.  Ql / Q2l = Q / Q2 << 3, Qh / Q2h = Q / Q2 >> 1.
+template <int C>
+__device__ __forceinline__ floatx4 key2x_kstep(uint32_t Ql, uint32_t Q2l, uint32_t Qh, uint32_t Q2h,
+                                               const char* tab, const half8& b, floatx4 acc) {
+  const uint32_t x0 = *reinterpret_cast<const uint32_t*>(tab + byte_x8<C>(Ql));
+  const uint32_t x1 = *reinterpret_cast<const uint32_t*>(tab + byte_x8<C>(Q2l));
+  const uint32_t x2 = *reinterpret_cast<const uint32_t*>(tab + byte_x8<C>(Qh));
+  const uint32_t x3 = *reinterpret_cast<const uint32_t*>(tab + byte_x8<C>(Q2h));
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x0, x1, x2, x3), b, acc, 0, 0, 0);
+}
+
 // sign K-step C: byte C of the sign word sw; sws = sw << 4
 template <int C>
 __device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const char* tab, const half8& b,
@@ -156,12 +198,22 @@ __device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const c
 // <u, 2s - 1> (qj) of head n (n < G; the other lanes hold partial sums).
 // pw: the tile token's KB plane words of coordinate word g4; sw: its sign
 // word; tab: the LDS tables of build_tables.
-template <int G, int KB>
+template <int G, int KB, bool X2>
 __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
                                             const half8 (&bu)[4], const char* tab, float (&cen)[4],
                                             float (&qj)[4]) {
   floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (KB == 2) {
+  if constexpr (X2) {
+    static_assert(KB == 2, "exact float16 levels exist for 2-bit keys only");
+    // same pair-index words as below; one float16 level per coordinate
+    const uint32_t Q = ((pw[1] << 2) & 0xCCCCCCCCu) | (pw[0] & 0x33333333u);
+    const uint32_t Q2 = (pw[1] & 0xCCCCCCCCu) | ((pw[0] >> 2) & 0x33333333u);
+    const uint32_t Ql = Q << 3, Q2l = Q2 << 3, Qh = Q >> 1, Q2h = Q2 >> 1;
+    accC = key2x_kstep<0>(Ql, Q2l, Qh, Q2h, tab, bq[0], accC);
+    accC = key2x_kstep<1>(Ql, Q2l, Qh, Q2h, tab, bq[1], accC);
+    accC = key2x_kstep<2>(Ql, Q2l, Qh, Q2h, tab, bq[2], accC);
+    accC = key2x_kstep<3>(Ql, Q2l, Qh, Q2h, tab, bq[3], accC);
+  } else if constexpr (KB == 2) {
     // nibble j of Q / Q2: the pair-table index of coordinates (4j, 4j+1) /
     // (4j+2, 4j+3): bits 0, 1 = plane 0 of the two, bits 2, 3 = plane 1.
     // Qs / Q2s hold the same shifted up by 4, so that every nibble is the
@@ -203,7 +255,7 @@ __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, con
 // This lane's query fragments for KV head s, built from the rotated queries
 // (q' = Pi q, u = S q', one row of d floats per query head) times the
 // factors fq and fu, in the layout described above.
-template <int G>
+template <int G, bool X2>
 __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const float* __restrict__ u,
                                             int64_t s, int lane, float fq, float fu, half8 (&bq)[8],
                                             half8 (&bu)[4]) {
@@ -219,13 +271,17 @@ __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const 
     return static_cast<_Float16>(0.f);
   };
   constexpr int kSlot[8] = {0, 1, 0, 1, 2, 3, 2, 3};
+  // X2 (exact float16 levels): 4 centroid K-steps, slot i = coordinate 8c + i
+  constexpr int kNC = X2 ? 4 : 8;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < kNC; ++c) {
     _Float16 h[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = part(fq * qg[32 * g4 + 4 * c + kSlot[i]]);
+    for (int i = 0; i < 8; ++i) h[i] = part(fq * qg[32 * g4 + (X2 ? 8 * c + i : 4 * c + kSlot[i])]);
     bq[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
   }
+#pragma unroll
+  for (int c = kNC; c < 8; ++c) bq[c] = u4_to_h8(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     _Float16 h[8];
@@ -233,6 +289,72 @@ __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const 
     for (int i = 0; i < 8; ++i) h[i] = part(fu * ug[32 * g4 + 8 * c + i]);
     bu[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
   }
+}
+
+// ------------------------------------------------------------ exact 2-bit levels
+// A 2-bit Lloyd-Max codebook is -a, -b, b, a (a > b > 0; symmetric about 0,
+// as the quantizer also assumes).  Under one common factor both magnitudes
+// become exact float16 numbers to about 1e-6 relative: a -> la = Q 2^(E-11)
+// (Q in [1024, 2047], a in [2^(E-1), 2^E), so la lies in a's binade) and
+// b -> lb = P 2^(e-11) la / Q, with P the 11-bit rounding of r Q (r = b/a,
+// r Q in [2^(e-1), 2^e)).  Every workgroup tries all 1024 values of Q (4 per
+// thread) and keeps the one with the smallest |P 2^(e-11) - r Q| / (r Q),
+// the smallest Q on a tie, so every workgroup picks the same levels.  The
+// decode logits then need one float16 K-slot per coordinate instead of a
+// hi + lo pair: 4 centroid K-steps per tile instead of 8.  The factor
+// fc = a / la rides on the query fragments, which keep their hi + lo split,
+// so the one inexact step is lb's ~1e-6 relative error (1.3e-6 at d = 128),
+// far inside decode's output tolerance.  The raw-logits kernel keeps the
+// hi + lo centroid pairs (fp32-grade) for its absolute tolerance.
+struct Levels2 {
+  float la, lb, fc;
+};
+
+__device__ __forceinline__ void levels2_from_q(double r, float a, int Q, Levels2& L) {
+  int e = 0, E = 0;
+  (void)frexp(r * Q, &e);
+  const double P = rint(ldexp(r * Q, 11 - e));
+  (void)frexpf(a, &E);
+  L.la = ldexpf(static_cast<float>(Q), E - 11);
+  L.lb = static_cast<float>(ldexp(P, e + E - 22));
+  L.fc = a / L.la;
+}
+
+// all threads of the workgroup call this (it holds a barrier); red: 4
+// 8-byte LDS slots
+__device__ __forceinline__ Levels2 exact_levels2(const float* __restrict__ ck, int tid,
+                                                 unsigned long long* red) {
+  const float a = ck[3];
+  const double r = static_cast<double>(ck[2]) / static_cast<double>(a);
+  unsigned long long best = ~0ull;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int Q = 1024 + 4 * (tid & 255) + i;
+    const double x = r * Q;
+    int e = 0;
+    (void)frexp(x, &e);
+    const double P = rint(ldexp(x, 11 - e));
+    const float err = static_cast<float>(fabs(ldexp(P, e - 11) - x) / x);
+    // err >= 0 (a NaN from a degenerate table sorts last): its bits order it
+    const unsigned long long key = (static_cast<unsigned long long>(__float_as_uint(err)) << 32) |
+                                   static_cast<unsigned int>(Q);
+    best = key < best ? key : best;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned int lo = __shfl_xor(static_cast<unsigned int>(best), o, 64);
+    const unsigned int hi = __shfl_xor(static_cast<unsigned int>(best >> 32), o, 64);
+    const unsigned long long other = (static_cast<unsigned long long>(hi) << 32) | lo;
+    best = other < best ? other : best;
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = best;
+  __syncthreads();
+  unsigned long long m = red[0];
+#pragma unroll
+  for (int w = 1; w < kDecThreads / 64; ++w) m = red[w] < m ? red[w] : m;
+  Levels2 L;
+  levels2_from_q(r, a, static_cast<int>(m & 0xFFFFu), L);
+  return L;
 }
 
 // The workgroup's code tables in LDS (kTabBytes at the start of its LDS),
@@ -248,14 +370,28 @@ __device__ __forceinline__ void query_frags(const float* __restrict__ qr, const 
 //    x (bit i -> slot i) as fp16;
 //  * at kVluOff (VB > 0), vlut[x]: the value centroids of the token pair
 //    whose fields are x & (2^VB - 1) and x >> VB.
-template <int KB, int VB>
+//  * X2 (2-bit keys on exact float16 levels): entry x (4 bytes at 8x) holds
+//    the levels of the coordinate pair whose plane-0 bits are x & 3 and
+//    plane-1 bits x >> 2, from {-la, -lb, lb, la} (exact_levels2).
+template <int KB, int VB, bool X2>
 __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const float* __restrict__ cv,
-                                             char* tab, int tid, int nthreads) {
+                                             char* tab, int tid, int nthreads, float la = 0.f,
+                                             float lb = 0.f) {
   auto hilo = [&](float c, _Float16& h, _Float16& l) {
     h = static_cast<_Float16>(c);
     l = static_cast<_Float16>(c - static_cast<float>(h));
   };
-  if constexpr (KB == 2) {
+  if constexpr (X2) {
+    static_assert(KB == 2, "exact float16 levels exist for 2-bit keys only");
+    for (int x = tid; x < 16; x += nthreads) {
+      auto level = [&](int idx) {   // idx 0..3 = -a, -b, b, a
+        const float v = (idx == 0 || idx == 3) ? la : lb;
+        return static_cast<_Float16>(idx < 2 ? -v : v);
+      };
+      const int i0 = (x & 1) | (((x >> 2) & 1) << 1), i1 = ((x >> 1) & 1) | (((x >> 3) & 1) << 1);
+      *reinterpret_cast<uint32_t*>(tab + 8 * x) = h2u(level(i0), level(i1));
+    }
+  } else if constexpr (KB == 2) {
     for (int x = tid; x < 16; x += nthreads) {
       _Float16 h[2], l[2];
 #pragma unroll
@@ -348,6 +484,39 @@ __device__ __forceinline__ void wait_vm() {
 #endif
 }
 
+// Token order of the key-plane and sign chunks in the ring.  Tile row n of
+// tile `tile` is token t = 8 (n/4) + 4 tile + n%4; its chunks sit at slot
+// ring_slot(t) = 16 tile + n, so the 16 tokens one tile reads fill 16
+// consecutive 16-byte slots.  In stream order (token t at slot t) the 16
+// rows would share 4 slots modulo 16 and every read of key-plane or sign
+// words would be a 4-way LDS bank conflict (measured ~3x the conflict-free
+// time); in this order 8-byte key-plane reads are conflict-free and 4-byte
+// sign-word reads 2-way.  The DMA lanes fetch their chunks in this order.
+__device__ __forceinline__ int ring_token(int slot) {   // inverse of ring_slot
+  return 8 * ((slot & 15) >> 2) + 4 * (slot >> 4) + (slot & 3);
+}
+
+// key-plane words (KB per coordinate word g4) and the sign word of the token
+// at ring slot `slot` (= 16 tile + n) of the packet at pk.  A token's 4 KB
+// plane words are its KB chunks, chunk h at slot 32 h + slot.
+template <int KB>
+__device__ __forceinline__ void ring_key_words(const char* pk, int slot, int g4, uint32_t (&kw)[KB],
+                                               uint32_t& sw) {
+  const uint32_t* kc = reinterpret_cast<const uint32_t*>(pk);
+  if constexpr (KB == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(kc + (32 * (g4 >> 1) + slot) * 4 + 2 * (g4 & 1));
+    kw[0] = v.x;
+    kw[1] = v.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < KB; ++q) {
+      const int w = g4 * KB + q;
+      kw[q] = kc[(32 * (w >> 2) + slot) * 4 + (w & 3)];
+    }
+  }
+  sw = reinterpret_cast<const uint32_t*>(pk + 512 * KB)[slot * 4 + g4];
+}
+
 // The LDS-DMA ring of one wave: the sources of this lane's 16-byte chunks of
 // the wave's first block, their advance per block of the wave (4 blocks of
 // the split), the ring slot addresses, and the waits.  P is the Packet.
@@ -374,10 +543,12 @@ struct BlockStream {
       const char* p = reinterpret_cast<const char*>(kcodes);
       int64_t st = 0;
       if (c < 32 * KB) {
-        p = reinterpret_cast<const char*>(kcodes) + tok * 16 * KB + 16 * c;
+        // ring slot c = 32 h + ring_slot(t) holds chunk h of token t
+        const int t = ring_token(c & 31);
+        p = reinterpret_cast<const char*>(kcodes) + tok * 16 * KB + 16 * (t * KB + (c >> 5));
         st = 4 * 32 * 16 * KB;
       } else if (c < 32 * KB + 32) {
-        p = reinterpret_cast<const char*>(ksigns) + tok * 16 + 16 * (c - 32 * KB);
+        p = reinterpret_cast<const char*>(ksigns) + tok * 16 + 16 * ring_token(c - 32 * KB);
         st = 4 * 32 * 16;
       } else if (c < 32 * (KB + 1 + VB)) {
         p = reinterpret_cast<const char*>(vcodes) + (tokv / 32) * 512 * VB + 16 * (c - 32 * (KB + 1));
@@ -483,9 +654,14 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
   for (int jj = 0; jj + 1 < kRing; ++jj)
     if (jj < nbw) st.issue(jj, jj, lane);
 
-  build_tables<KB, VB>(ck, cv, lds, tid, kDecThreads);  // visible after the barrier below
+  // 2-bit keys: exact float16 levels, one K-slot per coordinate
+  constexpr bool X2 = KB == 2;
+  __shared__ unsigned long long red2[X2 ? kDecThreads / 64 : 1];
+  Levels2 lev{0.f, 0.f, 1.f};
+  if constexpr (X2) lev = exact_levels2(ck, tid, red2);
+  build_tables<KB, VB, X2>(ck, cv, lds, tid, kDecThreads, lev.la, lev.lb);  // visible after the barrier below
   half8 bq[8], bu[4];
-  query_frags<G>(qr, u, s, lane, fq, fu, bq, bu);
+  query_frags<G, X2>(qr, u, s, lane, fq * lev.fc, fu, bq, bu);
   __syncthreads();
 
   floatx4 O[8];
@@ -500,7 +676,6 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
   float r_ref = 0.f, m_ref = -INFINITY, lsum = 0.f;
   float sig = 0.f, lthr = 0.f;                         // sigma; kTau - log2(sigma)
   bool first = true;
-  const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
   const int vbit0 = 8 * VB * g4;                       // this lane group's 8 value fields
   // the fields lie in record words vwlo and vwlo + 1 (the word after a
   // record is the next record's first, or the first norm row: read, unused)
@@ -518,14 +693,10 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
     float sv[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const int row = rowtok + 4 * tile;
-      uint32_t kw[KB];
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(pk + P::kKC) + (row * 4 + g4) * KB;
-#pragma unroll
-      for (int q = 0; q < KB; ++q) kw[q] = kp[q];
-      const uint32_t sw = reinterpret_cast<const uint32_t*>(pk + P::kSG)[row * 4 + g4];
+      uint32_t kw[KB], sw;
+      ring_key_words<KB>(pk + P::kKC, 16 * tile + n, g4, kw, sw);
       float cen[4], qj[4];
-      tile_logits<G, KB>(kw, sw, bq, bu, lds, cen, qj);
+      tile_logits<G, KB, X2>(kw, sw, bq, bu, lds, cen, qj);
       const int l0 = 8 * g4 + 4 * tile;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -712,12 +883,11 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>(
   for (int jj = 0; jj + 1 < kRing; ++jj)
     if (jj < nbw) st.issue(jj, jj, lane);
 
-  build_tables<KB, 0>(ck, nullptr, lds, tid, kDecThreads);
+  build_tables<KB, 0, false>(ck, nullptr, lds, tid, kDecThreads);
   half8 bq[8], bu[4];
-  query_frags<G>(qr, u, s, lane, 1.f, fu, bq, bu);
+  query_frags<G, false>(qr, u, s, lane, 1.f, fu, bq, bu);
   __syncthreads();
 
-  const int rowtok = 8 * (n >> 2) + (n & 3);          // token of A-row n (tile 0)
   float* out_h = out + (s * G + (n < G ? n : 0)) * T;
   const bool vec_ok = (Ti & 3) == 0;                  // 16-byte aligned output rows
   int slot = 0;
@@ -729,14 +899,10 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>(
     float lv[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      const int row = rowtok + 4 * tile;
-      uint32_t kw[KB];
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(pk + P::kKC) + (row * 4 + g4) * KB;
-#pragma unroll
-      for (int q = 0; q < KB; ++q) kw[q] = kp[q];
-      const uint32_t sw = reinterpret_cast<const uint32_t*>(pk + P::kSG)[row * 4 + g4];
+      uint32_t kw[KB], sw;
+      ring_key_words<KB>(pk + P::kKC, 16 * tile + n, g4, kw, sw);
       float cen[4], qj[4];
-      tile_logits<G, KB>(kw, sw, bq, bu, lds, cen, qj);
+      tile_logits<G, KB, false>(kw, sw, bq, bu, lds, cen, qj);
       const int l0 = 8 * g4 + 4 * tile;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
