@@ -369,10 +369,15 @@ def main():
     dom = max(stages, key=lambda st: st["ms"])
     src = {"quantize_k": "quantize.hip", "quantize_v": "quantize.hip",
            "logits": "decode_kernels.h" if w.Hq // w.Hkv <= 8 else "attention.hip",
-           "decode": "decode.hip", "topk": "topk.hip"}[dom["name"]]
+           "decode": "decode_kernels.h", "topk": "topk.hip"}[dom["name"]]
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    # the time divided into is the stage's event-timed call: for decode and
+    # logits that call launches query preparation (and decode's combine) too
+    calls = {"decode": f"tq_attn_decode: qprep_kernel, {dom['kernel']}, decode_combine_kernel",
+             "logits": f"tq_attn_logits: qprep_kernel, {dom['kernel']}"}
     roofline = {
         "kernel": dom["kernel"],
+        "timed_call": calls.get(dom["name"], dom["kernel"]),
         "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic_from_profiles(os.path.join(ROOT, "kv_cache_vector_quantize_amd", "csrc", src),
