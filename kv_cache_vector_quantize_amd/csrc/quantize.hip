@@ -175,6 +175,52 @@ __device__ __forceinline__ void quant_one(float y, const QTab<BITS>& tab, uint64
   idx = (cnt ^ sgn) + half;  // half + cnt, or half - 1 - cnt
 }
 
+// The same index as quant_one, for keys in the transposed layout (one token
+// per lane): appends the index's plane bits, inverted, below the bits
+// already in pw[] -- pw[BITS-1] <- the sign bit of y (the sign plane is set
+// for y's sign bit clear), pw[p] <- the sign bit of y XOR that of a - t for
+// the boundary t the magnitude search tested for plane p (set for
+// [a >= t] XNOR [y's sign bit clear]).  a - t is never -0 or NaN for finite
+// inputs, so its sign bit is exactly a < t, the compare quant_one makes.
+// Returns the signed centroid through C (y's sign, so -0.0 gives -mag).
+template <int BITS>
+__device__ __forceinline__ void quant_append(float y, const QTab<BITS>& tab, uint32_t* pw, float& C) {
+  const uint32_t yb = __float_as_uint(y);
+  const float a = fabsf(y);
+  auto push = [&](int p, uint32_t bits) { pw[p] = __builtin_amdgcn_alignbit(pw[p], bits, 31); };
+  push(BITS - 1, yb);
+  float mag;
+  if constexpr (BITS == 1) {
+    mag = tab.cpos[0];
+  } else if constexpr (BITS == 2) {
+    const float d1 = a - tab.tpos[0];
+    push(0, yb ^ __float_as_uint(d1));
+    mag = sel(d1 >= 0.f, tab.cpos[1], tab.cpos[0]);
+  } else if constexpr (BITS == 3) {
+    const float d1 = a - tab.tpos[1];
+    const bool m1 = d1 >= 0.f;
+    const float d2 = a - sel(m1, tab.tpos[2], tab.tpos[0]);
+    const bool m2 = d2 >= 0.f;
+    push(1, yb ^ __float_as_uint(d1));
+    push(0, yb ^ __float_as_uint(d2));
+    mag = sel(m1, sel(m2, tab.cpos[3], tab.cpos[2]), sel(m2, tab.cpos[1], tab.cpos[0]));
+  } else {
+    const float d1 = a - tab.tpos[3];
+    const bool m1 = d1 >= 0.f;
+    const float d2 = a - sel(m1, tab.tpos[5], tab.tpos[1]);
+    const bool m2 = d2 >= 0.f;
+    const float d3 = a - sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0]));
+    const bool m3 = d3 >= 0.f;
+    push(2, yb ^ __float_as_uint(d1));
+    push(1, yb ^ __float_as_uint(d2));
+    push(0, yb ^ __float_as_uint(d3));
+    const float lo4 = sel(m2, sel(m3, tab.cpos[3], tab.cpos[2]), sel(m3, tab.cpos[1], tab.cpos[0]));
+    const float hi4 = sel(m2, sel(m3, tab.cpos[7], tab.cpos[6]), sel(m3, tab.cpos[5], tab.cpos[4]));
+    mag = sel(m1, hi4, lo4);
+  }
+  C = copysignf(mag, y);
+}
+
 template <typename XT>
 struct RawX {
   static constexpr int kWords = sizeof(XT) == 4 ? 4 : 2;  // uint4 per thread (16 elements)
@@ -283,12 +329,19 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   for (int i = 0; i + 1 < kHalf; ++i) tab.tpos[i] = bnd[kHalf + i] * kResScale;
   if constexpr (BITS == 1) tab.tpos[0] = 0.f;
 
-  // B fragments: Pi^T for coordinates j = 32*wave + c32 and (keys) S^T for
-  // sketch rows i = 32*wave + c32; K-step c covers input index 16c + 8h + e.
+  // 32x32 tile row / column c32 <-> token or coordinate atok: output register
+  // v of lane half h is tile row 8(v/4) + 4h + v%4, and atok of that row is
+  // 16h + v
+  const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
+  // Pi fragments for coordinates j and (keys) S fragments for sketch rows
+  // i = j; K-step c covers input index 16c + 8h + e.  Values: B = Pi^T with
+  // j = 32*wave + c32 (output column = coordinate).  Keys: A = Pi with
+  // j = 32*wave + atok (output row = coordinate, permuted so that register v
+  // of lane half h is coordinate 32*wave + 16h + v).
   qhalf8 bph[8], bpl[HAD ? 1 : 8];
   qhalf8 bsh[KEY ? 8 : 1], bsl[KEY ? 8 : 1];
   {
-    const int j = 32 * wave + c32;
+    const int j = 32 * wave + (KEY ? atok : c32);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if constexpr (HAD) sign_frag(rot + j * kD + 16 * c + 8 * h, bph[c]);
@@ -308,8 +361,6 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   const int64_t blk0 = pos / kUnit;
   const int64_t nblk = (T + kUnit - 1) / kUnit - blk0;
   const int64_t units = nseq * nblk;
-  // A-row c32 of a 32x32 tile holds token atok
-  const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
   // staging role: token sv, elements 16*sq .. 16*sq+15
   const int sv = tid >> 3, sq = tid & 7;
   // (sequence, block) of the first unit and the per-iteration step
@@ -440,129 +491,135 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       load_raw(s1, b1, raw);  // the next unit, in flight during this unit's compute
     }
 
-    // ---------------- rotation: acc = X Pi^T (x kPiScale, inputs scaled)
+    // ---------------- rotation (x kPiScale, inputs scaled).  Values:
+    // acc = X Pi^T, acc[v] = token 16h + v of coordinate 32*wave + c32.
+    // Keys: acc = Pi X^T, acc[v] = coordinate 32*wave + 16h + v of token c32.
     qfloatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const qhalf8 ah = *reinterpret_cast<const qhalf8*>(&xs[xb][0][atok][16 * c + 8 * h]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bph[c], acc, 0, 0, 0);
-      if constexpr (!HAD) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bpl[c], acc, 0, 0, 0);
-      if constexpr (kSplitX) {
-        const qhalf8 al = *reinterpret_cast<const qhalf8*>(&xs[xb][kXP - 1][atok][16 * c + 8 * h]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bph[c], acc, 0, 0, 0);
-      }
-    }
-
-    // ---------------- quantize: acc[v] is token 16h + v, coordinate 32*wave + c32
-    float rv[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 r4 = *reinterpret_cast<const float4*>(&rinv_s[par][16 * h + 4 * q]);
-      rv[4 * q] = r4.x;
-      rv[4 * q + 1] = r4.y;
-      rv[4 * q + 2] = r4.z;
-      rv[4 * q + 3] = r4.w;
-    }
-    uint32_t cw0 = 0, cw1 = 0;  // key code words: lane = token + 32 * (plane & 1)
-    uint32_t vlo = 0, vhi = 0;  // value fields of tokens 16h .. 16h+15 (bits BITS*v ..)
-    float rprev = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float y = acc[v] * rv[v];
-      uint64_t P[BITS];
-      float C;
-      int idx;
-      quant_one<BITS>(y, tab, P, C, idx);
+      const qhalf8 xh = *reinterpret_cast<const qhalf8*>(&xs[xb][0][KEY ? c32 : atok][16 * c + 8 * h]);
       if constexpr (KEY) {
-#pragma unroll
-        for (int p = 0; p < BITS; ++p) {
-          const uint32_t lo = static_cast<uint32_t>(P[p]), hi = static_cast<uint32_t>(P[p] >> 32);
-          const int base = 32 * (p & 1);
-          if (p < 2) {
-            cw0 = writelane(lo, base + v, cw0);
-            cw0 = writelane(hi, base + 16 + v, cw0);
-          } else {
-            cw1 = writelane(lo, base + v, cw1);
-            cw1 = writelane(hi, base + 16 + v, cw1);
-          }
-        }
-        // residual x256 (for a zero vector y = 0 and the residual is unused:
-        // its signs and rnorm are fixed at the store)
-        const float r = y - C;
-        if (v & 1) {
-          // tokens (v-1, v) of coordinate 32*wave + c32: fp16 hi + lo
-          const qhalf2 hh = {static_cast<_Float16>(rprev), static_cast<_Float16>(r)};
-          const qhalf2 ll = split_lo(hh, rprev, r);
-          const int tk = 16 * h + v - 1, j = 32 * wave + c32;
-          rs[0][tk][j] = hh[0];
-          rs[0][tk + 1][j] = hh[1];
-          rs[1][tk][j] = ll[0];
-          rs[1][tk + 1][j] = ll[1];
-        }
-        rprev = r;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bph[c], xh, acc, 0, 0, 0);
+        if constexpr (!HAD) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bpl[c], xh, acc, 0, 0, 0);
       } else {
-        const int sh = BITS * v;
-        const uint32_t u = static_cast<uint32_t>(idx);
-        if (sh < 32) vlo |= u << sh;
-        if (sh + BITS > 32) vhi |= (sh < 32) ? (u >> (32 - sh)) : (u << (sh - 32));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, bph[c], acc, 0, 0, 0);
+        if constexpr (!HAD) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, bpl[c], acc, 0, 0, 0);
+      }
+      if constexpr (kSplitX) {
+        const qhalf8 xl = *reinterpret_cast<const qhalf8*>(&xs[xb][kXP - 1][KEY ? c32 : atok][16 * c + 8 * h]);
+        if constexpr (KEY) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bph[c], xl, acc, 0, 0, 0);
+        else acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl, bph[c], acc, 0, 0, 0);
       }
     }
 
     if constexpr (KEY) {
+      // ---------------- quantize (keys): acc[v] is coordinate 32*wave + 16h + v
+      // of token c32.  Descending v appends each plane bit below the ones
+      // before it, so after 16 steps coordinate 16h + v sits at bit v.
+      const float rt = rinv_s[par][c32];
+      uint32_t pw[BITS];   // code planes, inverted, coordinates 16h .. 16h+15
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) pw[p] = 0u;
+      uint32_t hw[8], lw[8];   // residual (x256) as fp16 hi / lo pairs of coordinates (2i, 2i+1)
+      float rr = 0.f;          // sum of the residual squares (x256^2)
+      float rodd = 0.f;
+#pragma unroll
+      for (int v = 15; v >= 0; --v) {
+        const float y = acc[v] * rt;
+        float C;
+        quant_append<BITS>(y, tab, pw, C);
+        // residual x256 (for a zero vector y = 0 and the residual is unused:
+        // its signs and rnorm are fixed at the store)
+        const float r = y - C;
+        rr = fmaf(r, r, rr);
+        if (v & 1) {
+          rodd = r;
+        } else {
+          const qhalf2 hh = {static_cast<_Float16>(r), static_cast<_Float16>(rodd)};
+          hw[v / 2] = h2u(hh);
+          lw[v / 2] = h2u(split_lo(hh, r, rodd));
+        }
+      }
+      // residual rows rs[hi / lo][token c32][coordinates 32*wave + 16h ..]
       {
-        const int tk = lane & 31, p = lane >> 5;
-        if (p < BITS && tk >= lo) {  // padding tokens get the zero-vector encoding
-          uint32_t* dst = codes + ((s * Tp + t0 + tk) * 4 + wave) * BITS;
-          dst[p] = cw0;
-          if (p + 2 < BITS) dst[p + 2] = cw1;
+        uint4* dh = reinterpret_cast<uint4*>(&rs[0][c32][32 * wave + 16 * h]);
+        uint4* dl = reinterpret_cast<uint4*>(&rs[1][c32][32 * wave + 16 * h]);
+        dh[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        dh[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+        dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+      }
+      // code words of token c32: lane half 0 takes half 1's 16 bits on top
+      uint32_t cw[BITS];
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) {
+        const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(pw[p]), 32, 64));
+        cw[p] = ~((pw[p] & 0xFFFFu) | (o << 16));
+      }
+      // ||r||^2 over this wave's 32 coordinates
+      const float rr32 = rr + __shfl_xor(rr, 32, 64);
+      if (h == 0) {
+        rho_s[par][wave][c32] = rr32;
+        if (c32 >= lo) {  // padding tokens get the zero-vector encoding
+          uint32_t* dst = codes + ((s * Tp + t0 + c32) * 4 + wave) * BITS;
+#pragma unroll
+          for (int p = 0; p < BITS; ++p) dst[p] = cw[p];
         }
       }
       __syncthreads();
-      // ---------------- sketch Z = R S^T (this wave's 32 sketch rows)
+      // ---------------- sketch Z^T = S R^T: z[v] is sketch row 32*wave + 16h + v
+      // of token c32
       qfloatx16 z;
 #pragma unroll
       for (int i = 0; i < 16; ++i) z[i] = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const qhalf8 ah = *reinterpret_cast<const qhalf8*>(&rs[0][atok][16 * c + 8 * h]);
-        const qhalf8 al = *reinterpret_cast<const qhalf8*>(&rs[1][atok][16 * c + 8 * h]);
-        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bsh[c], z, 0, 0, 0);
-        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bsl[c], z, 0, 0, 0);
-        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bsh[c], z, 0, 0, 0);
+        const qhalf8 rh = *reinterpret_cast<const qhalf8*>(&rs[0][c32][16 * c + 8 * h]);
+        const qhalf8 rl = *reinterpret_cast<const qhalf8*>(&rs[1][c32][16 * c + 8 * h]);
+        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rh, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsl[c], rh, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rl, z, 0, 0, 0);
       }
-      // ---------------- ||r||^2 over this wave's coordinates: diagonal of R R^T
-      // (16x16 tiles: A-row n of tile mt is token 16mt + n; k = 32*wave + 8*(lane/16) + e)
-      {
-        const int n = lane & 15, g = lane >> 4;
+      // sign bits, appended inverted from the float sign bits (z = -0.0, which
+      // only an all-zero residual can give, reads as negative; it lies in the
+      // parity band |z| <= 1e-5 either way)
+      uint32_t sw = 0u;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const qhalf8 gh = *reinterpret_cast<const qhalf8*>(&rs[0][16 * mt + n][32 * wave + 8 * g]);
-          const qhalf8 gl = *reinterpret_cast<const qhalf8*>(&rs[1][16 * mt + n][32 * wave + 8 * g]);
-          qfloatx4 d = {0.f, 0.f, 0.f, 0.f};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(gh, gh, d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(gh, gl, d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(gl, gh, d, 0, 0, 0);
-          // lane (g, n) holds rows 4g .. 4g+3 of column n: the diagonal when g = n/4
-          const int ii = n & 3;
-          const float dg = sel(ii & 2, sel(ii & 1, d[3], d[2]), sel(ii & 1, d[1], d[0]));
-          if (g == (n >> 2)) rho_s[par][wave][16 * mt + n] = dg;
-        }
-      }
-      uint32_t sw = 0;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint64_t Z = __ballot(z[v] >= 0.f);
-        sw = writelane(static_cast<uint32_t>(Z), v, sw);
-        sw = writelane(static_cast<uint32_t>(Z >> 32), 16 + v, sw);
-      }
-      if (lane >= lo && lane < kUnit) {
+      for (int v = 15; v >= 0; --v) sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(z[v]), 31);
+      const uint32_t so = static_cast<uint32_t>(__shfl_xor(static_cast<int>(sw), 32, 64));
+      if (h == 0 && c32 >= lo) {
+        uint32_t word = ~((sw & 0xFFFFu) | (so << 16));
         // a zero vector (padding included) has every sign bit set
-        if (n_s[par][lane] == 0.f) sw = 0xFFFFFFFFu;
-        signs[(s * Tp + t0 + lane) * 4 + wave] = sw;
+        if (n_s[par][c32] == 0.f) word = 0xFFFFFFFFu;
+        signs[(s * Tp + t0 + c32) * 4 + wave] = word;
       }
     } else {
+      // ---------------- quantize (values): acc[v] is token 16h + v of
+      // coordinate 32*wave + c32
+      float rv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 r4 = *reinterpret_cast<const float4*>(&rinv_s[par][16 * h + 4 * q]);
+        rv[4 * q] = r4.x;
+        rv[4 * q + 1] = r4.y;
+        rv[4 * q + 2] = r4.z;
+        rv[4 * q + 3] = r4.w;
+      }
+      uint32_t vlo = 0, vhi = 0;  // value fields of tokens 16h .. 16h+15 (bits BITS*v ..)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float y = acc[v] * rv[v];
+        uint64_t P[BITS];
+        float C;
+        int idx;
+        quant_one<BITS>(y, tab, P, C, idx);
+        const int sh = BITS * v;
+        const uint32_t u = static_cast<uint32_t>(idx);
+        if (sh < 32) vlo |= u << sh;
+        if (sh + BITS > 32) vhi |= (sh < 32) ? (u >> (32 - sh)) : (u << (sh - 32));
+      }
       // mask off the fields of padded tokens (zero vectors past the end of T)
       const int nv = nvalid - 16 * h;  // valid tokens of this lane half
       if (nv < 16) {
