@@ -270,18 +270,26 @@ def main():
     vb = value_record_bytes(w.v_bits, d, nb) if w.v_bits else 0
     qbytes = w.B * w.Hq * d * xb
 
-    # the stages of one step, in order, with their algorithmic bytes
+    # the stages of one step, in order, with their algorithmic bytes.  The
+    # quantize kernels reach fp32-grade products on the fp16 matrix cores
+    # with hi + lo splits: the rotation takes X Pi_hi + X Pi_lo (one product
+    # for the +-1 Walsh-Hadamard matrix), plus x_lo Pi_hi for fp32 input, and
+    # the key sketch R_hi S_hi + R_hi S_lo + R_lo S_hi; "mfma_flop_per_unit"
+    # counts those executed d x d products.
+    rot_products = (1 if had else 2) + (1 if w.x_dtype == "f32" else 0)
     stages = []
     if w.quantize_timed:
         stages.append({"name": "quantize_k", "bytes": nvec * (d * xb + kb), "units": nvec,
                        "fn": lambda: tq.tq_quantize(tk, K, pk),
                        "kernel": f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>",
-                       "flop_per_unit": 2 * d * d + 2 * m * d})
+                       "flop_per_unit": 2 * d * d + 2 * m * d,
+                       "mfma_flop_per_unit": (rot_products + 3) * 2 * d * d})
         if w.v_bits:
             stages.append({"name": "quantize_v", "bytes": nvec * (d * xb + vb), "units": nvec,
                            "fn": lambda: tq.tq_quantize(tv, V, pv),
                            "kernel": f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}{rtag}>",
-                           "flop_per_unit": 2 * d * d})
+                           "flop_per_unit": 2 * d * d,
+                           "mfma_flop_per_unit": rot_products * 2 * d * d})
     else:
         tq.tq_quantize(tk, K, pk)
         if w.v_bits:
@@ -395,6 +403,9 @@ def main():
     for st in stages:
         if st["name"].startswith("quantize"):
             stage_report[st["name"]]["mvec_s"] = round(nvec / (st["ms"] * 1e-3) / 1e6, 2)
+            mf = st["mfma_flop_per_unit"] * st["units"] / (st["ms"] * 1e-3) / 1e12
+            stage_report[st["name"]]["mfma_executed_tflops"] = round(mf, 2)
+            stage_report[st["name"]]["mfma_frac_fp16_peak"] = round(mf / FP16_MFMA_PEAK_TFLOPS, 4)
         elif st["name"] == "topk":
             stage_report[st["name"]]["scores_per_s"] = round(st["units"] / (st["ms"] * 1e-3), 1)
         else:
