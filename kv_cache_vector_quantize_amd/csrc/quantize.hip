@@ -9,32 +9,28 @@
 //  * a unit of work is 32 consecutive tokens of one sequence.  The 4 waves of
 //    a workgroup share it; wave w owns the 32 rotated coordinates
 //    [32w, 32w+32) and, for keys, the 32 sketch rows [32w, 32w+32), so one
-//    32x32 output tile per product.  Its slices of Pi^T and S^T live in
+//    32x32 output tile per product.  Its slices of Pi and S live in
 //    registers as fp16 hi + lo pairs for the whole kernel.
 //  * the 32 input vectors are staged in LDS as fp16.  Each vector is first
 //    scaled by a power of two that puts its norm just below 2^15: a bf16
 //    input is then exact in fp16, an fp32 input is split into fp16 hi + lo.
 //    Pi is held x16 so that its lo half stays a normal fp16 number.  The
 //    rotation X Pi^T carries about 22 significant bits, fp32-grade.
-//  * result layout: lane l holds coordinate 32w + l%32 of the 16 tokens
-//    16*(l/32) + v, v = 0..15 (A-row r of a tile is token
-//    16*((r/4)%2) + 4*(r/8) + r%4).  A wave-wide compare of register v is then
-//    two finished 32-bit words: the low half is word w of token v, the high
-//    half word w of token 16 + v.  Code planes and sign words are moved from
-//    those masks into lanes with v_writelane and stored lane by lane.
-//  * keys: the residual (x256, fp16 hi + lo) goes through LDS; the sketch is
-//    Z = R S^T with three products (hi*hi, hi*lo, lo*hi) and ||r||^2 is the
-//    diagonal of R R^T, each wave summing the 32 coordinates it owns.
-//  * values: every lane packs the b-bit fields of its 16 consecutive tokens
-//    of one coordinate; the 32-token record is the two lane halves' fields in
-//    token order.
+//  * values: lane l holds coordinate 32w + l%32 of the 16 tokens
+//    16*(l/32) + v, v = 0..15 (X Pi^T with A-row r of a tile token
+//    16*((r/4)%2) + 4*(r/8) + r%4); every lane packs the b-bit fields of its
+//    16 tokens, and the 32-token record of a coordinate is the two lane
+//    halves' fields in token order.
+//  * keys are computed transposed (Pi X^T, S R^T, the A rows permuted the
+//    same way): lane l holds coordinates 32w + 16*(l/32) + v of token l%32,
+//    so each lane builds its token's code-plane and sign words itself, one
+//    v_alignbit per bit from float sign bits, and sums its residual squares
+//    for ||r||^2.  The residual (x256, fp16 hi + lo) goes through LDS, one
+//    row per token; the sketch has three products (hi*hi, hi*lo, lo*hi).
 #include <math.h>
 
 #include "common.h"
 #include "launch.h"
-
-// v_writelane_b32: set lane `lane` of `old` to the wave-uniform `value`.
-extern "C" __device__ int tq_writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
 
 namespace tq {
 
@@ -50,10 +46,6 @@ constexpr int kUnit = 32;          // tokens per unit
 constexpr int kRowH = 136;         // LDS row stride in halves (272 B, a multiple of 16 B)
 constexpr float kPiScale = 16.f;   // Pi is held x16 so that its lo half stays normal
 constexpr float kResScale = 256.f; // rotated coordinates are handled x256 (exact)
-
-__device__ __forceinline__ uint32_t writelane(uint32_t value, int lane, uint32_t old) {
-  return static_cast<uint32_t>(tq_writelane_i32(static_cast<int>(value), lane, static_cast<int>(old)));
-}
 
 __device__ __forceinline__ uint32_t h2u(qhalf2 h) { return __builtin_bit_cast(uint32_t, h); }
 
@@ -126,62 +118,42 @@ struct QTab {
 // an address and keep the table out of registers)
 __device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
 
-// Index of y (x256 scale) = number of boundaries <= y.  Writes the lane masks
-// of the index bits into P (bit BITS-1 is the sign test: y's sign bit clear;
-// the lower bits are the magnitude cell, complemented for y < 0), returns the
-// signed centroid through C and the index through idx.  The sign test reads
-// the sign bit, so a -0.0 (only from a negative product that underflowed)
-// counts as negative, like the value it rounds.
+// Index of y (x256 scale) = number of boundaries <= y, for values: the sign
+// of y picks the upper or lower half (its sign bit, so a -0.0, only from a
+// negative product that underflowed, counts as negative like the value it
+// rounds) and a binary search over the positive boundaries the magnitude
+// cell, complemented for y < 0.
 template <int BITS>
-__device__ __forceinline__ void quant_one(float y, const QTab<BITS>& tab, uint64_t* P, float& C,
-                                          int& idx) {
+__device__ __forceinline__ int value_index(float y, const QTab<BITS>& tab) {
   const int sgn = static_cast<int>(__float_as_uint(y)) >> 31;   // 0, or -1 for a set sign bit
-  const bool ms = sgn == 0;
   const float a = fabsf(y);
-  const uint64_t Ms = __ballot(ms);
-  float mag;
   int cnt;
-  P[BITS - 1] = Ms;
   if constexpr (BITS == 1) {
-    mag = tab.cpos[0];
     cnt = 0;
   } else if constexpr (BITS == 2) {
-    const bool m1 = a >= tab.tpos[0];
-    P[0] = ~(Ms ^ __ballot(m1));
-    mag = sel(m1, tab.cpos[1], tab.cpos[0]);
-    cnt = m1 ? 1 : 0;
+    cnt = a >= tab.tpos[0] ? 1 : 0;
   } else if constexpr (BITS == 3) {
     const bool m1 = a >= tab.tpos[1];
     const bool m2 = a >= sel(m1, tab.tpos[2], tab.tpos[0]);
-    P[1] = ~(Ms ^ __ballot(m1));
-    P[0] = ~(Ms ^ __ballot(m2));
-    mag = sel(m1, sel(m2, tab.cpos[3], tab.cpos[2]), sel(m2, tab.cpos[1], tab.cpos[0]));
     cnt = (m1 ? 2 : 0) + (m2 ? 1 : 0);
   } else {
     const bool m1 = a >= tab.tpos[3];
     const bool m2 = a >= sel(m1, tab.tpos[5], tab.tpos[1]);
     const float t3 = sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0]));
     const bool m3 = a >= t3;
-    P[2] = ~(Ms ^ __ballot(m1));
-    P[1] = ~(Ms ^ __ballot(m2));
-    P[0] = ~(Ms ^ __ballot(m3));
-    const float lo4 = sel(m2, sel(m3, tab.cpos[3], tab.cpos[2]), sel(m3, tab.cpos[1], tab.cpos[0]));
-    const float hi4 = sel(m2, sel(m3, tab.cpos[7], tab.cpos[6]), sel(m3, tab.cpos[5], tab.cpos[4]));
-    mag = sel(m1, hi4, lo4);
     cnt = (m1 ? 4 : 0) + (m2 ? 2 : 0) + (m3 ? 1 : 0);
   }
   constexpr int half = 1 << (BITS - 1);
-  C = ms ? mag : -mag;
-  idx = (cnt ^ sgn) + half;  // half + cnt, or half - 1 - cnt
+  return (cnt ^ sgn) + half;  // half + cnt, or half - 1 - cnt
 }
 
-// The same index as quant_one, for keys in the transposed layout (one token
-// per lane): appends the index's plane bits, inverted, below the bits
+// The same index for keys in the transposed layout (one token per lane):
+// appends the index's plane bits, inverted, below the bits
 // already in pw[] -- pw[BITS-1] <- the sign bit of y (the sign plane is set
 // for y's sign bit clear), pw[p] <- the sign bit of y XOR that of a - t for
 // the boundary t the magnitude search tested for plane p (set for
 // [a >= t] XNOR [y's sign bit clear]).  a - t is never -0 or NaN for finite
-// inputs, so its sign bit is exactly a < t, the compare quant_one makes.
+// inputs, so its sign bit is exactly a < t, the compare value_index makes.
 // Returns the signed centroid through C (y's sign, so -0.0 gives -mag).
 template <int BITS>
 __device__ __forceinline__ void quant_append(float y, const QTab<BITS>& tab, uint32_t* pw, float& C) {
@@ -611,12 +583,8 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float y = acc[v] * rv[v];
-        uint64_t P[BITS];
-        float C;
-        int idx;
-        quant_one<BITS>(y, tab, P, C, idx);
         const int sh = BITS * v;
-        const uint32_t u = static_cast<uint32_t>(idx);
+        const uint32_t u = static_cast<uint32_t>(value_index<BITS>(y, tab));
         if (sh < 32) vlo |= u << sh;
         if (sh + BITS > 32) vhi |= (sh < 32) ? (u >> (32 - sh)) : (u << (sh - 32));
       }
