@@ -498,7 +498,10 @@ __device__ __forceinline__ int ring_token(int slot) {   // inverse of ring_slot
 
 // key-plane words (KB per coordinate word g4) and the sign word of the token
 // at ring slot `slot` (= 16 tile + n) of the packet at pk.  A token's 4 KB
-// plane words are its KB chunks, chunk h at slot 32 h + slot.
+// plane words are its KB chunks, chunk h at slot 32 h + slot: the 16 rows of
+// a tile read 16 consecutive chunks.  With 3 planes a lane's 3 words would
+// straddle two such chunks, so there a token's 3 chunks are adjacent
+// (slot 3 slot + h) and the 3 words contiguous: two reads, 2-way conflicts.
 template <int KB>
 __device__ __forceinline__ void ring_key_words(const char* pk, int slot, int g4, uint32_t (&kw)[KB],
                                                uint32_t& sw) {
@@ -507,6 +510,10 @@ __device__ __forceinline__ void ring_key_words(const char* pk, int slot, int g4,
     const uint2 v = *reinterpret_cast<const uint2*>(kc + (32 * (g4 >> 1) + slot) * 4 + 2 * (g4 & 1));
     kw[0] = v.x;
     kw[1] = v.y;
+  } else if constexpr (KB == 3) {
+    const uint32_t* w = kc + 12 * slot + 3 * g4;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) kw[q] = w[q];
   } else {
 #pragma unroll
     for (int q = 0; q < KB; ++q) {
@@ -543,9 +550,11 @@ struct BlockStream {
       const char* p = reinterpret_cast<const char*>(kcodes);
       int64_t st = 0;
       if (c < 32 * KB) {
-        // ring slot c = 32 h + ring_slot(t) holds chunk h of token t
-        const int t = ring_token(c & 31);
-        p = reinterpret_cast<const char*>(kcodes) + tok * 16 * KB + 16 * (t * KB + (c >> 5));
+        // ring slot c holds chunk h of token t: c = 32 h + ring_slot(t), or
+        // c = 3 ring_slot(t) + h for 3-plane keys (ring_key_words)
+        const int t = ring_token(KB == 3 ? c / 3 : c & 31);
+        const int hh = KB == 3 ? c % 3 : c >> 5;
+        p = reinterpret_cast<const char*>(kcodes) + tok * 16 * KB + 16 * (t * KB + hh);
         st = 4 * 32 * 16 * KB;
       } else if (c < 32 * KB + 32) {
         p = reinterpret_cast<const char*>(ksigns) + tok * 16 + 16 * ring_token(c - 32 * KB);
