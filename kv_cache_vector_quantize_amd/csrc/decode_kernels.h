@@ -22,8 +22,9 @@
 //    coordinates per K-step as fp16 hi/lo pairs, looked up from an LDS table
 //    by the index of a coordinate pair, against the query fragment: fp32-grade
 //    dots.  Decode with 2-bit keys uses exact float16 levels instead (one
-//    K-slot per coordinate, 8 coordinates per K-step; exact_levels2).  The 1-bit correction is the same contraction with A = +-1 (a
-//    table of sign nibbles) and B = u.  The hi and lo columns are summed with
+//    K-slot per coordinate, 8 coordinates per K-step; exact_levels2).  The
+//    1-bit correction is the same contraction with A = +-1 (a table of sign
+//    nibbles) and B = u.  The hi and lo columns are summed with
 //    one DPP row shift.
 //  * tile rows are ordered so that after the two tiles of a block, lane group
 //    g4 = lane/16 holds the logits of tokens 8*g4 .. 8*g4+7: exactly the
