@@ -54,6 +54,12 @@ __device__ __forceinline__ qhalf8 qu4(uint32_t a, uint32_t b, uint32_t c, uint32
   return __builtin_bit_cast(qhalf8, v);
 }
 
+// v_sqrt_f32: within 1 ulp (6e-8 relative), where sqrtf's correctly rounded
+// expansion costs ~15 instructions.  Norms need 1e-6 relative (fp32) or the
+// fp16 rounding of the exact value except within 1e-6 of a midpoint, and the
+// arguments here are 0 or at least 1 (sums of squares of scaled vectors).
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
 __device__ __forceinline__ float pow2f(int e) {  // 2^e for -126 <= e <= 127
   return __uint_as_float(static_cast<uint32_t>(127 + e) << 23);
 }
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       const float rho2 = rho_s[pp][0][tid] + rho_s[pp][1][tid] + rho_s[pp][2][tid] + rho_s[pp][3][tid];
       const float nx = n_s[pp][tid];
       store_norm(norm, norm_dtype, pend_base + tid, nx);
-      store_norm(rnorm, norm_dtype, pend_base + tid, nx * (sqrtf(rho2) / kResScale));
+      store_norm(rnorm, norm_dtype, pend_base + tid, nx * (hw_sqrt(rho2) / kResScale));
     }
   };
 
@@ -427,7 +433,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         ss = sum8(ss);
       }
       if (sq == 0) {
-        const float nr = sqrtf(ss);
+        const float nr = hw_sqrt(ss);
         n_s[par][sv] = ldexpf(nr, -sh);
         // the rotation product is kPiScale Pi x (dense) or sqrt(d) Pi_H x (HAD)
         static_assert(kD == 128, "sqrt(kD) below");
@@ -504,7 +510,12 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         quant_append<BITS>(y, tab, pw, C);
         // residual x256 (for a zero vector y = 0 and the residual is unused:
         // its signs and rnorm are fixed at the store)
-        const float r = y - C;
+        float r = y - C;
+#if defined(__HIP_DEVICE_COMPILE__)
+        // keep r a value of its own, so that its fp16 rounding below is one
+        // v_cvt_pk_f16_f32 per pair rather than a fused fma_mix per value
+        asm("" : "+v"(r));
+#endif
         rr = fmaf(r, r, rr);
         if (v & 1) {
           rodd = r;
