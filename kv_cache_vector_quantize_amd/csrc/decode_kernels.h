@@ -497,32 +497,49 @@ __device__ __forceinline__ int ring_token(int slot) {   // inverse of ring_slot
   return 8 * ((slot & 15) >> 2) + 4 * (slot >> 4) + (slot & 3);
 }
 
-// key-plane words (KB per coordinate word g4) and the sign word of the token
-// at ring slot `slot` (= 16 tile + n) of the packet at pk.  A token's 4 KB
-// plane words are its KB chunks, chunk h at slot 32 h + slot: the 16 rows of
-// a tile read 16 consecutive chunks.  With 3 planes a lane's 3 words would
-// straddle two such chunks, so there a token's 3 chunks are adjacent
-// (slot 3 slot + h) and the 3 words contiguous: two reads, 2-way conflicts.
+// Key-plane words (KB per coordinate word g4) and the sign word of the token
+// at ring slot 16 tile + n of a packet.  A token's 4 KB plane words are its
+// KB chunks, chunk h at slot 32 h + slot: the 16 rows of a tile read 16
+// consecutive chunks.  With 3 planes a lane's 3 words would straddle two
+// such chunks, so there a token's 3 chunks are adjacent (slot 3 slot + h)
+// and the 3 words contiguous: two reads, 2-way conflicts.
+//
+// key_lane_off: byte offset of lane (n, g4)'s words of tile 0 from the
+// packet's key segment; tile 1 lies key_tile_bytes further, word q 4q.
+// Sign words: P::kSG + 16 n + 4 g4, tile 1 256 bytes further.
 template <int KB>
-__device__ __forceinline__ void ring_key_words(const char* pk, int slot, int g4, uint32_t (&kw)[KB],
+__device__ __forceinline__ uint32_t key_lane_off(int n, int g4) {
+  if constexpr (KB == 2) return 512 * (g4 >> 1) + 16 * n + 8 * (g4 & 1);
+  else if constexpr (KB == 3) return 48 * n + 12 * g4;
+  else if constexpr (KB == 4) return 512 * g4 + 16 * n;
+  else return 16 * n + 4 * g4;
+}
+template <int KB>
+constexpr int key_tile_bytes() { return KB == 3 ? 768 : 256; }
+
+// kb, sb: this lane's key words and sign word of tile 0 (lds_at)
+template <int KB>
+__device__ __forceinline__ void ring_key_words(const char* kb, const char* sb, int tile, uint32_t (&kw)[KB],
                                                uint32_t& sw) {
-  const uint32_t* kc = reinterpret_cast<const uint32_t*>(pk);
+  const char* k = kb + key_tile_bytes<KB>() * tile;
   if constexpr (KB == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(kc + (32 * (g4 >> 1) + slot) * 4 + 2 * (g4 & 1));
+    const uint2 v = *reinterpret_cast<const uint2*>(k);
     kw[0] = v.x;
     kw[1] = v.y;
-  } else if constexpr (KB == 3) {
-    const uint32_t* w = kc + 12 * slot + 3 * g4;
-#pragma unroll
-    for (int q = 0; q < 3; ++q) kw[q] = w[q];
   } else {
 #pragma unroll
-    for (int q = 0; q < KB; ++q) {
-      const int w = g4 * KB + q;
-      kw[q] = kc[(32 * (w >> 2) + slot) * 4 + (w & 3)];
-    }
+    for (int q = 0; q < KB; ++q) kw[q] = reinterpret_cast<const uint32_t*>(k)[q];
   }
-  sw = reinterpret_cast<const uint32_t*>(pk + 512 * KB)[slot * 4 + g4];
+  sw = *reinterpret_cast<const uint32_t*>(sb + 256 * tile);
+}
+
+// base + off, with off pinned in one VGPR: the compiler would otherwise add
+// the per-block ring offset to every read's own lane offset separately; from
+// one pinned address per lane pattern the reads at constant distances carry
+// those distances as instruction immediates.
+__device__ __forceinline__ const char* lds_at(const char* base, uint32_t off) {
+  asm("" : "+v"(off));
+  return base + off;
 }
 
 // The LDS-DMA ring of one wave: the sources of this lane's 16-byte chunks of
@@ -690,12 +707,20 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
   // the fields lie in record words vwlo and vwlo + 1 (the word after a
   // record is the next record's first, or the first norm row: read, unused)
   const int vwlo = vbit0 >> 5, vsh = vbit0 & 31;
+  // this lane's byte offsets within a packet: key words, sign word, its 8
+  // tokens' norms (key and value), value record words
+  const uint32_t koff = P::kKC + key_lane_off<KB>(n, g4), soff = P::kSG + 16 * n + 4 * g4;
+  const uint32_t nkoff = 8 * NK * g4, nvoff = 8 * NV * g4;
+  const uint32_t voff = P::kVC + 4 * (n * VB + vwlo);
 
   int slot = 0;
   for (int j = 0; j < nbw; ++j) {
     st.advance(j, nbw, slot, lane);
-    const char* pk = ring + slot * kSlot + wave * P::kBytes;
+    const uint32_t pko = slot * kSlot + wave * P::kBytes;   // the block's packet in the ring
     slot = (slot == kRing - 1) ? 0 : slot + 1;
+    const char* kb = lds_at(ring, pko + koff);
+    const char* sb = lds_at(ring, pko + soff);
+    const char* nkb = lds_at(ring, pko + nkoff);
     const int tb = t0 + 32 * (wave + 4 * j);           // first token of the block
     const bool full = tb + 32 <= Ti;
 
@@ -704,25 +729,25 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       uint32_t kw[KB], sw;
-      ring_key_words<KB>(pk + P::kKC, 16 * tile + n, g4, kw, sw);
+      ring_key_words<KB>(kb, sb, tile, kw, sw);
       float cen[4], qj[4];
       tile_logits<G, KB, X2>(kw, sw, bq, bu, lds, cen, qj);
-      const int l0 = 8 * g4 + 4 * tile;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float nk = norm_at<NK>(pk + P::kNK, l0 + i), nr = norm_at<NK>(pk + P::kNR, l0 + i);
+        const float nk = norm_at<NK>(nkb + P::kNK, 4 * tile + i), nr = norm_at<NK>(nkb + P::kNR, 4 * tile + i);
         sv[4 * tile + i] = fmaf(nk, cen[i], fmaf(nr, qj[i], -r_ref));
       }
     }
     // ||v|| of this lane group's 8 tokens, and their largest
     float nv[8];
     uint32_t nvh[4];   // float16 norms: the 4 packed pairs as stored
+    const char* nvb = NV == NK ? nkb : lds_at(ring, pko + nvoff);
     if constexpr (NV == 2) {
-      const uint4 w = *reinterpret_cast<const uint4*>(pk + P::kNV + 16 * g4);
+      const uint4 w = *reinterpret_cast<const uint4*>(nvb + P::kNV);
       nvh[0] = w.x; nvh[1] = w.y; nvh[2] = w.z; nvh[3] = w.w;
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) nv[k] = norm_at<NV>(pk + P::kNV, 8 * g4 + k);
+      for (int k = 0; k < 8; ++k) nv[k] = norm_at<NV>(nvb + P::kNV, k);
     }
     if (!full) {
       // the context's last, partial block: tokens past T get no weight, and
@@ -803,7 +828,7 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
     }
     // two base addresses, so that every record word is an immediate offset
     // of a paired 4-byte read (at most 255 words away)
-    const uint32_t* vrec0 = reinterpret_cast<const uint32_t*>(pk + P::kVC) + n * VB + vwlo;
+    const uint32_t* vrec0 = reinterpret_cast<const uint32_t*>(lds_at(ring, pko + voff));
     const uint32_t* vrec1 = vrec0 + 64 * VB;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
@@ -900,23 +925,29 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>(
 
   float* out_h = out + (s * G + (n < G ? n : 0)) * T;
   const bool vec_ok = (Ti & 3) == 0;                  // 16-byte aligned output rows
+  // this lane's byte offsets within a packet: key words, sign word, norms
+  const uint32_t koff = P::kKC + key_lane_off<KB>(n, g4), soff = P::kSG + 16 * n + 4 * g4;
+  const uint32_t nkoff = 8 * NK * g4;
   int slot = 0;
   for (int j = 0; j < nbw; ++j) {
     st.advance(j, nbw, slot, lane);
-    const char* pk = ring + slot * kSlot + wave * P::kBytes;
+    const uint32_t pko = slot * kSlot + wave * P::kBytes;   // the block's packet in the ring
     slot = (slot == kRing - 1) ? 0 : slot + 1;
+    const char* kb = lds_at(ring, pko + koff);
+    const char* sb = lds_at(ring, pko + soff);
+    const char* nkb = lds_at(ring, pko + nkoff);
     const int tb = t0 + 32 * (wave + 4 * j);           // first token of the block
     float lv[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       uint32_t kw[KB], sw;
-      ring_key_words<KB>(pk + P::kKC, 16 * tile + n, g4, kw, sw);
+      ring_key_words<KB>(kb, sb, tile, kw, sw);
       float cen[4], qj[4];
       tile_logits<G, KB, false>(kw, sw, bq, bu, lds, cen, qj);
-      const int l0 = 8 * g4 + 4 * tile;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        lv[4 * tile + i] = fmaf(norm_at<NK>(pk + P::kNK, l0 + i), cen[i], norm_at<NK>(pk + P::kNR, l0 + i) * qj[i]);
+        lv[4 * tile + i] = fmaf(norm_at<NK>(nkb + P::kNK, 4 * tile + i), cen[i],
+                                norm_at<NK>(nkb + P::kNR, 4 * tile + i) * qj[i]);
     }
     // lane (g4, n < G): tokens tb + 8*g4 .. tb + 8*g4 + 7 of head n
     if (n < G) {
