@@ -776,8 +776,10 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
     // value norm passes sigma (rare after the first block)
     float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    bm = max_over_rows(bm);
+    // (each lane tests its own maxima: a column's threshold is passed by its
+    // row maximum exactly when it is passed by one of its lanes)
     if (__builtin_amdgcn_ballot_w64(first || bm > lthr || vm > sig) != 0) {
+      bm = max_over_rows(bm);
       sig = fmaxf(sig, max_over_rows(vm));
       const float ls = __builtin_amdgcn_logf(fmaxf(sig, 0x1p-90f));   // log2
       const float m_new = fmaxf(m_ref, bm + r_ref);
