@@ -234,7 +234,8 @@ size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m);
  * and rotated back once (out = Pi^T sum_t a_t ||v_t|| c_V[idx_t]).
  * Cites: a2a-mcp.org page, Stage 2 closing paragraph (no full dequantization
  * during inference); "How to implement", item 1.
- *   tk, tv   key / value tables (same d and rotation)
+ *   tk, tv   key / value tables of the same d; each may have its own rotation
+ *            (queries are rotated with tk->rot, the output back with tv->rot)
  *   q        in, [B][Hq][d] of q_dtype
  *   k, v     packed keys and values, nseq = B*Hkv, same T >= 1
  *   scale    softmax scale, > 0 (1/sqrt(d) for standard attention)

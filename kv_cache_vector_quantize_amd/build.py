@@ -16,8 +16,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
-# layout probes for the GPU unit tests, kept out of libtq.so's exports
-PROBE_LIB = os.path.join(PKG, "libtq_probe.so")
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -58,12 +56,7 @@ def build(verbose=False):
         for _, err in results:
             if err.strip():
                 print(err, file=sys.stderr)
-    objs = [o for o, _ in results]
-    probe = [o for o in objs if os.path.basename(o).startswith("probe")]
-    main = [o for o in objs if o not in probe]
-    _link(main, LIB)
-    if probe:
-        _link(probe, PROBE_LIB)
+    _link([o for o, _ in results], LIB)
     return LIB
 
 

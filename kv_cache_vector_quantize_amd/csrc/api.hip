@@ -168,11 +168,14 @@ size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m) {
 tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype,
                          int B, int Hq, int Hkv, const tq_packed* k, const tq_packed* v,
                          float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  // keys and values may use different rotations (of either kind): queries are
+  // rotated with the key table's Pi, the output rotated back with the value
+  // table's; both tables hold Pi densely.  The head dimensions must agree.
+  if (tk == nullptr || tv == nullptr || tv->d != tk->d) return TQ_EINVAL;
   tq_status st = check_tables(tk, true);
   if (st != TQ_OK) return st;
   st = check_tables(tv, false);
   if (st != TQ_OK) return st;
-  if (tv->d != tk->d || tv->rot_kind != tk->rot_kind) return TQ_EINVAL;
   st = check_packed(k, tk, TQ_KEY);
   if (st != TQ_OK) return st;
   st = check_packed(v, tv, TQ_VALUE);

@@ -128,7 +128,9 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombThreads), 0, stream, tk.rot,
+  // the value accumulator is in the value stream's rotated domain: rotate
+  // back with the value table's Pi (the query was rotated with the key's)
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * Hq), dim3(kCombThreads), 0, stream, tv.rot,
                      partials, nsplit, out);
   return hipGetLastError();
 }

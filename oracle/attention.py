@@ -23,7 +23,8 @@ Decode (readings): one query token per (batch, query head) attends to all T
 cached tokens (no mask); query head h uses KV head h // (Hq/Hkv); the
 softmax is over scale * l with scale = 1/sqrt(d); values are summed in the
 rotated domain, acc = sum_t a_t * ||v_t|| * c_V[idx_t], and rotated back
-once, o = Pi^T acc.
+once, o = Pi_v^T acc, with Pi_v the rotation the values were quantized with
+(the same Pi as the keys' unless the value stream has its own).
 """
 
 import numpy as np
@@ -73,8 +74,11 @@ def _softmax(x):
     return e / np.sum(e)
 
 
-def decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, scale=None):
-    """q [B, Hq, d]; key/value records [B, Hkv, T, ...]; returns out [B, Hq, d]."""
+def decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, scale=None, Pi_v=None):
+    """q [B, Hq, d]; key/value records [B, Hkv, T, ...]; returns out [B, Hq, d].
+
+    Pi rotated the keys (and so the query); Pi_v, the rotation the values
+    were quantized with, rotates the value sum back (default: Pi)."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
     Hkv = np.asarray(k_idx).shape[1]
@@ -84,6 +88,7 @@ def decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, sca
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     Pi = np.asarray(Pi, dtype=np.float64)
+    Pi_v = Pi if Pi_v is None else np.asarray(Pi_v, dtype=np.float64)
     cv = np.asarray(cv, dtype=np.float64)
     out = np.zeros((B, Hq, d))
     for b in range(B):
@@ -94,12 +99,12 @@ def decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, sca
             a = _softmax(scale * l)
             w = a * np.asarray(v_norm[b, g], dtype=np.float64)
             acc = w @ cv[v_idx[b, g]]
-            out[b, h] = Pi.T @ acc
+            out[b, h] = Pi_v.T @ acc
     return out
 
 
 def decode_from_records(q, k_codes, k_sign_words, k_norm, k_rnorm, v_codes, v_norm,
-                        T, Pi, S, ck, cv, scale=None):
+                        T, Pi, S, ck, cv, scale=None, Pi_v=None):
     """Same as ``decode`` but from the packed layout of ``packing``."""
     d = np.asarray(Pi).shape[0]
     B, Hkv = np.asarray(k_codes).shape[:2]
@@ -107,4 +112,4 @@ def decode_from_records(q, k_codes, k_sign_words, k_norm, k_rnorm, v_codes, v_no
     k_signs = None if S is None else unpack_signs(k_sign_words, np.asarray(S).shape[0])
     v_idx = unpack_value_codes(np.asarray(v_codes).reshape(B * Hkv, *np.asarray(v_codes).shape[2:]),
                                T).reshape(B, Hkv, T, d)
-    return decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, scale)
+    return decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, scale, Pi_v)

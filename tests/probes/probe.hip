@@ -1,7 +1,7 @@
 // Layout probes for the gfx950 matrix-core and DPP primitives the decode
 // and quantize kernels rely on; exported for the GPU unit test only (one wave, fixed
 // in-bounds sizes).
-#include "common.h"
+#include <hip/hip_runtime.h>
 
 namespace tq {
 

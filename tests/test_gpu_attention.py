@@ -200,3 +200,55 @@ def test_decode_value_norm_range():
     ref = _oracle_decode_rows(to64(q), pk, pv, 2, 3, B, Hq, Hkv, rows)
     ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
     assert ok, rel
+
+
+@pytest.mark.parametrize("v_kind", ["dense_other_seed", "hadamard"])
+def test_decode_separate_key_and_value_rotations(v_kind):
+    """Key and value tables built separately: the values rotated by a Pi of
+    their own (another Gaussian draw, or the Walsh-Hadamard rotation).  The
+    output is rotated back with the value table's Pi."""
+    say("decode separate rotations", v_kind)
+    B, Hkv, G, T = 1, 2, 4, 700
+    Hq = G * Hkv
+    Gk, Sk = inputs.table_gaussians(D, M)
+    Pi_k = oracle.rotation_from_gaussian(Gk)
+    if v_kind == "hadamard":
+        hs = inputs.hadamard_signs(D)
+        tv = tq.make_tables(None, None, 3, hadamard_signs=hs)
+        Pi_v = oracle.randomized_hadamard(hs)
+    else:
+        Gv, _ = inputs.table_gaussians(D, 0, seed=77)
+        tv = tq.make_tables(Gv, None, 3)
+        Pi_v = oracle.rotation_from_gaussian(Gv)
+    tk = gpu_tables(D, M, 2)
+    g = torch.Generator().manual_seed(21)
+    K = (torch.randn((B * Hkv, T, D), generator=g) * 1.5).to(torch.bfloat16).cuda().contiguous()
+    V = torch.randn((B * Hkv, T, D), generator=g).to(torch.bfloat16).cuda().contiguous()
+    pk = tq.alloc_packed(tq.TQ_KEY, tk, B * Hkv, T, "f16")
+    tq.tq_quantize(tk, K, pk)
+    pv = tq.alloc_packed(tq.TQ_VALUE, tv, B * Hkv, T, "f16")
+    tq.tq_quantize(tv, V, pv)
+    q = torch.randn((B, Hq, D), generator=g).cuda()
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv).cpu().numpy()
+    # the value codes follow the value table's rotation
+    _, _, cv, tbv = oracle_tables(D, 0, 3)
+    vidx, vn = value_records(pv)
+    vref = oracle.quantize_values(to64(V).reshape(-1, D), Pi_v, cv, tbv)
+    diff = vidx.reshape(-1, D) != vref["idx"]
+    near = np.min(np.abs(vref["yhat"][..., None] - tbv[None, None, :]), axis=-1) <= 1e-5
+    assert not np.any(diff & ~near)
+    _, S, ck, _ = oracle_tables(D, M, 2)
+    qn = to64(q)
+    for h in range(Hq):
+        s = h // G
+        kc = pk.codes[s].cpu().numpy().view(np.uint32)
+        ks = pk.signs[s].cpu().numpy().view(np.uint32)
+        vc = pv.codes[s].cpu().numpy().view(np.uint32)
+        ref = oracle.decode_from_records(
+            qn[0:1, h:h + 1], kc[None, None], ks[None, None],
+            pk.norm[s].cpu().numpy().astype(np.float64)[None, None],
+            pk.rnorm[s].cpu().numpy().astype(np.float64)[None, None], vc[None, None],
+            pv.norm[s].cpu().numpy().astype(np.float64)[None, None], T, Pi_k, S, ck, cv,
+            Pi_v=Pi_v)[0, 0]
+        ok, rel = decode_close(got[0, h][None], ref[None])
+        assert ok, (h, rel)

@@ -12,10 +12,19 @@ from kv_cache_vector_quantize_amd import tq
 
 pytestmark = pytest.mark.gpu
 
+PROBE_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "libtq_probe.so")
+
+
+def _probe_lib():
+    if not os.path.exists(PROBE_LIB):   # normally built ahead by __graft_entry__.build()
+        from probes import build as probe_build
+        probe_build.build()
+    return ctypes.CDLL(PROBE_LIB)
+
 
 def test_mfma_16x16x32_f16_layout_and_dpp_row_shift():
     tq.lib()
-    L = ctypes.CDLL(os.path.join(os.path.dirname(tq._LIB_PATH), "libtq_probe.so"))
+    L = _probe_lib()
     L.tq_probe_mfma_layout.restype = ctypes.c_int
     L.tq_probe_mfma_layout.argtypes = [ctypes.c_void_p] * 5
     rng = np.random.default_rng(0)
@@ -37,7 +46,7 @@ def test_mfma_16x16x32_f16_layout_and_dpp_row_shift():
 
 def test_mfma_32x32x16_f16_layout():
     tq.lib()
-    L = ctypes.CDLL(os.path.join(os.path.dirname(tq._LIB_PATH), "libtq_probe.so"))
+    L = _probe_lib()
     L.tq_probe_mfma_32x32x16.restype = ctypes.c_int
     L.tq_probe_mfma_32x32x16.argtypes = [ctypes.c_void_p] * 4
     rng = np.random.default_rng(1)

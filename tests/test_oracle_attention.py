@@ -163,3 +163,31 @@ def test_decode_gqa_mapping_and_records_roundtrip():
     out2 = oracle.decode_from_records(q, kc, ks, rs(kr["norm"]), rs(kr["rnorm"]), vc, rs(vr["norm"]),
                                       T, Pi, S, ck, cv)
     assert np.array_equal(out, out2)
+
+
+def test_decode_with_separate_key_and_value_rotations():
+    """Keys quantized with one rotation and values with another: the output is
+    the softmax-weighted sum of the values dequantized with their own
+    rotation, n Pi_v^T c[idx] (the query is rotated with the keys' Pi)."""
+    d, m, T = 128, 128, 7
+    Pi, S, ck, tk = _setup(d, m, 2)
+    Pi_v = oracle.rotation_from_gaussian(np.random.default_rng(77).standard_normal((d, d)))
+    assert np.max(np.abs(Pi_v - Pi)) > 0.1
+    cv, tv = oracle.lloyd_max(d, 3)
+    rng = np.random.default_rng(12)
+    K, V, q = rng.standard_normal((T, d)), rng.standard_normal((T, d)), rng.standard_normal(d)
+    kr = oracle.quantize_keys(K, Pi, S, ck, tk)
+    vr = oracle.quantize_values(V, Pi_v, cv, tv)
+    logits = oracle.key_logits(q, kr["idx"], kr["signs"], kr["norm"], kr["rnorm"], Pi, S, ck)
+    a = np.exp(logits / math.sqrt(d) - np.max(logits / math.sqrt(d)))
+    a /= a.sum()
+    vhat = vr["norm"][:, None] * (cv[vr["idx"]] @ Pi_v)      # n Pi_v^T c[idx]
+    out = oracle.decode(q[None, None], kr["idx"][None, None], kr["signs"][None, None],
+                        kr["norm"][None, None], kr["rnorm"][None, None], vr["idx"][None, None],
+                        vr["norm"][None, None], Pi, S, ck, cv, Pi_v=Pi_v)[0, 0]
+    assert np.allclose(out, a @ vhat, rtol=1e-12, atol=1e-13)
+    # rotating the values back with the keys' Pi would be wrong
+    wrong = oracle.decode(q[None, None], kr["idx"][None, None], kr["signs"][None, None],
+                          kr["norm"][None, None], kr["rnorm"][None, None], vr["idx"][None, None],
+                          vr["norm"][None, None], Pi, S, ck, cv)[0, 0]
+    assert np.linalg.norm(wrong - a @ vhat) > 0.1 * np.linalg.norm(a @ vhat)
