@@ -139,25 +139,6 @@ def test_decode_small(G, T):
     assert ok, rel
 
 
-@pytest.mark.parametrize("cfg", [3, 5])
-def test_decode_full_size_sampled_rows(cfg):
-    w = inputs.WORKLOADS[cfg]
-    say("decode full size", w.name)
-    K = inputs.keys(w, device="cuda").reshape(w.nseq, w.T, D)
-    tk, pk = _keys(K, w.k_bits, w.norm_dtype)
-    del K
-    V = inputs.values(w, device="cuda").reshape(w.nseq, w.T, D)
-    tv, pv = _values(V, w.v_bits, w.norm_dtype)
-    del V
-    q = inputs.queries(w, device="cuda")
-    got = tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv).cpu().numpy()
-    rng = np.random.default_rng(cfg)
-    rows = [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(3)]
-    ref = _oracle_decode_rows(to64(q), pk, pv, w.k_bits, w.v_bits, w.B, w.Hq, w.Hkv, rows)
-    ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
-    assert ok, rel
-
-
 @pytest.mark.parametrize("kbits,vbits,knd,vnd,G", [
     (1, 4, "f32", "f32", 4), (3, 1, "f16", "f32", 2), (4, 2, "f32", "f16", 8), (2, 3, "f32", "f16", 1)])
 def test_decode_code_widths_and_norm_dtypes(kbits, vbits, knd, vnd, G):

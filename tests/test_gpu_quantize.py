@@ -151,36 +151,3 @@ def test_deterministic_across_runs():
     b = _quantize_keys(X, 3, "f16")
     for u, v in ((a.codes, b.codes), (a.signs, b.signs), (a.norm, b.norm), (a.rnorm, b.rnorm)):
         assert torch.equal(u, v)
-
-
-@pytest.mark.parametrize("cfg", [3, 4])
-def test_full_size_quantize_sampled(cfg):
-    """The full workload in the bench's launch configuration; the oracle
-    checks sampled tokens (keys) and sampled 32-token blocks (values)."""
-    w = inputs.WORKLOADS[cfg]
-    say("full-size quantize", w.name)
-    K = inputs.keys(w, device="cuda").reshape(w.nseq, w.T, D)
-    pk = _quantize_keys(K, w.k_bits, w.norm_dtype)
-    rng = np.random.default_rng(cfg)
-    rows = np.sort(rng.choice(w.nseq * w.T, size=3000, replace=False))
-    Pi, S, c, t = oracle_tables(D, M, w.k_bits)
-    sel = torch.as_tensor(rows, device="cuda")
-    x = to64(K.reshape(-1, D)[sel])
-    codes = pk.codes.reshape(-1, D // 32, w.k_bits)[sel].cpu().numpy().view(np.uint32)
-    signs = pk.signs.reshape(-1, M // 32)[sel].cpu().numpy().view(np.uint32)
-    rep = check_key_stream(x, oracle.unpack_key_codes(codes, D), oracle.unpack_signs(signs, M),
-                           pk.norm.reshape(-1)[sel].cpu().numpy(),
-                           pk.rnorm.reshape(-1)[sel].cpu().numpy(), Pi, S, c, t, w.norm_dtype)
-    assert rep["ok"], rep
-    del K, pk
-    V = inputs.values(w, device="cuda").reshape(w.nseq, w.T, D)
-    pv = _quantize_values(V, w.v_bits, w.norm_dtype)
-    Piv, _, cv, tv = oracle_tables(D, 0, w.v_bits)
-    nblk = (w.T + 31) // 32
-    for s, blk in zip(rng.integers(0, w.nseq, 24), rng.integers(0, nblk, 24)):
-        x = to64(V[s, blk * 32:(blk + 1) * 32])
-        words = pv.codes[s, blk].cpu().numpy().view(np.uint32)[None, None]
-        idx = oracle.unpack_value_codes(words.reshape(1, 1, D, w.v_bits), 32)[0]
-        rep = check_value_stream(x, idx, pv.norm[s, blk * 32:(blk + 1) * 32].cpu().numpy(), Piv,
-                                 cv, tv, w.norm_dtype)
-        assert rep["ok"], (s, blk, rep)
