@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 3
+#define TQ_ABI_VERSION 4
 
 typedef enum {
   TQ_OK = 0,
@@ -251,6 +251,28 @@ size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m);
 tq_status tq_attn_decode(const tq_tables *tk, const tq_tables *tv, const void *q, int q_dtype,
                          int B, int Hq, int Hkv, const tq_packed *k, const tq_packed *v,
                          float scale, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * tq_attn_decode_static -- tq_attn_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, same kernels; the
+ * workspace is an array the library keeps in the memory of every GPU it runs
+ * on (tq_attn_decode_static_capacity() bytes, 16 MiB, held until the process
+ * ends).  The call allocates nothing and calls no allocating routine.
+ *   Arguments as tq_attn_decode, without ws / ws_bytes.
+ *   TQ_EWORKSPACE when tq_decode_workspace() of the call's shape exceeds the
+ *   capacity (about 30,000 query-head x split partials: e.g. 512 query heads
+ *   over 131072 tokens need 4.8 MB, 64 heads over 524288 tokens 3.3 MB).
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's contents (each call writes every byte of it that it reads
+ * before reading it).  Calls whose execution overlaps on one GPU -- on
+ * different streams, or from threads that do not order their streams --
+ * race on the array and must not be issued; calls on one stream are ordered.
+ */
+size_t tq_attn_decode_static_capacity(void);
+tq_status tq_attn_decode_static(const tq_tables *tk, const tq_tables *tv, const void *q, int q_dtype,
+                                int B, int Hq, int Hkv, const tq_packed *k, const tq_packed *v,
+                                float scale, float *out, hipStream_t stream);
 
 /* Workspace bytes for tq_topk (0 for invalid sizes). */
 size_t tq_topk_workspace(int64_t rows, int64_t n, int k);

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/tq.h"
 #include "launch.h"
 
@@ -18,6 +20,8 @@ bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
 
 
 tq_status from_hip(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
 
 // Tables of a stream as the hot-path kernels need them.
 tq_status check_tables(const tq_tables* t, bool key) {
@@ -51,6 +55,40 @@ tq_status check_packed(const tq_packed* p, const tq_tables* t, int role) {
   }
   return TQ_OK;
 }
+
+// The array behind tq_attn_decode_static: decode's workspace for callers
+// that cannot allocate.  Every GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as a
+// device address: device_scratch() takes the address of the current
+// device's copy from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = static_cast<size_t>(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+tq_status device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TQ_EHIP;
+  if (dev >= kMaxDevices) return TQ_EUNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return TQ_EHIP;
+  *ptr = g_scratch_ptr[dev];
+  return TQ_OK;
+}
+
+tq_status decode_args(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype, int B,
+                      int Hq, int Hkv, const tq_packed* k, const tq_packed* v, float scale,
+                      const float* out);
+tq_status decode_checked(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype,
+                         int B, int Hq, int Hkv, const tq_packed* k, const tq_packed* v,
+                         float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 tq_status check_heads(int B, int Hq, int Hkv, int max_group) {
   if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return TQ_EINVAL;
@@ -126,8 +164,6 @@ tq_status tq_append(const tq_tables* t, const void* x, int x_dtype, int64_t n, c
   return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, out->T, n, true, stream));
 }
 
-size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
-
 size_t tq_logits_workspace(int B, int Hq, int d, int m) {
   if (B < 0 || Hq < 0 || d < 0 || m < 0) return 0;
   const size_t nh = static_cast<size_t>(B) * Hq;
@@ -168,6 +204,33 @@ size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m) {
 tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype,
                          int B, int Hq, int Hkv, const tq_packed* k, const tq_packed* v,
                          float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_checked(tk, tv, q, q_dtype, B, Hq, Hkv, k, v, scale, out, ws, ws_bytes, stream);
+}
+
+size_t tq_attn_decode_static_capacity(void) { return kScratchBytes; }
+
+tq_status tq_attn_decode_static(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype,
+                                int B, int Hq, int Hkv, const tq_packed* k, const tq_packed* v,
+                                float scale, float* out, hipStream_t stream) {
+  // arguments first, then the workspace the shape needs against the array,
+  // then the current device's copy of the array
+  tq_status st = decode_args(tk, tv, q, q_dtype, B, Hq, Hkv, k, v, scale, out);
+  if (st != TQ_OK || B == 0) return st;
+  if (tq_decode_workspace(B, Hq, Hkv, k->T, tk->d, tk->m) > kScratchBytes) return TQ_EWORKSPACE;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != TQ_OK) return st;
+  return decode_checked(tk, tv, q, q_dtype, B, Hq, Hkv, k, v, scale, out, ws, kScratchBytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Every argument of a decode call but the workspace.
+tq_status decode_args(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype, int B,
+                      int Hq, int Hkv, const tq_packed* k, const tq_packed* v, float scale,
+                      const float* out) {
   // keys and values may use different rotations (of either kind): queries are
   // rotated with the key table's Pi, the output rotated back with the value
   // table's; both tables hold Pi densely.  The head dimensions must agree.
@@ -190,7 +253,16 @@ tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q
   if (!(scale > 0.0f) || !isfinite(scale)) return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
   if (B == 0) return TQ_OK;
-  if (!ok_ptr(q) || !ok_ptr(out) || !ok_ptr(ws)) return TQ_EINVAL;
+  if (!ok_ptr(q) || !ok_ptr(out)) return TQ_EINVAL;
+  return TQ_OK;
+}
+
+tq_status decode_checked(const tq_tables* tk, const tq_tables* tv, const void* q, int q_dtype,
+                         int B, int Hq, int Hkv, const tq_packed* k, const tq_packed* v,
+                         float scale, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const tq_status st = decode_args(tk, tv, q, q_dtype, B, Hq, Hkv, k, v, scale, out);
+  if (st != TQ_OK || B == 0) return st;
+  if (!ok_ptr(ws)) return TQ_EINVAL;
   const tq::DecodeWorkspace lay = tq::decode_workspace_layout(B, Hq, Hkv, k->T, tk->d, tk->m);
   if (ws_bytes < lay.total) return TQ_EWORKSPACE;
   char* base = static_cast<char*>(ws);
@@ -200,6 +272,10 @@ tq_status tq_attn_decode(const tq_tables* tk, const tq_tables* tv, const void* q
   if (e != hipSuccess) return TQ_EHIP;
   return from_hip(tq::launch_decode(*tk, *tv, qr, u, B, Hq, Hkv, *k, *v, scale, ws, lay, out, stream));
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t tq_topk_workspace(int64_t rows, int64_t n, int k) {
   if (rows < 0 || rows > 65535 || n < 1 || n > INT32_MAX || k < 1 || k > 32 || k > n) return 0;

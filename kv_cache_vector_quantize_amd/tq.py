@@ -84,6 +84,12 @@ def lib():
     L.tq_attn_decode.argtypes = [ctypes.POINTER(Tables), ctypes.POINTER(Tables), vp, i32, i32,
                                  i32, i32, ctypes.POINTER(Packed), ctypes.POINTER(Packed),
                                  ctypes.c_float, vp, vp, sz, vp]
+    L.tq_attn_decode_static_capacity.restype = sz
+    L.tq_attn_decode_static_capacity.argtypes = []
+    L.tq_attn_decode_static.restype = i32
+    L.tq_attn_decode_static.argtypes = [ctypes.POINTER(Tables), ctypes.POINTER(Tables), vp, i32, i32,
+                                        i32, i32, ctypes.POINTER(Packed), ctypes.POINTER(Packed),
+                                        ctypes.c_float, vp, vp]
     _lib = L
     return L
 
@@ -320,6 +326,21 @@ def tq_attn_decode(tk, tv, q, k, v, B, Hq, Hkv, scale=None, ws=None, out=None):
     _check(L.tq_attn_decode(ctypes.byref(t1), ctypes.byref(t2), _ptr(q), _dtype_code(q), B, Hq,
                             Hkv, ctypes.byref(p1), ctypes.byref(p2), float(scale), _ptr(out),
                             _ptr(ws), ws.numel(), _stream(q.device)), "tq_attn_decode")
+    return out
+
+
+def tq_attn_decode_static(tk, tv, q, k, v, B, Hq, Hkv, scale=None, out=None):
+    """tq_attn_decode with the library's own per-GPU workspace (no allocation
+    by the library; ``out`` is allocated here only when not given)."""
+    assert q.is_contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(tk.d)
+    if out is None:
+        out = torch.empty((B, Hq, tk.d), dtype=torch.float32, device=q.device)
+    t1, t2, p1, p2 = tk.c_struct(), tv.c_struct(), k.c_struct(), v.c_struct()
+    _check(lib().tq_attn_decode_static(ctypes.byref(t1), ctypes.byref(t2), _ptr(q), _dtype_code(q), B,
+                                       Hq, Hkv, ctypes.byref(p1), ctypes.byref(p2), float(scale),
+                                       _ptr(out), _stream(q.device)), "tq_attn_decode_static")
     return out
 
 

@@ -30,10 +30,10 @@ def declared_functions():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
-    assert L.tq_abi_version() == 3
+    assert L.tq_abi_version() == 4
 
 
 def test_status_strings(L):
@@ -205,3 +205,24 @@ def test_attention_validation(L):
     pv2 = _packed(tq, role=1, m=0, bits=3, nseq=2, T=64)
     assert L.tq_attn_decode(by(tk), by(tv), q, 1, 1, 32, 2, by(pk2), by(pv2), 0.1, vp(FAKE),
                             vp(FAKE), 1 << 30, None) == -2
+
+
+@needs_no_gpu
+def test_static_decode_rejects_shapes_beyond_its_array(L):
+    """tq_attn_decode_static checks the workspace its shape needs against the
+    array's capacity before anything else: 64 sequences x 64 query heads
+    over 524288 tokens need far more than 16 MiB of split partials."""
+    from kv_cache_vector_quantize_amd import tq
+    by, vp = ctypes.byref, ctypes.c_void_p
+    assert L.tq_attn_decode_static_capacity() == 16 << 20
+    B, Hq, Hkv, T = 64, 64, 8, 524288
+    assert L.tq_decode_workspace(B, Hq, Hkv, T, 128, 128) > 16 << 20
+    tk, tv = _tables(tq), _tables(tq, m=0, sketch=False, bits=3)
+    pk = _packed(tq, nseq=B * Hkv, T=T)
+    pv = _packed(tq, role=1, m=0, bits=3, nseq=B * Hkv, T=T)
+    assert L.tq_attn_decode_static(by(tk), by(tv), vp(FAKE), 1, B, Hq, Hkv, by(pk), by(pv), 0.088,
+                                   vp(FAKE), None) == -3
+    # a bad argument is still rejected as such
+    assert L.tq_attn_decode_static(by(tk), by(tv), vp(FAKE), 1, 1, 30, 8, by(_packed(tq, nseq=8, T=64)),
+                                   by(_packed(tq, role=1, m=0, bits=3, nseq=8, T=64)), 0.088,
+                                   vp(FAKE), None) == -1
