@@ -657,6 +657,351 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Keys, whole stream: the same arithmetic as quantize_mfma_kernel, arranged
+// as a software pipeline so that each wave issues matrix-core and vector
+// work of different units side by side.  Iteration i of a workgroup, one
+// barrier at its end:
+//   phase 1: sketch of unit i-1 (24 MFMAs on the residual staged in LDS)
+//            with the quantization of unit i (the vector ALU on the rotation
+//            computed in iteration i-1: plane bits, residual into LDS);
+//   phase 2: rotation of unit i+1 (16 MFMAs on its staged input) with the
+//            sign bits of unit i-1 and the staging of unit i+2 (norm, range
+//            test, float16 copy into LDS).
+// Residual and input staging are double-buffered by unit parity, the
+// per-token scales ring over 4 units, so one barrier per unit orders every
+// LDS reuse.  Stores and the (rare) out-of-range rescaling happen between
+// the phases, so that each phase is one straight block of code.
+template <typename XT, int BITS, bool HAD>
+__global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
+    const float* __restrict__ rot, const float* __restrict__ sketch,
+    const float* __restrict__ cent, const float* __restrict__ bnd, const XT* __restrict__ x,
+    uint32_t nblk, uint32_t units, int64_t T, int64_t Tp, uint32_t* __restrict__ codes,
+    uint32_t* __restrict__ signs, void* __restrict__ norm, void* __restrict__ rnorm,
+    int norm_dtype) {
+  constexpr bool kSplitX = sizeof(XT) == 4;
+  constexpr int kXP = kSplitX ? 2 : 1;
+  __shared__ __align__(16) _Float16 xs[2][kXP][kUnit][kRowH];   // staged input, by unit parity
+  __shared__ __align__(16) _Float16 rs[2][2][kUnit][kRowH];     // residual hi / lo, by unit parity
+  __shared__ __align__(16) float rinv_s[4][kUnit];              // per-token scale, ring of 4 units
+  __shared__ float n_s[4][kUnit];                               // ||x||, ring of 4 units
+  __shared__ float rho_s[2][4][kUnit];                          // per-wave ||r||^2 (x256^2), by parity
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, h = lane >> 5;
+  const int sv = tid >> 3, sq = tid & 7;   // staging role: token sv, elements 16 sq ..
+
+  QTab<BITS> tab;
+  constexpr int kHalf = (1 << BITS) / 2;
+#pragma unroll
+  for (int i = 0; i < kHalf; ++i) tab.cpos[i] = cent[kHalf + i] * kResScale;
+#pragma unroll
+  for (int i = 0; i + 1 < kHalf; ++i) tab.tpos[i] = bnd[kHalf + i] * kResScale;
+  if constexpr (BITS == 1) tab.tpos[0] = 0.f;
+
+  // A = Pi rows / S rows, permuted as in quantize_mfma_kernel (keys)
+  const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
+  qhalf8 bph[8], bpl[HAD ? 1 : 8], bsh[8], bsl[8];
+  {
+    const int j = 32 * wave + atok;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (HAD) sign_frag(rot + j * kD + 16 * c + 8 * h, bph[c]);
+      else split_frag(rot + j * kD + 16 * c + 8 * h, kPiScale, bph[c], bpl[c]);
+      split_frag(sketch + j * kD + 16 * c + 8 * h, 1.f, bsh[c], bsl[c]);
+    }
+  }
+
+  const uint32_t g0 = blockIdx.x, gstep = gridDim.x;
+  const int n_units = static_cast<int>((units - g0 + gstep - 1) / gstep);   // >= 1 (grid <= units)
+  // first token (sequence * Tp + token) of the workgroup's unit i
+  auto unit_base = [&](int i) -> int64_t {
+    const uint32_t g = g0 + static_cast<uint32_t>(i) * gstep;
+    const uint32_t s = g / nblk, b = g - s * nblk;
+    return static_cast<int64_t>(s) * Tp + static_cast<int64_t>(b) * kUnit;
+  };
+  // loads of unit i's staging share.  Always issued (from token 0 of a valid
+  // unit for lanes past T or units past the workgroup's last), so that the
+  // waits count a fixed number of loads; `ok` marks the lanes whose data
+  // is real, the others are zeroed when the data is used.
+  auto load_unit = [&](int i, RawX<XT>& raw, bool& ok) {
+    const bool unit_ok = i < n_units;
+    const uint32_t g = g0 + static_cast<uint32_t>(unit_ok ? i : 0) * gstep;
+    const uint32_t s = g / nblk, b = g - s * nblk;
+    const int64_t t = static_cast<int64_t>(b) * kUnit + sv;
+    ok = unit_ok && t < T;
+    const uint4* src =
+        reinterpret_cast<const uint4*>(x + ((static_cast<int64_t>(s) * T + (ok ? t : 0)) * kD + 16 * sq));
+#pragma unroll
+    for (int r = 0; r < RawX<XT>::kWords; ++r) raw.w[r] = src[r];
+  };
+  auto keep = [&](RawX<XT>& raw, bool ok) {
+#pragma unroll
+    for (int r = 0; r < RawX<XT>::kWords; ++r)
+      if (!ok) raw.w[r] = make_uint4(0u, 0u, 0u, 0u);
+  };
+  constexpr float kRotScale = HAD ? 11.313708498984761f : kPiScale;   // sqrt(128) or 16
+  static_assert(kD == 128, "sqrt(kD) above");
+  // staging, common path (||x|| in [1, 2^14): no rescaling).  Every lane of
+  // a token writes the token's norm and scale (the same values), so that no
+  // branch splits the block; returns whether the token needs rescaling.
+  auto stage_common = [&](const RawX<XT>& raw, int slot, int buf) -> bool {
+    float xv[16];
+    unpack_raw<XT>(raw, xv);
+    const float ss = sum8(sumsq16<XT>(raw, xv));
+    const float nr = hw_sqrt(ss);
+    n_s[slot][sv] = nr;
+    rinv_s[slot][sv] = (ss > 0.f) ? (kResScale / kRotScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
+    uint32_t wh[8], wl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const qhalf2 hh = {static_cast<_Float16>(xv[2 * e]), static_cast<_Float16>(xv[2 * e + 1])};
+      wh[e] = h2u(hh);
+      if constexpr (kSplitX) {
+        const qhalf2 ll = {static_cast<_Float16>(xv[2 * e] - static_cast<float>(hh[0])),
+                           static_cast<_Float16>(xv[2 * e + 1] - static_cast<float>(hh[1]))};
+        wl[e] = h2u(ll);
+      }
+    }
+    uint4* dh = reinterpret_cast<uint4*>(&xs[buf][0][sv][16 * sq]);
+    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+    if constexpr (kSplitX) {
+      uint4* dl = reinterpret_cast<uint4*>(&xs[buf][kXP - 1][sv][16 * sq]);
+      dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+      dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+    }
+    return !(ss >= 1.f && ss < 0x1p28f);
+  };
+  // staging of a unit with at least one token outside that range: the
+  // general path of quantize_mfma_kernel, for every token (the tokens in
+  // range take sh = 0 and rewrite what stage_common wrote)
+  auto stage_general = [&](const RawX<XT>& raw, int slot, int buf) {
+    float xv[16];
+    unpack_raw<XT>(raw, xv);
+    float ss = sum8(sumsq16<XT>(raw, xv));
+    int sh;
+    if (ss >= 1.f && ss < 0x1p28f) {
+      sh = 0;
+    } else if (ss >= 0x1p-100f && ss <= 0x1p100f) {
+      int e;
+      (void)frexpf(ss, &e);
+      sh = 15 - ((e + 1) >> 1);
+      const float f = pow2f(sh);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xv[i] *= f;
+      ss *= f * f;
+    } else {
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(xv[i]));
+      mx = max8(mx);
+      int e = 0;
+      if (mx > 0.f) (void)frexpf(mx, &e);
+      sh = 11 - e;
+      ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        xv[i] = ldexpf(xv[i], sh);
+        ss = fmaf(xv[i], xv[i], ss);
+      }
+      ss = sum8(ss);
+    }
+    const float nr = hw_sqrt(ss);
+    n_s[slot][sv] = ldexpf(nr, -sh);
+    rinv_s[slot][sv] = (ss > 0.f) ? (kResScale / kRotScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
+    uint32_t wh[8], wl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const qhalf2 hh = {static_cast<_Float16>(xv[2 * e]), static_cast<_Float16>(xv[2 * e + 1])};
+      wh[e] = h2u(hh);
+      if constexpr (kSplitX) {
+        const qhalf2 ll = {static_cast<_Float16>(xv[2 * e] - static_cast<float>(hh[0])),
+                           static_cast<_Float16>(xv[2 * e + 1] - static_cast<float>(hh[1]))};
+        wl[e] = h2u(ll);
+      }
+    }
+    uint4* dh = reinterpret_cast<uint4*>(&xs[buf][0][sv][16 * sq]);
+    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+    if constexpr (kSplitX) {
+      uint4* dl = reinterpret_cast<uint4*>(&xs[buf][kXP - 1][sv][16 * sq]);
+      dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+      dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+    }
+  };
+  auto stage = [&](const RawX<XT>& raw, int slot, int buf) {
+    const bool rare = stage_common(raw, slot, buf);
+    if (__builtin_amdgcn_ballot_w64(rare) != 0) stage_general(raw, slot, buf);
+  };
+  // rotation of the unit staged in xs[buf]: acc[v] = coordinate 32 wave + 16 h + v of token c32
+  auto rotate = [&](int buf, qfloatx16& acc) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const qhalf8 xh = *reinterpret_cast<const qhalf8*>(&xs[buf][0][c32][16 * c + 8 * h]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bph[c], xh, acc, 0, 0, 0);
+      if constexpr (!HAD) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bpl[c], xh, acc, 0, 0, 0);
+      if constexpr (kSplitX) {
+        const qhalf8 xl = *reinterpret_cast<const qhalf8*>(&xs[buf][kXP - 1][c32][16 * c + 8 * h]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(bph[c], xl, acc, 0, 0, 0);
+      }
+    }
+  };
+  // norms of unit i (rho_s holds every wave's share of ||r||^2)
+  auto store_norms = [&](int i) {
+    if (tid < kUnit) {
+      const int pp = i & 1, slot = i & 3;
+      const float rho2 = rho_s[pp][0][tid] + rho_s[pp][1][tid] + rho_s[pp][2][tid] + rho_s[pp][3][tid];
+      const float nx = n_s[slot][tid];
+      const int64_t base = unit_base(i);
+      store_norm(norm, norm_dtype, base + tid, nx);
+      store_norm(rnorm, norm_dtype, base + tid, nx * (hw_sqrt(rho2) / kResScale));
+    }
+  };
+
+  constexpr bool kTwoSets = !kSplitX;   // bf16: loads two units ahead
+  RawX<XT> rawA, rawB;
+  bool okA, okB;
+  // ---- prologue: stage units 0 and 1, loads of units 2 and 3 in flight,
+  // rotation of unit 0
+  load_unit(0, rawA, okA);
+  load_unit(1, rawB, okB);
+  keep(rawA, okA);
+  stage(rawA, 0, 0);
+  keep(rawB, okB);
+  stage(rawB, 1, 1);
+  load_unit(2, rawA, okA);
+  if constexpr (kTwoSets) load_unit(3, rawB, okB);
+  __syncthreads();
+  qfloatx16 acc, z;
+  rotate(0, acc);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) z[k] = 0.f;
+
+  auto iteration = [&](int i, RawX<XT>& raw, bool& ok) {
+    const int pb = i & 1;
+    // ---------------- phase 1: sketch of unit i-1 with the quantization of unit i
+    const float rt = rinv_s[i & 3][c32];
+    uint32_t pw[BITS];
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) pw[p] = 0u;
+    uint32_t hw[8], lw[8];
+    float rr = 0.f, rodd = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) z[k] = 0.f;
+    auto qstep = [&](int v) {
+      const float y = acc[v] * rt;
+      float C;
+      quant_append<BITS>(y, tab, pw, C);
+      float r = y - C;
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm("" : "+v"(r));
+#endif
+      rr = fmaf(r, r, rr);
+      if (v & 1) {
+        rodd = r;
+      } else {
+        const qhalf2 hh = {static_cast<_Float16>(r), static_cast<_Float16>(rodd)};
+        hw[v / 2] = h2u(hh);
+        lw[v / 2] = h2u(split_lo(hh, r, rodd));
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const qhalf8 rh = *reinterpret_cast<const qhalf8*>(&rs[pb ^ 1][0][c32][16 * c + 8 * h]);
+      const qhalf8 rl = *reinterpret_cast<const qhalf8*>(&rs[pb ^ 1][1][c32][16 * c + 8 * h]);
+      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rh, z, 0, 0, 0);
+      qstep(15 - 2 * c);
+      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsl[c], rh, z, 0, 0, 0);
+      qstep(14 - 2 * c);
+      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rl, z, 0, 0, 0);
+    }
+    {
+      uint4* dh = reinterpret_cast<uint4*>(&rs[pb][0][c32][32 * wave + 16 * h]);
+      uint4* dl = reinterpret_cast<uint4*>(&rs[pb][1][c32][32 * wave + 16 * h]);
+      dh[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      dh[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+      dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+    }
+    uint32_t cw[BITS];
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) {
+      const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(pw[p]), 32, 64));
+      cw[p] = ~((pw[p] & 0xFFFFu) | (o << 16));
+    }
+    const float rr32 = rr + __shfl_xor(rr, 32, 64);
+    // codes and ||r||^2 share of unit i
+    if (h == 0) {
+      rho_s[pb][wave][c32] = rr32;
+      uint32_t* dst = codes + ((unit_base(i) + c32) * 4 + wave) * BITS;
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) dst[p] = cw[p];
+    }
+    // ---------------- phase 2: rotation of unit i+1 with the sign bits of
+    // unit i-1 and the staging of unit i+2
+    uint32_t sw = 0u;
+#pragma unroll
+    for (int v = 15; v >= 0; --v) sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(z[v]), 31);
+    const uint32_t so = static_cast<uint32_t>(__shfl_xor(static_cast<int>(sw), 32, 64));
+    rotate(pb ^ 1, acc);
+    keep(raw, ok);
+    const bool rare = stage_common(raw, (i + 2) & 3, pb);
+    if (__builtin_amdgcn_ballot_w64(rare) != 0) stage_general(raw, (i + 2) & 3, pb);
+    if (i > 0) {
+      if (h == 0) {
+        uint32_t word = ~((sw & 0xFFFFu) | (so << 16));
+        if (n_s[(i - 1) & 3][c32] == 0.f) word = 0xFFFFFFFFu;   // a zero vector: every sign bit set
+        signs[(unit_base(i - 1) + c32) * 4 + wave] = word;
+      }
+      store_norms(i - 1);
+    }
+    if constexpr (kTwoSets) load_unit(i + 4, raw, ok);
+    else load_unit(i + 3, raw, ok);
+    __syncthreads();
+  };
+
+  int i = 0;
+  if constexpr (kTwoSets) {
+    for (; i + 1 < n_units; i += 2) {
+      iteration(i, rawA, okA);
+      iteration(i + 1, rawB, okB);
+    }
+    if (i < n_units) {
+      iteration(i, rawA, okA);
+      ++i;
+    }
+  } else {
+    for (; i < n_units; ++i) iteration(i, rawA, okA);
+  }
+  // ---- epilogue: sketch and signs of the last unit
+  {
+    const int last = n_units - 1, pb = last & 1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) z[k] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const qhalf8 rh = *reinterpret_cast<const qhalf8*>(&rs[pb][0][c32][16 * c + 8 * h]);
+      const qhalf8 rl = *reinterpret_cast<const qhalf8*>(&rs[pb][1][c32][16 * c + 8 * h]);
+      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rh, z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsl[c], rh, z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rl, z, 0, 0, 0);
+    }
+    uint32_t sw = 0u;
+#pragma unroll
+    for (int v = 15; v >= 0; --v) sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(z[v]), 31);
+    const uint32_t so = static_cast<uint32_t>(__shfl_xor(static_cast<int>(sw), 32, 64));
+    if (h == 0) {
+      uint32_t word = ~((sw & 0xFFFFu) | (so << 16));
+      if (n_s[last & 3][c32] == 0.f) word = 0xFFFFFFFFu;
+      signs[(unit_base(last) + c32) * 4 + wave] = word;
+    }
+    store_norms(last);
+  }
+}
+
 static int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -695,11 +1040,43 @@ static void launch_dtypes(dim3 grid, hipStream_t stream, const tq_tables& t, con
   }
 }
 
+template <typename XT, bool HAD>
+static void launch_keys_pipe(unsigned grid, hipStream_t stream, const tq_tables& t, const void* x,
+                             const tq_packed& out, uint32_t nblk, uint32_t units) {
+#define TQ_QK(B)                                                                                     \
+  hipLaunchKernelGGL((quantize_keys_pipe_kernel<XT, B, HAD>), dim3(grid), dim3(kQThreads), 0, stream, \
+                     t.rot, t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), nblk, units,  \
+                     out.T, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,           \
+                     out.norm_dtype)
+  switch (t.bits) {
+    case 1: TQ_QK(1); break;
+    case 2: TQ_QK(2); break;
+    case 3: TQ_QK(3); break;
+    default: TQ_QK(4); break;
+  }
+#undef TQ_QK
+}
+
 hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,
                            int64_t pos, int64_t n, bool append, hipStream_t stream) {
   const int64_t nblk = (pos + n + kUnit - 1) / kUnit - pos / kUnit;
   const int64_t units = out.nseq * nblk;
   if (units == 0) return hipSuccess;
+  if (!append && out.role == TQ_KEY && units < (static_cast<int64_t>(1) << 31)) {
+    // whole key streams: the software-pipelined kernel (2 workgroups per CU)
+    const int64_t cap = 2 * static_cast<int64_t>(device_cus());
+    const unsigned grid = static_cast<unsigned>(units < cap ? units : cap);
+    const bool had = t.rot_kind == TQ_ROT_HADAMARD;
+    const uint32_t nb = static_cast<uint32_t>(nblk), nu = static_cast<uint32_t>(units);
+    if (x_dtype == TQ_BF16) {
+      if (had) launch_keys_pipe<uint16_t, true>(grid, stream, t, x, out, nb, nu);
+      else launch_keys_pipe<uint16_t, false>(grid, stream, t, x, out, nb, nu);
+    } else {
+      if (had) launch_keys_pipe<float, true>(grid, stream, t, x, out, nb, nu);
+      else launch_keys_pipe<float, false>(grid, stream, t, x, out, nb, nu);
+    }
+    return hipGetLastError();
+  }
   const int64_t cap = (out.role == TQ_KEY ? 2 : 3) * static_cast<int64_t>(device_cus());
   const dim3 grid(static_cast<unsigned>(units < cap ? units : cap));
   const bool had = t.rot_kind == TQ_ROT_HADAMARD;
