@@ -28,20 +28,25 @@ invariants, brute force).  No function here is "parity unpinned".
 """
 
 from .codebook import (beta_density, bin_mass, bin_first_moment, lloyd_max,
-                       codebook_mse)
+                       codebook_mse, split_codebook, split_widths, centroid_values)
 from .rotation import rotation_from_gaussian, hadamard_matrix, randomized_hadamard
 from .quantize import quantize_keys, quantize_values, residual_and_sketch
 from .packing import (pack_key_codes, unpack_key_codes, pack_signs, unpack_signs,
-                      pack_value_codes, unpack_value_codes, round_norms)
+                      pack_value_codes, unpack_value_codes, round_norms,
+                      pack_key_codes_split, unpack_key_codes_split, pack_value_codes_split,
+                      unpack_value_codes_split)
 from .attention import (query_prep, key_logits, key_logits_from_records,
                         decode, decode_from_records, qjl_scale)
 from .search import topk, search_from_records
 
 __all__ = [
     "beta_density", "bin_mass", "bin_first_moment", "lloyd_max", "codebook_mse",
+    "split_codebook", "split_widths", "centroid_values",
     "rotation_from_gaussian", "hadamard_matrix", "randomized_hadamard", "quantize_keys", "quantize_values",
     "residual_and_sketch", "pack_key_codes", "unpack_key_codes", "pack_signs",
     "unpack_signs", "pack_value_codes", "unpack_value_codes", "round_norms",
+    "pack_key_codes_split", "unpack_key_codes_split", "pack_value_codes_split",
+    "unpack_value_codes_split",
     "query_prep", "key_logits", "key_logits_from_records", "decode",
     "decode_from_records", "qjl_scale", "topk", "search_from_records",
 ]

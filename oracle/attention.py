@@ -29,6 +29,7 @@ once, o = Pi_v^T acc, with Pi_v the rotation the values were quantized with
 
 import numpy as np
 
+from .codebook import centroid_values
 from .packing import unpack_key_codes, unpack_signs, unpack_value_codes
 
 
@@ -50,9 +51,8 @@ def key_logits(q, idx, signs, norm, rnorm, Pi, S, centroids):
     idx [T, d] ints, signs [T, m] bools, norm / rnorm [T] (the stored,
     possibly rounded, values)."""
     qr, u = query_prep(q, Pi, S)
-    c = np.asarray(centroids, dtype=np.float64)
     norm = np.asarray(norm, dtype=np.float64)
-    mse_term = norm * (c[idx] @ qr)
+    mse_term = norm * (centroid_values(centroids, idx) @ qr)
     if S is None:
         return mse_term
     m = np.asarray(S).shape[0]
@@ -89,7 +89,6 @@ def decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, sca
         scale = 1.0 / np.sqrt(d)
     Pi = np.asarray(Pi, dtype=np.float64)
     Pi_v = Pi if Pi_v is None else np.asarray(Pi_v, dtype=np.float64)
-    cv = np.asarray(cv, dtype=np.float64)
     out = np.zeros((B, Hq, d))
     for b in range(B):
         for h in range(Hq):
@@ -98,7 +97,7 @@ def decode(q, k_idx, k_signs, k_norm, k_rnorm, v_idx, v_norm, Pi, S, ck, cv, sca
                            k_norm[b, g], k_rnorm[b, g], Pi, S, ck)
             a = _softmax(scale * l)
             w = a * np.asarray(v_norm[b, g], dtype=np.float64)
-            acc = w @ cv[v_idx[b, g]]
+            acc = w @ centroid_values(cv, v_idx[b, g])
             out[b, h] = Pi_v.T @ acc
     return out
 

@@ -137,3 +137,51 @@ def codebook_mse(d, centroids, bounds):
         m1 = bin_first_moment(d, e[i], e[i + 1])
         total += ci * (ci * m0 - 2.0 * m1)
     return total
+
+
+# ------------------------------------------------------- fractional widths
+# The pages report quality at 2.5 and 3.5 bits per channel (qiita page,
+# "Which bit width is 'lossless'?", first table) without saying how a
+# fractional width is formed.  Reading: a fixed split of the rotated
+# coordinates -- the first `hi` coordinates use the (b+1)-bit Lloyd-Max
+# codebook of the same Beta law, the others the b-bit one (3.5 bits: half
+# the coordinates at 4 bits, half at 3).  The rotated coordinates are
+# exchangeable (each follows the same law), so which ones carry the extra
+# bit does not change the expected distortion, and each group's codebook
+# is the MSE-optimal one for its width.
+
+def split_codebook(d, hi, lo_codebook, hi_codebook):
+    """Per-coordinate codebook of a split width: rows j < hi hold
+    ``hi_codebook`` = (centroids, bounds), rows j >= hi ``lo_codebook``.
+
+    Returns (C [d, L], B [d, L-1]) with L the larger level count; the
+    shorter rows are padded (centroids with NaN, never indexed; bounds with
+    +inf, never reached)."""
+    (c_lo, t_lo), (c_hi, t_hi) = lo_codebook, hi_codebook
+    if not 0 <= hi <= d:
+        raise ValueError("need 0 <= hi <= d")
+    L = max(len(c_lo), len(c_hi))
+    C = np.full((d, L), np.nan)
+    B = np.full((d, L - 1), np.inf)
+    C[:hi, :len(c_hi)] = c_hi
+    B[:hi, :len(t_hi)] = t_hi
+    C[hi:, :len(c_lo)] = c_lo
+    B[hi:, :len(t_lo)] = t_lo
+    return C, B
+
+
+def split_widths(d, bits, hi):
+    """Bits of every coordinate of a split width: bits + 1 below hi, bits above."""
+    return np.where(np.arange(d) < hi, bits + 1, bits)
+
+
+def centroid_values(centroids, idx):
+    """c[idx]: the centroid of every index.  ``centroids`` is one codebook
+    (1-D, shared by every coordinate) or one row per coordinate (2-D,
+    ``split_codebook``), in which case coordinate j (the last axis of idx)
+    takes row j."""
+    c = np.asarray(centroids, dtype=np.float64)
+    idx = np.asarray(idx)
+    if c.ndim == 1:
+        return c[idx]
+    return c[np.arange(c.shape[0]), idx]

@@ -109,3 +109,84 @@ def round_norms(x, dtype):
     if dtype == "f16":
         return x.astype(np.float16)
     raise ValueError(dtype)
+
+
+# ------------------------------------------------ split (fractional) widths
+# A fractional width gives the leading coordinates one bit more than the
+# rest (codebook.split_codebook).  The records keep the layouts above, with
+# each 32-coordinate word (keys) or each coordinate (values) taking its own
+# number of planes / bits, concatenated in coordinate order:
+#   keys    record[..., sum(word_bits)]: word w's word_bits[w] planes,
+#           word after word (bit k of plane p of word w = bit p of
+#           idx[32 w + k]);
+#   values  record[S, block, sum(coord_bits)]: coordinate j's coord_bits[j]
+#           words at offset sum(coord_bits[:j]), its 32 tokens' fields in
+#           token order as in pack_value_codes.
+# With equal widths these are exactly the uniform layouts.
+
+def pack_key_codes_split(idx, word_bits):
+    idx = np.asarray(idx, dtype=np.int64)
+    *lead, d = idx.shape
+    if d != 32 * len(word_bits):
+        raise ValueError("one width per 32-coordinate word")
+    out = np.zeros((*lead, int(np.sum(word_bits))), dtype=np.uint64)
+    o = 0
+    for w, nb in enumerate(word_bits):
+        for p in range(nb):
+            for k in range(32):
+                out[..., o] |= ((idx[..., 32 * w + k] >> p) & 1).astype(np.uint64) << np.uint64(k)
+            o += 1
+    return out.astype(np.uint32)
+
+
+def unpack_key_codes_split(words, d, word_bits):
+    words = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    *lead, nwords = words.shape
+    if nwords != int(np.sum(word_bits)) or d != 32 * len(word_bits):
+        raise ValueError("record size does not match the widths")
+    idx = np.zeros((*lead, d), dtype=np.int64)
+    o = 0
+    for w, nb in enumerate(word_bits):
+        for p in range(nb):
+            for k in range(32):
+                idx[..., 32 * w + k] |= ((words[..., o] >> k) & 1) << p
+            o += 1
+    return idx
+
+
+def pack_value_codes_split(idx, coord_bits):
+    """idx [S, T, d] -> records [S, ceil(T/32), sum(coord_bits)]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    S, T, d = idx.shape
+    nb = (T + 31) // 32
+    padded = np.zeros((S, nb * 32, d), dtype=np.int64)
+    padded[:, :T] = idx
+    blocks = padded.reshape(S, nb, 32, d)
+    out = np.zeros((S, nb, int(np.sum(coord_bits))), dtype=np.uint64)
+    o = 0
+    for j in range(d):
+        b = int(coord_bits[j])
+        for k in range(32):
+            for p in range(b):
+                w, sh = divmod(b * k + p, 32)
+                out[:, :, o + w] |= ((blocks[:, :, k, j] >> p) & 1).astype(np.uint64) << np.uint64(sh)
+        o += b
+    return out.astype(np.uint32)
+
+
+def unpack_value_codes_split(words, T, coord_bits):
+    words = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    S, nb, nwords = words.shape
+    d = len(coord_bits)
+    if nwords != int(np.sum(coord_bits)):
+        raise ValueError("record size does not match the widths")
+    blocks = np.zeros((S, nb, 32, d), dtype=np.int64)
+    o = 0
+    for j in range(d):
+        b = int(coord_bits[j])
+        for k in range(32):
+            for p in range(b):
+                w, sh = divmod(b * k + p, 32)
+                blocks[:, :, k, j] |= ((words[:, :, o + w] >> sh) & 1) << p
+        o += b
+    return blocks.reshape(S, nb * 32, d)[:, :T]

@@ -25,9 +25,14 @@ Readings (the pages are silent on these):
   scale).
 * a zero vector gets norm 0, the index of the cell just above 0
   (L/2), a zero residual and all sign bits 1; it contributes nothing.
+
+``centroids`` / ``bounds`` are one codebook shared by every coordinate, or
+one row per coordinate (a fractional width, ``codebook.split_codebook``).
 """
 
 import numpy as np
+
+from .codebook import centroid_values
 
 
 def _rotate_normalise(X, Pi):
@@ -43,20 +48,26 @@ def _rotate_normalise(X, Pi):
 def _indices(yhat, bounds, zero_mask):
     bounds = np.asarray(bounds, dtype=np.float64)
     idx = np.zeros(yhat.shape, dtype=np.int64)
-    for t in bounds:                   # count of boundaries at or below y
-        idx += (yhat >= t)
-    L = bounds.size + 1
-    idx[zero_mask] = L // 2
+    if bounds.ndim == 1:
+        for t in bounds:               # count of boundaries at or below y
+            idx += (yhat >= t)
+        L = bounds.size + 1
+        idx[zero_mask] = L // 2
+        return idx
+    # one row of boundaries per coordinate (a split width; padding is +inf)
+    for i in range(bounds.shape[1]):
+        idx += (yhat >= bounds[:, i])
+    L = np.sum(np.isfinite(bounds), axis=1) + 1      # levels of each coordinate
+    idx[zero_mask] = (L // 2)[None, :].repeat(int(np.sum(zero_mask)), axis=0)
     return idx
 
 
 def residual_and_sketch(yhat, idx, centroids, S, norm):
     """Residual r = yhat - c[idx], its stored norm ||x||*||r||, the sketch
     z = S r and the sign bits (z >= 0).  Zero vectors give r = 0, z = 0."""
-    c = np.asarray(centroids, dtype=np.float64)
     S = np.asarray(S, dtype=np.float64)
     zero = np.asarray(norm) == 0.0
-    r = yhat - c[idx]
+    r = yhat - centroid_values(centroids, idx)
     r[zero] = 0.0
     rho = np.sqrt(np.sum(r * r, axis=-1))
     z = r @ S.T
