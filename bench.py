@@ -35,12 +35,16 @@ def _sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def key_record_bytes(bits, d=128, m=128, norm_bytes=2):
-    return (d // 32) * bits * 4 + (m // 32) * 4 + 2 * norm_bytes
+def key_record_bytes(bits, d=128, m=128, norm_bytes=2, hi=0):
+    """Bytes of one packed key: code planes (one more plane for the hi/32
+    leading words of a split stream), sign words, two norms."""
+    return ((d // 32) * bits + hi // 32) * 4 + (m // 32) * 4 + 2 * norm_bytes
 
 
-def value_record_bytes(bits, d=128, norm_bytes=2):
-    return (d // 32) * bits * 4 + norm_bytes
+def value_record_bytes(bits, d=128, norm_bytes=2, hi=0):
+    """Bytes of one packed value: d fields of bits (+1 for the hi leading
+    coordinates of a split stream), one norm."""
+    return (d * bits + hi) // 8 + norm_bytes
 
 
 def traffic_from_profiles(kernel_src, kernel_name, workload):
@@ -229,6 +233,9 @@ def main():
     ap.add_argument("--serve-steps", type=int, default=32,
                     help="decode workloads: also time this many serving steps (append one key "
                          "and one value per sequence, then decode) ending at the full context")
+    ap.add_argument("--split", action="store_true",
+                    help="fractional widths: keys and values at bits + 1/2 (the leading half of the "
+                         "rotated coordinates at bits + 1; e.g. 2.5-bit keys + QJL, 3.5-bit values)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (counter scaling)")
     args = ap.parse_args()
@@ -255,9 +262,13 @@ def main():
     G, S = inputs.table_gaussians(d, m)
     had = args.rotation == "hadamard"
     hs = inputs.hadamard_signs(d) if had else None
-    tk = tq.make_tables(G, S, w.k_bits, dev, hadamard_signs=hs)
-    tv = tq.make_tables(G, None, w.v_bits, dev, hadamard_signs=hs) if w.v_bits else None
-    rtag = ", hadamard" if had else ""
+    hi = d // 2 if args.split else 0
+    if args.split and had:
+        print("--split takes the QR rotation", file=sys.stderr)
+        sys.exit(2)
+    tk = tq.make_tables(G, S, w.k_bits, dev, hadamard_signs=hs, hi_coords=hi)
+    tv = tq.make_tables(G, None, w.v_bits, dev, hadamard_signs=hs, hi_coords=hi) if w.v_bits else None
+    rtag = (", hadamard" if had else "") + (", split" if hi else "")
     t0 = time.perf_counter()
     K = inputs.keys(w, device=dev).reshape(w.nseq, w.T, d)
     V = inputs.values(w, device=dev).reshape(w.nseq, w.T, d) if w.v_bits else None
@@ -266,8 +277,8 @@ def main():
     pv = tq.alloc_packed(tq.TQ_VALUE, tv, w.nseq, w.T, w.norm_dtype, dev) if w.v_bits else None
     nvec = w.nseq * w.T
     nb = 2 if w.norm_dtype == "f16" else 4
-    kb = key_record_bytes(w.k_bits, d, m, nb)
-    vb = value_record_bytes(w.v_bits, d, nb) if w.v_bits else 0
+    kb = key_record_bytes(w.k_bits, d, m, nb, hi)
+    vb = value_record_bytes(w.v_bits, d, nb, hi) if w.v_bits else 0
     qbytes = w.B * w.Hq * d * xb
 
     # the stages of one step, in order, with their algorithmic bytes.  The
@@ -281,7 +292,8 @@ def main():
     if w.quantize_timed:
         stages.append({"name": "quantize_k", "bytes": nvec * (d * xb + kb), "units": nvec,
                        "fn": lambda: tq.tq_quantize(tk, K, pk),
-                       "kernel": f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>",
+                       "kernel": (f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>" if hi
+                                  else f"quantize_keys_pipe_kernel<{w.x_dtype}, {w.k_bits}{rtag}>"),
                        "flop_per_unit": 2 * d * d + 2 * m * d,
                        "mfma_flop_per_unit": (rot_products + 3) * 2 * d * d})
         if w.v_bits:
@@ -417,7 +429,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "d": d,
-                   "k_bits": w.k_bits, "qjl_m": m, "v_bits": w.v_bits, "norms": w.norm_dtype,
+                   "k_bits": w.k_bits + (0.5 if hi else 0), "qjl_m": m,
+                   "v_bits": (w.v_bits + (0.5 if hi else 0)) if w.v_bits else 0, "norms": w.norm_dtype,
                    "inputs": inputs_desc, "rotation": args.rotation,
                    "step": [st["name"] for st in stages],
                    "parallelism": "1 GPU"},

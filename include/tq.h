@@ -56,6 +56,22 @@
  *   z = S r, r = Pi x/||x|| - centroid[idx] (rotated domain, unit scale).
  *   Norms are float32 or float16 (round to nearest even), per tq_packed.
  *   A zero vector stores norms 0, idx 2^(bits-1) everywhere and sign bits 1.
+ *
+ * Fractional widths (split streams, hi_coords > 0): the first hi_coords
+ * rotated coordinates are quantized with the (bits+1)-bit codebook
+ * (centroids_hi / bounds_hi), the others with the bits-bit one -- bits + 1/2
+ * per coordinate for hi_coords = d/2, e.g. 2.5 and 3.5 (qiita page, "Which
+ * bit width is 'lossless'?", first table; the split of the rotated
+ * coordinates is this library's reading, the pages give no mechanism).  The
+ * layouts keep the rules above, each coordinate word (keys) or coordinate
+ * (values) taking its own width, concatenated in coordinate order:
+ *   key stream   codes[s][Tp][W], W = (d/32) bits + hi_coords/32: the planes
+ *                of word w (bits+1 of them for 32 w < hi_coords, else bits)
+ *                at record word sum of the widths of words 0..w-1
+ *   value stream codes[s][Tp/32][V], V = d bits + hi_coords: the record of
+ *                coordinate j (bits+1 words for j < hi_coords, else bits) at
+ *                record word sum of the widths of coordinates 0..j-1
+ *   A zero vector stores idx 2^(width-1) at each coordinate.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -68,7 +84,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 4
+#define TQ_ABI_VERSION 5
 
 typedef enum {
   TQ_OK = 0,
@@ -98,6 +114,10 @@ typedef struct {
   const float *sketch;     /* S, m x d row-major, iid N(0,1); NULL when m == 0    */
   const float *centroids;  /* 2^bits ascending, unit-sphere scale                 */
   const float *bounds;     /* 2^bits - 1 ascending decision boundaries            */
+  int32_t hi_coords;       /* leading rotated coordinates at bits + 1: 0 (every  */
+                           /* coordinate at bits) or d/2 (bits + 1/2 per coord)   */
+  const float *centroids_hi; /* 2^(bits+1) centroids, NULL when hi_coords == 0    */
+  const float *bounds_hi;  /* 2^(bits+1) - 1 boundaries, NULL when hi_coords == 0 */
 } tq_tables;
 
 /* A packed key or value stream of nseq sequences of T tokens (caller-owned). */
@@ -115,6 +135,7 @@ typedef struct {
   int32_t norm_dtype;      /* TQ_F32 or TQ_F16                                    */
   int32_t capacity;        /* tokens stored per sequence (Tp): 0, or a multiple   */
                            /* of 32 that is >= T (a cache that grows by append)   */
+  int32_t hi_coords;       /* must equal the tables' hi_coords                    */
 } tq_packed;
 
 /* Version of this ABI (TQ_ABI_VERSION of the built library). */
@@ -176,7 +197,9 @@ tq_status tq_hadamard_rotation(int d, const float *signs, float *rot32, hipStrea
  * "How to implement", item 1 (quantize on every cache update).
  *   t      tables of the stream (t->m > 0 for keys, 0 for values)
  *   x      in, [out->nseq][out->T][d] of x_dtype (TQ_F32 or TQ_BF16)
- *   out    packed stream to write; role, bits, d, m must match t
+ *   out    packed stream to write; role, bits, d, m, hi_coords must match t
+ * Split streams (hi_coords = d/2) take bits 1..3 and a dense rotation
+ * (TQ_EUNSUPPORTED otherwise).
  */
 tq_status tq_quantize(const tq_tables *t, const void *x, int x_dtype, const tq_packed *out,
                       hipStream_t stream);
@@ -218,7 +241,8 @@ size_t tq_logits_workspace(int B, int Hq, int d, int m);
  *   logits   out, [B][Hq][T] float32; query head h reads kv head h/(Hq/Hkv)
  *   ws       workspace of at least tq_logits_workspace(B, Hq, d, m) bytes
  * Hq/Hkv must be 1, 2, 4, 8 or 16 (else TQ_EUNSUPPORTED); T < 2^28 and
- * B*Hkv <= 65535 (else TQ_EUNSUPPORTED).
+ * B*Hkv <= 65535 (else TQ_EUNSUPPORTED).  A split key stream (hi_coords =
+ * d/2) takes bits 2 or 3 and Hq/Hkv <= 8.
  */
 tq_status tq_attn_logits(const tq_tables *tk, const void *q, int q_dtype, int B, int Hq, int Hkv,
                          const tq_packed *k, float *logits, void *ws, size_t ws_bytes,
@@ -243,7 +267,9 @@ size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m);
  *   ws       workspace of at least tq_decode_workspace(B, Hq, Hkv, T, d, m) bytes
  * Hq/Hkv must be 1, 2, 4 or 8, T < 2^28 and B*Hkv <= 65535 (else
  * TQ_EUNSUPPORTED).  Key and value norms may be stored as float16 or float32
- * independently.  Logits carry float32-grade accuracy (float16 hi/lo operand
+ * independently.  Split streams (hi_coords = d/2: 2.5 / 3.5-bit keys or
+ * values) are decoded when both streams are split, with bits 2 or 3 each and
+ * float16 norms (else TQ_EUNSUPPORTED).  Logits carry float32-grade accuracy (float16 hi/lo operand
  * pairs, float32 accumulation); the value weights enter the value contraction
  * as float16 (at most 2^8 relative to the running maximum): out matches an
  * exact evaluation to a few 1e-4 of its norm (the tests bound it by 2e-3).

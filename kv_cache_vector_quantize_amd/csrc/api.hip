@@ -32,16 +32,27 @@ tq_status check_tables(const tq_tables* t, bool key) {
   if (key ? t->m == 0 : t->m != 0) return TQ_EINVAL;
   if (!ok_ptr(t->rot) || !ok_ptr(t->centroids) || !ok_ptr(t->bounds)) return TQ_EINVAL;
   if (key ? !ok_ptr(t->sketch) : t->sketch != nullptr) return TQ_EINVAL;
+  // split (fractional) widths: the leading hi_coords coordinates at bits + 1
+  if (t->hi_coords < 0 || t->hi_coords > t->d || t->hi_coords % 32 != 0) return TQ_EINVAL;
+  if (t->hi_coords > 0) {
+    if (t->bits > 3 || !ok_ptr(t->centroids_hi) || !ok_ptr(t->bounds_hi)) return TQ_EINVAL;
+  } else if (t->centroids_hi != nullptr || t->bounds_hi != nullptr) {
+    return TQ_EINVAL;
+  }
   if (t->d != kSupportedD) return TQ_EUNSUPPORTED;
   if (key && t->m != kSupportedM) return TQ_EUNSUPPORTED;
+  if (t->hi_coords != 0 && t->hi_coords != t->d / 2) return TQ_EUNSUPPORTED;
   return TQ_OK;
 }
+
+bool split(const tq_tables* t) { return t->hi_coords != 0; }
 
 tq_status check_packed(const tq_packed* p, const tq_tables* t, int role) {
   if (p == nullptr) return TQ_EINVAL;
   if (p->role != role) return TQ_EINVAL;
   if (p->capacity < 0 || p->capacity % 32 != 0 || (p->capacity != 0 && p->capacity < p->T)) return TQ_EINVAL;
-  if (p->bits != t->bits || p->d != t->d || p->m != t->m) return TQ_EINVAL;
+  if (p->bits != t->bits || p->d != t->d || p->m != t->m || p->hi_coords != t->hi_coords)
+    return TQ_EINVAL;
   if (p->nseq < 0 || p->T < 0) return TQ_EINVAL;
   if (p->norm_dtype != TQ_F32 && p->norm_dtype != TQ_F16) return TQ_EINVAL;
   const bool empty = p->nseq == 0 || p->T == 0;
@@ -142,6 +153,7 @@ tq_status tq_quantize(const tq_tables* t, const void* x, int x_dtype, const tq_p
   st = check_packed(out, t, out->role);
   if (st != TQ_OK) return st;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
+  if (split(t) && t->rot_kind != TQ_ROT_DENSE) return TQ_EUNSUPPORTED;
   if (out->nseq == 0 || out->T == 0) return TQ_OK;
   if (!ok_ptr(x)) return TQ_EINVAL;
   return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, 0, out->T, false, stream));
@@ -157,6 +169,7 @@ tq_status tq_append(const tq_tables* t, const void* x, int x_dtype, int64_t n, c
   st = check_packed(out, t, out->role);
   if (st != TQ_OK) return st;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
+  if (split(t) && t->rot_kind != TQ_ROT_DENSE) return TQ_EUNSUPPORTED;
   // the new tokens must fit the stream's storage
   if (n < 0 || out->capacity == 0 || n > out->capacity - out->T) return TQ_EINVAL;
   if (out->nseq == 0 || n == 0) return TQ_OK;
@@ -182,6 +195,8 @@ tq_status tq_attn_logits(const tq_tables* tk, const void* q, int q_dtype, int B,
   if (k->nseq != static_cast<int64_t>(B) * Hkv) return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
   if (k->nseq > 65535) return TQ_EUNSUPPORTED;  // one grid row per sequence
+  // split keys: 2.5 / 3.5 bits on the matrix-core tiles
+  if (split(tk) && (tk->bits < 2 || Hq / Hkv > 8)) return TQ_EUNSUPPORTED;
   if (B == 0 || k->T == 0) return TQ_OK;
   if (!ok_ptr(q) || !ok_ptr(logits) || !ok_ptr(ws)) return TQ_EINVAL;
   if (ws_bytes < tq_logits_workspace(B, Hq, tk->d, tk->m)) return TQ_EWORKSPACE;
@@ -250,6 +265,12 @@ tq_status decode_args(const tq_tables* tk, const tq_tables* tv, const void* q, i
   if (k->T < 1 && B > 0) return TQ_EINVAL;
   if (k->nseq > 65535) return TQ_EUNSUPPORTED;  // one grid row per sequence
   if (k->T >= (static_cast<int64_t>(1) << 28)) return TQ_EUNSUPPORTED;  // 32-bit record offsets
+  // split streams: both split, bits 2 or 3 each, float16 norms
+  if (split(tk) || split(tv)) {
+    if (!split(tk) || !split(tv) || tk->bits < 2 || tv->bits < 2 || k->norm_dtype != TQ_F16 ||
+        v->norm_dtype != TQ_F16)
+      return TQ_EUNSUPPORTED;
+  }
   if (!(scale > 0.0f) || !isfinite(scale)) return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
   if (B == 0) return TQ_OK;

@@ -110,8 +110,9 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
   if (B == 0) return hipSuccess;
   const int G = Hq / Hkv;
   const int64_t nseq = static_cast<int64_t>(B) * Hkv;
+  const bool mx = tk.hi_coords != 0;
   const int occ = ring_occupancy_bytes(packet_bytes(k.bits, v.bits, k.norm_dtype == TQ_F16 ? 2 : 4,
-                                                     v.norm_dtype == TQ_F16 ? 2 : 4));
+                                                    v.norm_dtype == TQ_F16 ? 2 : 4, mx), mx);
   const int len = split_length(nseq, k.T, kDecMaxSplit, static_cast<int64_t>(occ) * kCus);
   const int nsplit = static_cast<int>((k.T + len - 1) / len);
   // the softmax runs in base 2: the query fragments carry scale * log2(e),

@@ -58,6 +58,14 @@ constexpr float kTau = 8.0f;      // raise the reference max when a block exceed
 // 2-bit key table is therefore indexed by coordinate pairs (16 entries)
 // rather than quads.
 constexpr int kSgnOff = 2048, kVluOff = 4096, kTabBytes = kVluOff + 1024;
+// Split streams (MX, fractional widths): coordinates 0..63 take one bit more
+// than 64..127.  The wide key pair table sits at 0 and the wide value table
+// at kVluOff as above; the narrow ones follow the sign table and the wide
+// value table.
+constexpr int kNarrowKeyOff = kSgnOff + 256, kNarrowVluOff = kVluOff + 1024;
+constexpr int kTabBytesMix = kNarrowVluOff + 256;
+template <bool MX>
+constexpr int tab_bytes() { return MX ? kTabBytesMix : kTabBytes; }
 
 
 __device__ __forceinline__ uint32_t h2u(_Float16 lo, _Float16 hi) {
@@ -199,12 +207,21 @@ __device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const c
 // <u, 2s - 1> (qj) of head n (n < G; the other lanes hold partial sums).
 // pw: the tile token's KB plane words of coordinate word g4; sw: its sign
 // word; tab: the LDS tables of build_tables.
-template <int G, int KB, bool X2>
+// MX (split streams): pw holds KB planes, the narrow words' top plane zero,
+// and ktab is the lane's own pair table (wide or narrow, generic layout).
+template <int G, int KB, bool X2, bool MX = false>
 __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
                                             const half8 (&bu)[4], const char* tab, float (&cen)[4],
-                                            float (&qj)[4]) {
+                                            float (&qj)[4], const char* ktab = nullptr) {
   floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (X2) {
+  if constexpr (MX) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint2 x = *reinterpret_cast<const uint2*>(ktab + (pair_index<KB>(pw, 2 * c) << 3));
+      const uint2 y = *reinterpret_cast<const uint2*>(ktab + (pair_index<KB>(pw, 2 * c + 1) << 3));
+      accC = __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), bq[c], accC, 0, 0, 0);
+    }
+  } else if constexpr (X2) {
     static_assert(KB == 2, "exact float16 levels exist for 2-bit keys only");
     // same pair-index words as below; one float16 level per coordinate
     const uint32_t Q = ((pw[1] << 2) & 0xCCCCCCCCu) | (pw[0] & 0x33333333u);
@@ -374,6 +391,53 @@ __device__ __forceinline__ Levels2 exact_levels2(const float* __restrict__ ck, i
 //  * X2 (2-bit keys on exact float16 levels): entry x (4 bytes at 8x) holds
 //    the levels of the coordinate pair whose plane-0 bits are x & 3 and
 //    plane-1 bits x >> 2, from {-la, -lb, lb, la} (exact_levels2).
+// generic pair table of a kb-bit codebook (entry x: uint2 at 8x, as below)
+__device__ __forceinline__ void build_pair_table(const float* __restrict__ ck, int kb, char* tab, int tid,
+                                                 int nthreads) {
+  uint2* pair = reinterpret_cast<uint2*>(tab);
+  for (int x = tid; x < (1 << (2 * kb)); x += nthreads) {
+    int ia = 0, ib = 0;
+    for (int p = 0; p < kb; ++p) {
+      ia |= ((x >> (2 * p)) & 1) << p;
+      ib |= ((x >> (2 * p + 1)) & 1) << p;
+    }
+    const float ca = ck[ia], cb = ck[ib];
+    const _Float16 ha = static_cast<_Float16>(ca), hb = static_cast<_Float16>(cb);
+    const _Float16 la = static_cast<_Float16>(ca - static_cast<float>(ha));
+    const _Float16 lb = static_cast<_Float16>(cb - static_cast<float>(hb));
+    pair[x] = make_uint2(h2u(ha, hb), h2u(la, lb));
+  }
+}
+
+// value pair table of a vb-bit codebook (entry x: the centroids of the token
+// pair whose fields are x & (2^vb - 1) and x >> vb)
+__device__ __forceinline__ void build_value_table(const float* __restrict__ cv, int vb, char* tab, int tid,
+                                                  int nthreads) {
+  uint32_t* vlut = reinterpret_cast<uint32_t*>(tab);
+  for (int x = tid; x < (1 << (2 * vb)); x += nthreads)
+    vlut[x] = h2u(static_cast<_Float16>(cv[x & ((1 << vb) - 1)]), static_cast<_Float16>(cv[x >> vb]));
+}
+
+// Tables of split streams: key pair tables (KB + 1 bits at 0, KB bits at
+// kNarrowKeyOff; the lanes of words 0 and 1 index the first, of words 2 and
+// 3 the second, with a zero top plane), the sign table, and value tables
+// (VB + 1 bits at kVluOff, VB bits at kNarrowVluOff).
+template <int KB, int VB>
+__device__ __forceinline__ void build_tables_mix(const float* __restrict__ ck, const float* __restrict__ ck_hi,
+                                                 const float* __restrict__ cv, const float* __restrict__ cv_hi,
+                                                 char* tab, int tid, int nthreads) {
+  build_pair_table(ck_hi, KB + 1, tab, tid, nthreads);
+  build_pair_table(ck, KB, tab + kNarrowKeyOff, tid, nthreads);
+  for (int x = tid; x < 16; x += nthreads) {
+    auto pm = [&](int i) { return static_cast<_Float16>(((x >> i) & 1) ? 1.f : -1.f); };
+    *reinterpret_cast<uint2*>(tab + kSgnOff + 16 * x) = make_uint2(h2u(pm(0), pm(1)), h2u(pm(2), pm(3)));
+  }
+  if constexpr (VB > 0) {
+    build_value_table(cv_hi, VB + 1, tab + kVluOff, tid, nthreads);
+    build_value_table(cv, VB, tab + kNarrowVluOff, tid, nthreads);
+  }
+}
+
 template <int KB, int VB, bool X2>
 __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const float* __restrict__ cv,
                                              char* tab, int tid, int nthreads, float la = 0.f,
@@ -436,13 +500,17 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ ck, const
 constexpr int kRing = 3;
 static_assert(kRing == 2 || kRing == 3, "the waits below cover rings of 2 or 3 blocks");
 
-// NK / NV: bytes per stored key / value norm (2: float16, 4: float32)
-template <int KB, int VB, int NK, int NV>
+// NK / NV: bytes per stored key / value norm (2: float16, 4: float32).  MX:
+// split streams, whose key records hold 4 KB + 2 words per token (words 0
+// and 1 at KB + 1 planes) and value records 128 VB + 64 words per block.
+template <int KB, int VB, int NK, int NV, bool MX = false>
 struct Packet {
-  static constexpr int kKC = 0;                // key plane words [32 tokens][4][KB]
-  static constexpr int kSG = 512 * KB;         // sign words [32][4]
-  static constexpr int kVC = kSG + 512;        // value records [128 coordinates][VB]
-  static constexpr int kNK = kVC + 512 * VB;   // ||k|| [32]
+  static constexpr int kKeyRec = MX ? 4 * KB + 2 : 4 * KB;          // words per token
+  static constexpr int kValRec = VB == 0 ? 0 : (MX ? 128 * VB + 64 : 128 * VB);  // words per block
+  static constexpr int kKC = 0;                // key plane words [32 tokens][kKeyRec]
+  static constexpr int kSG = 128 * kKeyRec;    // sign words [32][4]
+  static constexpr int kVC = kSG + 512;        // value records [kValRec]
+  static constexpr int kNK = kVC + 4 * kValRec;   // ||k|| [32]
   static constexpr int kNR = kNK + 32 * NK;    // ||k|| ||r|| [32]
   static constexpr int kNV = kNR + 32 * NK;    // ||v|| [32]
   static constexpr int kBytes = kNV + 32 * NV;
@@ -555,19 +623,42 @@ struct BlockStream {
   // tok / tokv: index of the wave's first token in the key / value stream
   // (sequence * its stride + token); value segment and value norms are empty
   // when P has VB = 0 / NV = 0
-  template <int KB, int VB, int NK, int NV>
+  template <int KB, int VB, int NK, int NV, bool MX = false>
   __device__ __forceinline__ void init(const uint32_t* kcodes, const uint32_t* ksigns, const void* knorm,
                                        const void* krnorm, const uint32_t* vcodes, const void* vnorm,
                                        int64_t tok, int64_t tokv, int lane, uint32_t ring_wave0,
                                        int slot_bytes) {
     ring0 = ring_wave0;
     kslot = slot_bytes;
+    constexpr int kKeyChunks = 8 * P::kKeyRec;         // 32 tokens x kKeyRec words / 16 B
+    constexpr int kValChunks = P::kValRec / 4;
 #pragma unroll
     for (int i = 0; i < P::kInstr; ++i) {
       const int c = 64 * i + lane;
       const char* p = reinterpret_cast<const char*>(kcodes);
       int64_t st = 0;
-      if (c < 32 * KB) {
+      if (MX && c < kKeyChunks) {
+        // split keys: the block's records in token order
+        p = reinterpret_cast<const char*>(kcodes) + tok * 4 * P::kKeyRec + 16 * c;
+        st = 4 * 32 * 4 * P::kKeyRec;
+      } else if (MX && c < kKeyChunks + 32) {
+        p = reinterpret_cast<const char*>(ksigns) + tok * 16 + 16 * ring_token(c - kKeyChunks);
+        st = 4 * 32 * 16;
+      } else if (MX && c < kKeyChunks + 32 + kValChunks) {
+        p = reinterpret_cast<const char*>(vcodes) + (tokv / 32) * 4 * P::kValRec + 16 * (c - kKeyChunks - 32);
+        st = 4 * 4 * P::kValRec;
+      } else if (MX && c < kKeyChunks + 32 + kValChunks + 4 * NK) {
+        const int e = c - kKeyChunks - 32 - kValChunks;
+        const int row = e / (2 * NK);
+        p = reinterpret_cast<const char*>(row == 0 ? knorm : krnorm) + tok * NK + 16 * (e - 2 * NK * row);
+        st = 4 * 32 * NK;
+      } else if (MX && c < P::kChunks) {
+        const int e = c - kKeyChunks - 32 - kValChunks - 4 * NK;
+        p = reinterpret_cast<const char*>(vnorm) + tokv * NV + 16 * e;
+        st = 4 * 32 * NV;
+      } else if (MX) {
+        // past the packet: nothing is fetched (lanes of the last instruction only)
+      } else if (c < 32 * KB) {
         // ring slot c holds chunk h of token t: c = 32 h + ring_slot(t), or
         // c = 3 ring_slot(t) + h for 3-plane keys (ring_key_words)
         const int t = ring_token(KB == 3 ? c / 3 : c & 31);
@@ -630,33 +721,47 @@ __device__ __forceinline__ float norm_at(const char* p, int i) {
 
 // workgroups per CU that the LDS of a workgroup (tables + ring of packets of
 // `bytes`) allows, at most 3; the host sizes decode splits by it
-constexpr int ring_occupancy_bytes(int bytes) {
-  return (kTabBytes + kRing * 4 * bytes) * 3 <= 160 * 1024 ? 3 : 2;
+constexpr int ring_occupancy_bytes(int bytes, bool mx = false) {
+  return ((mx ? kTabBytesMix : kTabBytes) + kRing * 4 * bytes) * 3 <= 160 * 1024 ? 3 : 2;
 }
 
-// bytes of one block's packet (Packet<KB, VB, NK, NV>::kBytes)
-constexpr int packet_bytes(int kb, int vb, int nk, int nv) {
-  return 512 * kb + 512 + 512 * vb + 64 * nk + 32 * nv;
+// bytes of one block's packet (Packet<KB, VB, NK, NV, MX>::kBytes)
+constexpr int packet_bytes(int kb, int vb, int nk, int nv, bool mx = false) {
+  return 512 * kb + 512 + 512 * vb + 64 * nk + 32 * nv + (mx ? 256 + (vb > 0 ? 256 : 0) : 0);
 }
 
-template <typename P>
+template <typename P, bool MX = false>
 constexpr int ring_occupancy() {
-  return ring_occupancy_bytes(P::kBytes);
+  return ring_occupancy_bytes(P::kBytes, MX);
+}
+static_assert(packet_bytes(3, 3, 2, 2, true) == Packet<3, 3, 2, 2, true>::kBytes, "split packet size");
+static_assert(packet_bytes(2, 3, 2, 2) == Packet<2, 3, 2, 2>::kBytes, "packet size");
+
+// The key-table base and key-word offset of lane (n, g4) in a split stream:
+// words 0 and 1 (lane groups 0, 1) use the wide table, 2 and 3 the narrow
+// one; the lane's token row t = 8 (n/4) + n%4 of tile 0 (tile 1: 4 tokens
+// on), its word's planes after those of the words before it.
+template <int KB>
+__device__ __forceinline__ uint32_t mix_key_lane_off(int n, int g4) {
+  constexpr int rec = 4 * KB + 2;
+  const int t = 8 * (n >> 2) + (n & 3);
+  return 4 * (t * rec + g4 * KB + (g4 < 2 ? g4 : 2));
 }
 
-template <int G, int KB, int VB, int NK, int NV>
-__global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>>())) void decode_mfma_kernel(
+template <int G, int KB, int VB, int NK, int NV, bool MX = false>
+__global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV, MX>, MX>())) void decode_mfma_kernel(
     const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
     const float* __restrict__ cv, int64_t T, int64_t TpK, int64_t TpV, int split_len,
     const uint32_t* __restrict__ kcodes, const uint32_t* __restrict__ ksigns, const void* knorm,
     const void* krnorm, const uint32_t* __restrict__ vcodes, const void* vnorm, float fq, float fu,
-    int nsplit, float* __restrict__ partials) {
-  using P = Packet<KB, VB, NK, NV>;
+    int nsplit, float* __restrict__ partials, const float* __restrict__ ck_hi = nullptr,
+    const float* __restrict__ cv_hi = nullptr) {
+  using P = Packet<KB, VB, NK, NV, MX>;
   constexpr int VL = 1 << (2 * VB);
   constexpr int kSlot = 4 * P::kBytes;   // one ring slot: the 4 waves' packets
   // code tables (build_tables); the ring; after the main loop the ring holds
   // the four waves' softmax states for the merge
-  __shared__ __align__(16) char lds[kTabBytes];
+  __shared__ __align__(16) char lds[tab_bytes<MX>()];
   constexpr int kMerge = (2 * 4 * 16 + 4 * G * kDD) * 4;
   __shared__ __align__(16) char ring[kRing * kSlot > kMerge ? kRing * kSlot : kMerge];
   const uint32_t* vlut = reinterpret_cast<const uint32_t*>(lds + kVluOff);
@@ -675,18 +780,20 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
   const int nbw = (nb_split > wave) ? (nb_split - wave + 3) / 4 : 0;
 
   BlockStream<P> st;
-  st.template init<KB, VB, NK, NV>(kcodes, ksigns, knorm, krnorm, vcodes, vnorm, s * TpK + t0 + 32 * wave,
-                                   s * TpV + t0 + 32 * wave, lane, lds_addr(ring) + wave * P::kBytes, kSlot);
+  st.template init<KB, VB, NK, NV, MX>(kcodes, ksigns, knorm, krnorm, vcodes, vnorm, s * TpK + t0 + 32 * wave,
+                                       s * TpV + t0 + 32 * wave, lane, lds_addr(ring) + wave * P::kBytes, kSlot);
 #pragma unroll
   for (int jj = 0; jj + 1 < kRing; ++jj)
     if (jj < nbw) st.issue(jj, jj, lane);
 
   // 2-bit keys: exact float16 levels, one K-slot per coordinate
-  constexpr bool X2 = KB == 2;
+  constexpr bool X2 = KB == 2 && !MX;
   __shared__ unsigned long long red2[X2 ? kDecThreads / 64 : 1];
   Levels2 lev{0.f, 0.f, 1.f};
   if constexpr (X2) lev = exact_levels2(ck, tid, red2);
-  build_tables<KB, VB, X2>(ck, cv, lds, tid, kDecThreads, lev.la, lev.lb);  // visible after the barrier below
+  // visible after the barrier below
+  if constexpr (MX) build_tables_mix<KB, VB>(ck, ck_hi, cv, cv_hi, lds, tid, kDecThreads);
+  else build_tables<KB, VB, X2>(ck, cv, lds, tid, kDecThreads, lev.la, lev.lb);
   half8 bq[8], bu[4];
   query_frags<G, X2>(qr, u, s, lane, fq * lev.fc, fu, bq, bu);
   __syncthreads();
@@ -709,9 +816,18 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
   const int vwlo = vbit0 >> 5, vsh = vbit0 & 31;
   // this lane's byte offsets within a packet: key words, sign word, its 8
   // tokens' norms (key and value), value record words
-  const uint32_t koff = P::kKC + key_lane_off<KB>(n, g4), soff = P::kSG + 16 * n + 4 * g4;
+  const uint32_t koff = P::kKC + (MX ? mix_key_lane_off<KB>(n, g4) : key_lane_off<KB>(n, g4));
+  const uint32_t soff = P::kSG + 16 * n + 4 * g4;
   const uint32_t nkoff = 8 * NK * g4, nvoff = 8 * NV * g4;
   const uint32_t voff = P::kVC + 4 * (n * VB + vwlo);
+  // split streams: lane's key table, and the value record words / shifts of
+  // the wide coordinates (0..63, VB + 1 bits) and the narrow ones (VB bits)
+  const char* ktab = lds + ((MX && g4 >= 2) ? kNarrowKeyOff : 0);
+  constexpr int VW = MX ? VB + 1 : VB;
+  const int vbitW = 8 * VW * g4;
+  const uint32_t voffW = P::kVC + 4 * (n * VW + (vbitW >> 5));
+  const uint32_t voffN = P::kVC + 4 * (64 * VW + n * VB + vwlo);
+  const int vshW = vbitW & 31;
 
   int slot = 0;
   for (int j = 0; j < nbw; ++j) {
@@ -728,10 +844,22 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
     float sv[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      uint32_t kw[KB], sw;
-      ring_key_words<KB>(kb, sb, tile, kw, sw);
       float cen[4], qj[4];
-      tile_logits<G, KB, X2>(kw, sw, bq, bu, lds, cen, qj);
+      if constexpr (MX) {
+        // split keys: KB + 1 plane words read for every word, the narrow
+        // words' top one cleared; token rows 4 tokens apart between tiles
+        uint32_t kw[KB + 1];
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(kb + 16 * (4 * KB + 2) * tile);
+#pragma unroll
+        for (int q = 0; q <= KB; ++q) kw[q] = kp[q];
+        if (g4 >= 2) kw[KB] = 0u;
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + 256 * tile);
+        tile_logits<G, KB + 1, false, true>(kw, sw, bq, bu, lds, cen, qj, ktab);
+      } else {
+        uint32_t kw[KB], sw;
+        ring_key_words<KB>(kb, sb, tile, kw, sw);
+        tile_logits<G, KB, X2>(kw, sw, bq, bu, lds, cen, qj);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float nk = norm_at<NK>(nkb + P::kNK, 4 * tile + i), nr = norm_at<NK>(nkb + P::kNR, 4 * tile + i);
@@ -828,6 +956,24 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
         pa[k] = static_cast<_Float16>(p * nv[k]);
       }
     }
+    if constexpr (MX) {
+      // split values: coordinates 0..63 (nt < 4) at VB + 1 bits, 64..127 at VB
+      const uint32_t* vrw = reinterpret_cast<const uint32_t*>(lds_at(ring, pko + voffW));
+      const uint32_t* vrn = reinterpret_cast<const uint32_t*>(lds_at(ring, pko + voffN));
+      const uint32_t* vlutW = reinterpret_cast<const uint32_t*>(lds + kVluOff);
+      const uint32_t* vlutN = reinterpret_cast<const uint32_t*>(lds + kNarrowVluOff);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bool wide_nt = nt < 4;
+        const uint32_t* vr = wide_nt ? vrw + 16 * nt * VW : vrn + 16 * (nt - 4) * VB;
+        const uint32_t X = __builtin_amdgcn_alignbit(vr[1], vr[0], wide_nt ? vshW : vsh);
+        uint32_t bw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bw[q] = wide_nt ? vlutW[(X >> (2 * VW * q)) & ((1 << (2 * VW)) - 1)] : vlutN[(X >> (2 * VB * q)) & (VL - 1)];
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, u4_to_h8(bw[0], bw[1], bw[2], bw[3]), O[nt], 0, 0, 0);
+      }
+    } else {
     // two base addresses, so that every record word is an immediate offset
     // of a paired 4-byte read (at most 255 words away)
     const uint32_t* vrec0 = reinterpret_cast<const uint32_t*>(lds_at(ring, pko + voff));
@@ -840,6 +986,7 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
 #pragma unroll
       for (int q = 0; q < 4; ++q) bw[q] = vlut[(X >> (2 * VB * q)) & (VL - 1)];
       O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, u4_to_h8(bw[0], bw[1], bw[2], bw[3]), O[nt], 0, 0, 0);
+    }
     }
   }
 
@@ -891,15 +1038,15 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV>
 // with ||r_t|| the stored ||k|| ||r^||.  One workgroup per (split, KV head),
 // the same tiles and block stream as decode (no value segment);
 // out[(s*G + g) * T + t].  fu = sqrt(pi/2)/m rides on the sign fragments.
-template <int G, int KB, int NK>
-__global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>())) void logits_mfma_kernel(
+template <int G, int KB, int NK, bool MX = false>
+__global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0, MX>, MX>())) void logits_mfma_kernel(
     const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck,
     int64_t T, int64_t TpK, int split_len, const uint32_t* __restrict__ kcodes,
     const uint32_t* __restrict__ ksigns, const void* knorm, const void* krnorm, float fu,
-    float* __restrict__ out) {
-  using P = Packet<KB, 0, NK, 0>;
+    float* __restrict__ out, const float* __restrict__ ck_hi = nullptr) {
+  using P = Packet<KB, 0, NK, 0, MX>;
   constexpr int kSlot = 4 * P::kBytes;
-  __shared__ __align__(16) char lds[kTabBytes];
+  __shared__ __align__(16) char lds[tab_bytes<MX>()];
   __shared__ __align__(16) char ring[kRing * kSlot];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -914,13 +1061,15 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>(
   const int nbw = (nb_split > wave) ? (nb_split - wave + 3) / 4 : 0;
 
   BlockStream<P> st;
-  st.template init<KB, 0, NK, 0>(kcodes, ksigns, knorm, krnorm, nullptr, nullptr, s * TpK + t0 + 32 * wave, 0,
-                                 lane, lds_addr(ring) + wave * P::kBytes, kSlot);
+  st.template init<KB, 0, NK, 0, MX>(kcodes, ksigns, knorm, krnorm, nullptr, nullptr, s * TpK + t0 + 32 * wave, 0,
+                                     lane, lds_addr(ring) + wave * P::kBytes, kSlot);
 #pragma unroll
   for (int jj = 0; jj + 1 < kRing; ++jj)
     if (jj < nbw) st.issue(jj, jj, lane);
 
-  build_tables<KB, 0, false>(ck, nullptr, lds, tid, kDecThreads);
+  if constexpr (MX) build_tables_mix<KB, 0>(ck, ck_hi, nullptr, nullptr, lds, tid, kDecThreads);
+  else build_tables<KB, 0, false>(ck, nullptr, lds, tid, kDecThreads);
+  const char* ktab = lds + ((MX && g4 >= 2) ? kNarrowKeyOff : 0);
   half8 bq[8], bu[4];
   query_frags<G, false>(qr, u, s, lane, 1.f, fu, bq, bu);
   __syncthreads();
@@ -928,7 +1077,8 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>(
   float* out_h = out + (s * G + (n < G ? n : 0)) * T;
   const bool vec_ok = (Ti & 3) == 0;                  // 16-byte aligned output rows
   // this lane's byte offsets within a packet: key words, sign word, norms
-  const uint32_t koff = P::kKC + key_lane_off<KB>(n, g4), soff = P::kSG + 16 * n + 4 * g4;
+  const uint32_t koff = P::kKC + (MX ? mix_key_lane_off<KB>(n, g4) : key_lane_off<KB>(n, g4));
+  const uint32_t soff = P::kSG + 16 * n + 4 * g4;
   const uint32_t nkoff = 8 * NK * g4;
   int slot = 0;
   for (int j = 0; j < nbw; ++j) {
@@ -942,10 +1092,20 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0>>(
     float lv[8];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      uint32_t kw[KB], sw;
-      ring_key_words<KB>(kb, sb, tile, kw, sw);
       float cen[4], qj[4];
-      tile_logits<G, KB, false>(kw, sw, bq, bu, lds, cen, qj);
+      if constexpr (MX) {
+        uint32_t kw[KB + 1];
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(kb + 16 * (4 * KB + 2) * tile);
+#pragma unroll
+        for (int q = 0; q <= KB; ++q) kw[q] = kp[q];
+        if (g4 >= 2) kw[KB] = 0u;
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + 256 * tile);
+        tile_logits<G, KB + 1, false, true>(kw, sw, bq, bu, lds, cen, qj, ktab);
+      } else {
+        uint32_t kw[KB], sw;
+        ring_key_words<KB>(kb, sb, tile, kw, sw);
+        tile_logits<G, KB, false>(kw, sw, bq, bu, lds, cen, qj);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         lv[4 * tile + i] = fmaf(norm_at<NK>(nkb + P::kNK, 4 * tile + i), cen[i],
@@ -996,12 +1156,30 @@ static void launch_vb(int vb, dim3 grid, hipStream_t stream, const tq_tables& tk
   }
 }
 
+// split streams (validated: both split, bits 2 or 3 each, float16 norms)
+template <int G, int KB, int VB>
+static void launch_mix(dim3 grid, hipStream_t stream, const tq_tables& tk, const tq_tables& tv,
+                       const float* qr, const float* u, const tq_packed& k, const tq_packed& v, int len,
+                       float fq, float fu, int nsplit, float* partials) {
+  hipLaunchKernelGGL((decode_mfma_kernel<G, KB, VB, 2, 2, true>), grid, dim3(kDecThreads), 0, stream, qr, u,
+                     tk.centroids, tv.centroids, k.T, stream_stride(k), stream_stride(v), len, k.codes,
+                     k.signs, k.norm, k.rnorm, v.codes, v.norm, fq, fu, nsplit, partials, tk.centroids_hi,
+                     tv.centroids_hi);
+}
+
 template <int G>
 static hipError_t launch_g(const tq_tables& tk, const tq_tables& tv, const float* qr,
                            const float* u, int64_t nseq, const tq_packed& k, const tq_packed& v,
                            float fq, float fu, float* partials, int len, int nsplit,
                            hipStream_t stream) {
   dim3 grid(static_cast<unsigned>(nsplit), static_cast<unsigned>(nseq));
+  if (tk.hi_coords != 0) {
+    if (tk.bits == 2 && tv.bits == 2) launch_mix<G, 2, 2>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials);
+    else if (tk.bits == 2) launch_mix<G, 2, 3>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials);
+    else if (tv.bits == 2) launch_mix<G, 3, 2>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials);
+    else launch_mix<G, 3, 3>(grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials);
+    return hipGetLastError();
+  }
   switch (tk.bits) {
     case 1: launch_vb<G, 1>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
     case 2: launch_vb<G, 2>(tv.bits, grid, stream, tk, tv, qr, u, k, v, len, fq, fu, nsplit, partials); break;
@@ -1028,6 +1206,17 @@ static hipError_t launch_logits_g(const tq_tables& tk, const float* qr, const fl
                          u, tk.centroids, k.T, stream_stride(k), len, k.codes, k.signs, k.norm,    \
                          k.rnorm, fu, out);                                                        \
   } while (0)
+  if (tk.hi_coords != 0) {   // split keys (validated: bits 2 or 3)
+#define TQ_LOGM(KBV, NKV)                                                                          \
+  hipLaunchKernelGGL((logits_mfma_kernel<G, KBV, NKV, true>), grid, dim3(kDecThreads), 0, stream, qr, u, \
+                     tk.centroids, k.T, stream_stride(k), len, k.codes, k.signs, k.norm, k.rnorm, fu, out,  \
+                     tk.centroids_hi)
+    const bool f16 = k.norm_dtype == TQ_F16;
+    if (tk.bits == 2) { if (f16) TQ_LOGM(2, 2); else TQ_LOGM(2, 4); }
+    else { if (f16) TQ_LOGM(3, 2); else TQ_LOGM(3, 4); }
+#undef TQ_LOGM
+    return hipGetLastError();
+  }
   switch (tk.bits) {
     case 1: TQ_LOG(1); break;
     case 2: TQ_LOG(2); break;

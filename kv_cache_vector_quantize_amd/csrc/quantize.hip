@@ -29,6 +29,8 @@
 //    row per token; the sketch has three products (hi*hi, hi*lo, lo*hi).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -274,17 +276,27 @@ __device__ __forceinline__ float sumsq16(const RawX<XT>& r, const float* xv) {
   return ss;
 }
 
+template <int W>
+using Width = std::integral_constant<int, W>;
+
 // APPEND: the stream already holds tokens below pos (a separate instance, so
 // that the whole-stream launches carry none of the merge code).  HAD: Pi is
 // a randomized Walsh-Hadamard rotation, whose sqrt(d) Pi has entries +-1:
 // one fp16 product rotates exactly, where a general Pi needs hi + lo.
-template <typename XT, bool KEY, int BITS, bool APPEND, bool HAD>
+// MIX: a split (fractional-width) stream -- coordinates 0..63, the words of
+// waves 0 and 1, take BITS + 1 bits from the second codebook (cent_hi,
+// bnd_hi), coordinates 64..127 BITS bits; each word (keys) or coordinate
+// (values) keeps its own width in the records.
+template <typename XT, bool KEY, int BITS, bool APPEND, bool HAD, bool MIX = false>
 __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     const float* __restrict__ rot, const float* __restrict__ sketch,
     const float* __restrict__ cent, const float* __restrict__ bnd, const XT* __restrict__ x,
     int64_t nseq, int64_t pos_arg, int64_t T, int64_t Tp, uint32_t* __restrict__ codes,
     uint32_t* __restrict__ signs,
-    void* __restrict__ norm, void* __restrict__ rnorm, int norm_dtype) {
+    void* __restrict__ norm, void* __restrict__ rnorm, int norm_dtype,
+    const float* __restrict__ cent_hi = nullptr, const float* __restrict__ bnd_hi = nullptr) {
+  static_assert(!MIX || BITS + 1 <= 4, "split streams widen BITS by one, up to 4");
+  constexpr int BW = MIX ? BITS + 1 : BITS;   // width of the leading coordinates
   constexpr bool kSplitX = sizeof(XT) == 4;  // fp32 input: stage hi and lo
   constexpr int kXP = kSplitX ? 2 : 1;
   // keys: one staging buffer (the sketch barrier separates its reads from the
@@ -306,6 +318,19 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
 #pragma unroll
   for (int i = 0; i + 1 < kHalf; ++i) tab.tpos[i] = bnd[kHalf + i] * kResScale;
   if constexpr (BITS == 1) tab.tpos[0] = 0.f;
+  QTab<BW> tabw;   // the leading coordinates' table (MIX only)
+  if constexpr (MIX) {
+    constexpr int kHalfW = (1 << BW) / 2;
+#pragma unroll
+    for (int i = 0; i < kHalfW; ++i) tabw.cpos[i] = cent_hi[kHalfW + i] * kResScale;
+#pragma unroll
+    for (int i = 0; i + 1 < kHalfW; ++i) tabw.tpos[i] = bnd_hi[kHalfW + i] * kResScale;
+  }
+  // record words per token (keys) / per block (values), and where this
+  // wave's word (keys) or coordinate c32 (values) starts in the record
+  constexpr int kKeyRec = MIX ? 4 * BITS + 2 : 4 * BITS;
+  constexpr int kValRec = MIX ? kD * BITS + kD / 2 : kD * BITS;
+  const bool wide = MIX && wave < 2;
 
   // 32x32 tile row / column c32 <-> token or coordinate atok: output register
   // v of lane half h is tile row 8(v/4) + 4h + v%4, and atok of that row is
@@ -497,9 +522,11 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       // of token c32.  Descending v appends each plane bit below the ones
       // before it, so after 16 steps coordinate 16h + v sits at bit v.
       const float rt = rinv_s[par][c32];
-      uint32_t pw[BITS];   // code planes, inverted, coordinates 16h .. 16h+15
+      auto quantize_key_word = [&](auto wc, const auto& tb) {
+      constexpr int WB = decltype(wc)::value;
+      uint32_t pw[WB];   // code planes, inverted, coordinates 16h .. 16h+15
 #pragma unroll
-      for (int p = 0; p < BITS; ++p) pw[p] = 0u;
+      for (int p = 0; p < WB; ++p) pw[p] = 0u;
       uint32_t hw[8], lw[8];   // residual (x256) as fp16 hi / lo pairs of coordinates (2i, 2i+1)
       float rr = 0.f;          // sum of the residual squares (x256^2)
       float rodd = 0.f;
@@ -507,7 +534,7 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       for (int v = 15; v >= 0; --v) {
         const float y = acc[v] * rt;
         float C;
-        quant_append<BITS>(y, tab, pw, C);
+        quant_append<WB>(y, tb, pw, C);
         // residual x256 (for a zero vector y = 0 and the residual is unused:
         // its signs and rnorm are fixed at the store)
         float r = y - C;
@@ -535,9 +562,9 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
       }
       // code words of token c32: lane half 0 takes half 1's 16 bits on top
-      uint32_t cw[BITS];
+      uint32_t cw[WB];
 #pragma unroll
-      for (int p = 0; p < BITS; ++p) {
+      for (int p = 0; p < WB; ++p) {
         const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(pw[p]), 32, 64));
         cw[p] = ~((pw[p] & 0xFFFFu) | (o << 16));
       }
@@ -546,11 +573,16 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       if (h == 0) {
         rho_s[par][wave][c32] = rr32;
         if (c32 >= lo) {  // padding tokens get the zero-vector encoding
-          uint32_t* dst = codes + ((s * Tp + t0 + c32) * 4 + wave) * BITS;
+          // this wave's word: after the planes of the words before it
+          const int woff = wave * BITS + (MIX ? (wave < 2 ? wave : 2) : 0);
+          uint32_t* dst = codes + (s * Tp + t0 + c32) * kKeyRec + woff;
 #pragma unroll
-          for (int p = 0; p < BITS; ++p) dst[p] = cw[p];
+          for (int p = 0; p < WB; ++p) dst[p] = cw[p];
         }
       }
+      };
+      if (wide) quantize_key_word(Width<BW>{}, tabw);
+      else quantize_key_word(Width<BITS>{}, tab);
       __syncthreads();
       // ---------------- sketch Z^T = S R^T: z[v] is sketch row 32*wave + 16h + v
       // of token c32
@@ -590,43 +622,48 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         rv[4 * q + 2] = r4.z;
         rv[4 * q + 3] = r4.w;
       }
-      uint32_t vlo = 0, vhi = 0;  // value fields of tokens 16h .. 16h+15 (bits BITS*v ..)
+      // the record of coordinate j = 32*wave + c32: WB words, after the
+      // records of the coordinates before it
+      auto quantize_value_coord = [&](auto wc, const auto& tb) {
+      constexpr int WB = decltype(wc)::value;
+      uint32_t vlo = 0, vhi = 0;  // value fields of tokens 16h .. 16h+15 (bits WB*v ..)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float y = acc[v] * rv[v];
-        const int sh = BITS * v;
-        const uint32_t u = static_cast<uint32_t>(value_index<BITS>(y, tab));
+        const int sh = WB * v;
+        const uint32_t u = static_cast<uint32_t>(value_index<WB>(y, tb));
         if (sh < 32) vlo |= u << sh;
-        if (sh + BITS > 32) vhi |= (sh < 32) ? (u >> (32 - sh)) : (u << (sh - 32));
+        if (sh + WB > 32) vhi |= (sh < 32) ? (u >> (32 - sh)) : (u << (sh - 32));
       }
       // mask off the fields of padded tokens (zero vectors past the end of T)
       const int nv = nvalid - 16 * h;  // valid tokens of this lane half
       if (nv < 16) {
-        const int nbits = nv > 0 ? BITS * nv : 0;
+        const int nbits = nv > 0 ? WB * nv : 0;
         const uint32_t mlo = nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u);
         const uint32_t mhi = nbits <= 32 ? 0u : ((1u << (nbits - 32)) - 1u);
         vlo &= mlo;
         vhi &= mhi;
       }
-      // lane half h holds record bits [16*BITS*h, 16*BITS*(h+1))
+      // lane half h holds record bits [16*WB*h, 16*WB*(h+1))
       const int j = 32 * wave + c32;
-      uint32_t* dst = codes + ((s * (Tp / kUnit) + blk0 + blk) * kD + j) * BITS;
-      // record word q; its bits below BITS*lo belong to kept tokens and are
+      const int joff = MIX ? (j < kD / 2 ? j * BW : (kD / 2) * BW + (j - kD / 2) * BITS) : j * BITS;
+      uint32_t* dst = codes + (s * (Tp / kUnit) + blk0 + blk) * kValRec + joff;
+      // record word q; its bits below WB*lo belong to kept tokens and are
       // merged from the stored record (only in a block that an append resumes)
       auto put = [&](int q, uint32_t w) {
-        const int kb = BITS * lo - 32 * q;
+        const int kb = WB * lo - 32 * q;
         if (kb > 0) {
           const uint32_t keep = kb >= 32 ? 0xFFFFFFFFu : (1u << kb) - 1u;
           w = (dst[q] & keep) | (w & ~keep);
         }
         dst[q] = w;
       };
-      if constexpr (BITS == 1) {
+      if constexpr (WB == 1) {
         const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
         if (h == 0) put(0, vlo | (other << 16));
-      } else if constexpr (BITS == 2) {
+      } else if constexpr (WB == 2) {
         put(h, vlo);
-      } else if constexpr (BITS == 3) {
+      } else if constexpr (WB == 3) {
         const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
         if (h == 0) {
           put(0, vlo);
@@ -638,6 +675,9 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         put(2 * h, vlo);
         put(2 * h + 1, vhi);
       }
+      };
+      if (wide) quantize_value_coord(Width<BW>{}, tabw);
+      else quantize_value_coord(Width<BITS>{}, tab);
       if (tid >= lo && tid < kUnit) store_norm(norm, norm_dtype, s * Tp + t0 + tid, n_s[par][tid]);
     }
     if constexpr (KEY) {
@@ -1013,16 +1053,26 @@ static int device_cus() {
 template <typename XT, bool KEY, bool APPEND, bool HAD>
 static void launch_bits(dim3 grid, hipStream_t stream, const tq_tables& t, const void* x,
                         const tq_packed& out, int64_t pos, int64_t n) {
-#define TQ_QL(B)                                                                                    \
-  hipLaunchKernelGGL((quantize_mfma_kernel<XT, KEY, B, APPEND, HAD>), grid, dim3(kQThreads), 0, stream, t.rot,  \
-                     t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), out.nseq, pos,    \
+#define TQ_QL(B, MX)                                                                                \
+  hipLaunchKernelGGL((quantize_mfma_kernel<XT, KEY, B, APPEND, HAD, MX>), grid, dim3(kQThreads), 0, stream,  \
+                     t.rot, t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), out.nseq, pos, \
                      pos + n, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,       \
-                     out.norm_dtype)
+                     out.norm_dtype, t.centroids_hi, t.bounds_hi)
+  if (t.hi_coords != 0) {   // split stream (validated: d/2 leading coordinates, bits 1..3)
+    if constexpr (!HAD) {
+      switch (t.bits) {
+        case 1: TQ_QL(1, true); break;
+        case 2: TQ_QL(2, true); break;
+        default: TQ_QL(3, true); break;
+      }
+    }
+    return;
+  }
   switch (t.bits) {
-    case 1: TQ_QL(1); break;
-    case 2: TQ_QL(2); break;
-    case 3: TQ_QL(3); break;
-    default: TQ_QL(4); break;
+    case 1: TQ_QL(1, false); break;
+    case 2: TQ_QL(2, false); break;
+    case 3: TQ_QL(3, false); break;
+    default: TQ_QL(4, false); break;
   }
 #undef TQ_QL
 }
@@ -1062,7 +1112,7 @@ hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const
   const int64_t nblk = (pos + n + kUnit - 1) / kUnit - pos / kUnit;
   const int64_t units = out.nseq * nblk;
   if (units == 0) return hipSuccess;
-  if (!append && out.role == TQ_KEY && units < (static_cast<int64_t>(1) << 31)) {
+  if (!append && out.role == TQ_KEY && t.hi_coords == 0 && units < (static_cast<int64_t>(1) << 31)) {
     // whole key streams: the software-pipelined kernel (2 workgroups per CU)
     const int64_t cap = 2 * static_cast<int64_t>(device_cus());
     const unsigned grid = static_cast<unsigned>(units < cap ? units : cap);

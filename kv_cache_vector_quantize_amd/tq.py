@@ -32,7 +32,8 @@ class Tables(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("m", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("rot_kind", ctypes.c_int32), ("rot", ctypes.c_void_p),
                 ("sketch", ctypes.c_void_p), ("centroids", ctypes.c_void_p),
-                ("bounds", ctypes.c_void_p)]
+                ("bounds", ctypes.c_void_p), ("hi_coords", ctypes.c_int32),
+                ("centroids_hi", ctypes.c_void_p), ("bounds_hi", ctypes.c_void_p)]
 
 
 class Packed(ctypes.Structure):
@@ -40,7 +41,8 @@ class Packed(ctypes.Structure):
                 ("m", ctypes.c_int32), ("nseq", ctypes.c_int64), ("T", ctypes.c_int64),
                 ("codes", ctypes.c_void_p), ("signs", ctypes.c_void_p),
                 ("norm", ctypes.c_void_p), ("rnorm", ctypes.c_void_p),
-                ("norm_dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+                ("norm_dtype", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("hi_coords", ctypes.c_int32)]
 
 
 _lib = None
@@ -164,18 +166,28 @@ class StreamTables:
     centroids: torch.Tensor
     bounds: torch.Tensor
     rot_kind: int = TQ_ROT_DENSE
+    hi_coords: int = 0
+    centroids_hi: Optional[torch.Tensor] = None
+    bounds_hi: Optional[torch.Tensor] = None
 
     def c_struct(self):
         return Tables(self.d, self.m, self.bits, self.rot_kind, self.rot.data_ptr(),
                       None if self.sketch is None else self.sketch.data_ptr(),
-                      self.centroids.data_ptr(), self.bounds.data_ptr())
+                      self.centroids.data_ptr(), self.bounds.data_ptr(), self.hi_coords,
+                      _dp(self.centroids_hi), _dp(self.bounds_hi))
+
+    def coord_bits(self):
+        """Bits of every coordinate (bits + 1 for the leading hi_coords)."""
+        return [self.bits + 1 if j < self.hi_coords else self.bits for j in range(self.d)]
 
 
-def make_tables(G, S, bits, device="cuda", hadamard_signs=None):
+def make_tables(G, S, bits, device="cuda", hadamard_signs=None, hi_coords=0):
     """Rotation from the Gaussian G (numpy/torch float64 [d, d]) -- or, given
     hadamard_signs (d values +-1), the randomized Walsh-Hadamard rotation
     from them (G is then unused) -- sketch S (float64 [m, d] or None) and the
-    Lloyd-Max codebook, all built on the device by the library."""
+    Lloyd-Max codebook, all built on the device by the library.  hi_coords
+    > 0 makes a split (fractional-width) stream: the leading hi_coords
+    rotated coordinates take the (bits+1)-bit codebook, built here too."""
     if hadamard_signs is not None:
         sg = torch.as_tensor(hadamard_signs, dtype=torch.float32).to(device)
         rot32, kind = tq_hadamard_rotation(sg), TQ_ROT_HADAMARD
@@ -186,7 +198,12 @@ def make_tables(G, S, bits, device="cuda", hadamard_signs=None):
     sk = None if S is None else torch.as_tensor(S, dtype=torch.float64).to(device).float().contiguous()
     _, _, c32, b32 = tq_codebook(d, bits, device)
     b32 = b32.clone() if b32.numel() else torch.zeros(1, dtype=torch.float32, device=device)
-    return StreamTables(d, 0 if sk is None else sk.shape[0], bits, rot32, sk, c32, b32, kind)
+    ch, bh = None, None
+    if hi_coords:
+        _, _, ch, bh = tq_codebook(d, bits + 1, device)
+        bh = bh.clone()
+    return StreamTables(d, 0 if sk is None else sk.shape[0], bits, rot32, sk, c32, b32, kind,
+                        hi_coords, ch, bh)
 
 
 @dataclass
@@ -207,6 +224,7 @@ class PackedStream:
     buf_rnorm: Optional[torch.Tensor]
     norm_dtype: int
     capacity: int = 0
+    hi_coords: int = 0
 
     @property
     def Tp(self):
@@ -231,7 +249,7 @@ class PackedStream:
     def c_struct(self):
         return Packed(self.role, self.bits, self.d, self.m, self.nseq, self.T,
                       self.buf_codes.data_ptr(), _dp(self.buf_signs), self.buf_norm.data_ptr(),
-                      _dp(self.buf_rnorm), self.norm_dtype, self.capacity)
+                      _dp(self.buf_rnorm), self.norm_dtype, self.capacity, self.hi_coords)
 
 
 def padded_tokens(T):
@@ -253,16 +271,23 @@ def alloc_packed(role, tables, nseq, T, norm_dtype="f16", device="cuda", capacit
     if capacity and (capacity % 32 or capacity < T):
         raise ValueError(f"capacity {capacity} must be a multiple of 32 and >= T = {T}")
     Tp = capacity if capacity else padded_tokens(T)
+    hi = tables.hi_coords
     if role == TQ_KEY:
-        codes = torch.zeros((nseq, Tp, d // 32, bits), dtype=torch.int32, device=device)
+        if hi:   # split stream: one record of (d/32) bits + hi/32 words per token
+            codes = torch.zeros((nseq, Tp, (d // 32) * bits + hi // 32), dtype=torch.int32, device=device)
+        else:
+            codes = torch.zeros((nseq, Tp, d // 32, bits), dtype=torch.int32, device=device)
         signs = torch.zeros((nseq, Tp, m // 32), dtype=torch.int32, device=device)
         rnorm = torch.zeros((nseq, Tp), dtype=tdt, device=device)
     else:
-        codes = torch.zeros((nseq, Tp // 32, d, bits), dtype=torch.int32, device=device)
+        if hi:   # split stream: one record of d bits + hi words per block
+            codes = torch.zeros((nseq, Tp // 32, d * bits + hi), dtype=torch.int32, device=device)
+        else:
+            codes = torch.zeros((nseq, Tp // 32, d, bits), dtype=torch.int32, device=device)
         signs, rnorm = None, None
     norm = torch.zeros((nseq, Tp), dtype=tdt, device=device)
     return PackedStream(role, bits, d, m if role == TQ_KEY else 0, nseq, T, codes, signs, norm,
-                        rnorm, nd, capacity)
+                        rnorm, nd, capacity, hi)
 
 
 # ------------------------------------------------------------ hot-path calls

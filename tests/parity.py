@@ -94,7 +94,10 @@ def check_value_stream(X, idx_gpu, norm_gpu, Pi, c, t, norm_dtype):
 def _check_codes(ref, idx_gpu, t):
     diff = idx_gpu != ref["idx"]
     dist = np.full(ref["yhat"].shape, np.inf)
-    for ti in np.asarray(t, dtype=np.float64):       # distance to the nearest boundary
+    t = np.asarray(t, dtype=np.float64)
+    # distance to the nearest boundary (t: one codebook's boundaries, or one
+    # row per coordinate for a split width, padded with +inf)
+    for ti in (t if t.ndim == 1 else t.T):
         dist = np.minimum(dist, np.abs(ref["yhat"] - ti))
     inband = dist <= BAND
     neighbour = np.abs(idx_gpu - ref["idx"]) <= 1

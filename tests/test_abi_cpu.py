@@ -33,7 +33,7 @@ def test_exports_every_declared_function(L):
     assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
-    assert L.tq_abi_version() == 4
+    assert L.tq_abi_version() == 5
 
 
 def test_status_strings(L):
@@ -66,14 +66,15 @@ needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                                   reason="fake device pointers are only used without a GPU")
 
 
-def _tables(tq, d=128, m=128, bits=2, rot_kind=0, sketch=True):
-    return tq.Tables(d, m, bits, rot_kind, FAKE, FAKE if sketch else None, FAKE, FAKE)
+def _tables(tq, d=128, m=128, bits=2, rot_kind=0, sketch=True, hi=0):
+    return tq.Tables(d, m, bits, rot_kind, FAKE, FAKE if sketch else None, FAKE, FAKE, hi,
+                     FAKE if hi else None, FAKE if hi else None)
 
 
-def _packed(tq, role=0, bits=2, d=128, m=128, nseq=1, T=4, nd=2, cap=0):
+def _packed(tq, role=0, bits=2, d=128, m=128, nseq=1, T=4, nd=2, cap=0, hi=0):
     key = role == 0
     return tq.Packed(role, bits, d, m, nseq, T, FAKE, FAKE if key else None, FAKE,
-                     FAKE if key else None, nd, cap)
+                     FAKE if key else None, nd, cap, hi)
 
 
 @needs_no_gpu
@@ -226,3 +227,42 @@ def test_static_decode_rejects_shapes_beyond_its_array(L):
     assert L.tq_attn_decode_static(by(tk), by(tv), vp(FAKE), 1, 1, 30, 8, by(_packed(tq, nseq=8, T=64)),
                                    by(_packed(tq, role=1, m=0, bits=3, nseq=8, T=64)), 0.088,
                                    vp(FAKE), None) == -1
+
+
+@needs_no_gpu
+def test_split_width_validation(L):
+    """Fractional widths: hi_coords 0 or d/2 (others unsupported or invalid),
+    the second codebook present exactly for split tables, packed and tables
+    agreeing, bits + 1 <= 4, dense rotation for quantize; logits take split
+    keys of 2 or 3 bits, decode needs both streams split with float16 norms."""
+    from kv_cache_vector_quantize_amd import tq
+    by, vp = ctypes.byref, ctypes.c_void_p
+    x = vp(FAKE)
+    q = lambda t, p: L.tq_quantize(by(t), x, 1, by(p), None)
+    # hi_coords not a multiple of 32, or past d: invalid; 32 / 96: unsupported
+    for hi, want in ((16, -1), (160, -1), (32, -2), (96, -2)):
+        assert q(_tables(tq, hi=hi), _packed(tq, hi=hi)) == want, hi
+    # split tables need the second codebook; uniform ones must not carry it
+    t = tq.Tables(128, 128, 2, 0, FAKE, FAKE, FAKE, FAKE, 64, None, None)
+    assert q(t, _packed(tq, hi=64)) == -1
+    t = tq.Tables(128, 128, 2, 0, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None)
+    assert q(t, _packed(tq)) == -1
+    # bits + 1 must stay <= 4
+    assert q(_tables(tq, bits=4, hi=64), _packed(tq, bits=4, hi=64)) == -1
+    # packed and tables disagree
+    assert q(_tables(tq, hi=64), _packed(tq, hi=0)) == -1
+    # Walsh-Hadamard rotation with a split: unsupported
+    assert q(_tables(tq, hi=64, rot_kind=1), _packed(tq, hi=64)) == -2
+    # logits: split 1-bit keys unsupported
+    tk1 = _tables(tq, bits=1, hi=64)
+    assert L.tq_attn_logits(by(tk1), x, 1, 1, 4, 1, by(_packed(tq, bits=1, hi=64)), vp(FAKE), vp(FAKE),
+                            1 << 20, None) == -2
+    # decode: one stream split, the other not -> unsupported; f32 norms -> unsupported
+    tk, tv = _tables(tq, hi=64), _tables(tq, m=0, sketch=False, bits=3)
+    pk, pv = _packed(tq, nseq=8, T=64, hi=64), _packed(tq, role=1, m=0, bits=3, nseq=8, T=64)
+    args = lambda tv_, pk_, pv_: (by(tk), by(tv_), x, 1, 1, 32, 8, by(pk_), by(pv_), 0.1, vp(FAKE),
+                                  vp(FAKE), 1 << 30, None)
+    assert L.tq_attn_decode(*args(tv, pk, pv)) == -2
+    tvs = _tables(tq, m=0, sketch=False, bits=3, hi=64)
+    pvs32 = _packed(tq, role=1, m=0, bits=3, nseq=8, T=64, nd=0, hi=64)
+    assert L.tq_attn_decode(*args(tvs, pk, pvs32)) == -2

@@ -1,0 +1,161 @@
+"""GPU parity of split (fractional-width) streams: the leading half of the
+rotated coordinates at bits + 1, the rest at bits -- 1.5, 2.5 and 3.5 bits
+per coordinate -- against the oracle's split codebook (quantize every
+vector, appends against a bulk quantize, logits from the GPU's records,
+decode from the GPU's records)."""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_vector_quantize_amd import inputs, tq
+
+from gpu_common import say, to64
+from parity import check_key_stream, check_value_stream, decode_close, logits_close
+
+pytestmark = pytest.mark.gpu
+D = M = 128
+HI = D // 2
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_split(m, bits):
+    G, S = inputs.table_gaussians(D, M)
+    Pi = oracle.rotation_from_gaussian(G)
+    C, B = oracle.split_codebook(D, HI, oracle.lloyd_max(D, bits), oracle.lloyd_max(D, bits + 1))
+    return Pi, (S if m else None), C, B
+
+
+_tabs = {}
+
+
+def split_tables(m, bits):
+    if (m, bits) not in _tabs:
+        G, S = inputs.table_gaussians(D, M)
+        _tabs[(m, bits)] = tq.make_tables(G, S if m else None, bits, hi_coords=HI)
+    return _tabs[(m, bits)]
+
+
+def _keys(X, bits, nd, capacity=0):
+    t = split_tables(M, bits)
+    p = tq.alloc_packed(tq.TQ_KEY, t, X.shape[0], X.shape[1], nd, capacity=capacity)
+    tq.tq_quantize(t, X, p)
+    return t, p
+
+
+def _values(X, bits, nd):
+    t = split_tables(0, bits)
+    p = tq.alloc_packed(tq.TQ_VALUE, t, X.shape[0], X.shape[1], nd)
+    tq.tq_quantize(t, X, p)
+    return t, p
+
+
+def key_records(p, bits):
+    wb = oracle.split_widths(D, bits, HI)[::32]
+    idx = oracle.unpack_key_codes_split(p.codes.cpu().numpy().view(np.uint32), D, wb)
+    sg = oracle.unpack_signs(p.signs.cpu().numpy().view(np.uint32), M)
+    return idx, sg, p.norm.cpu().numpy(), p.rnorm.cpu().numpy()
+
+
+def value_records(p, bits):
+    cb = oracle.split_widths(D, bits, HI)
+    idx = oracle.unpack_value_codes_split(p.codes.cpu().numpy().view(np.uint32), p.T, cb)
+    return idx, p.norm.cpu().numpy()
+
+
+@pytest.mark.parametrize("bits,dtype,nd", [(1, torch.bfloat16, "f16"), (2, torch.bfloat16, "f16"),
+                                           (3, torch.bfloat16, "f16"), (3, torch.float32, "f32")])
+def test_split_keys_and_values_quantize(bits, dtype, nd):
+    say("split quantize", bits, dtype, nd)
+    w = inputs.WORKLOADS[2]
+    X = inputs.key_slice(w, 0, 1, device="cuda", T=3 * 347).reshape(3, 347, D).to(dtype).contiguous()
+    X[1, 5] = 0.0                                               # a zero vector
+    _, pk = _keys(X, bits, nd)
+    Pi, S, C, B = oracle_split(M, bits)
+    idx, sg, n, rn = key_records(pk, bits)
+    rep = check_key_stream(to64(X).reshape(-1, D), idx.reshape(-1, D), sg.reshape(-1, M), n.reshape(-1),
+                           rn.reshape(-1), Pi, S, C, B, nd)
+    assert rep["ok"], rep
+    # the wide half really uses its extra levels
+    assert idx[..., :HI].max() == (1 << (bits + 1)) - 1 and idx[..., HI:].max() == (1 << bits) - 1
+    # zero vector and padding tokens: idx = 2^(width-1) per coordinate, signs all set
+    zero_idx = np.where(np.arange(D) < HI, 1 << bits, 1 << (bits - 1))
+    assert np.array_equal(idx[1, 5], zero_idx) and sg[1, 5].all()
+    pad = oracle.unpack_key_codes_split(pk.buf_codes[:, 347:].cpu().numpy().view(np.uint32), D,
+                                        oracle.split_widths(D, bits, HI)[::32])
+    assert np.all(pad == zero_idx)
+    _, pv = _values(X, bits, nd)
+    Piv, _, Cv, Bv = oracle_split(0, bits)
+    vidx, vn = value_records(pv, bits)
+    rep = check_value_stream(to64(X).reshape(-1, D), vidx.reshape(-1, D), vn.reshape(-1), Piv, Cv, Bv, nd)
+    assert rep["ok"], rep
+    # fields of the padding tokens of each last block are zero
+    full = oracle.unpack_value_codes_split(pv.codes.cpu().numpy().view(np.uint32), pv.Tp,
+                                           oracle.split_widths(D, bits, HI))
+    assert np.all(full[:, 347:] == 0)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_split_appends_equal_bulk_quantize(bits):
+    say("split appends", bits)
+    g = torch.Generator().manual_seed(31)
+    X = torch.randn((2, 200, D), generator=g).to(torch.bfloat16).cuda().contiguous()
+    for role in (tq.TQ_KEY, tq.TQ_VALUE):
+        t = split_tables(M if role == tq.TQ_KEY else 0, bits)
+        bulk = tq.alloc_packed(role, t, 2, 200, "f16", capacity=224)
+        tq.tq_quantize(t, X, bulk)
+        app = tq.alloc_packed(role, t, 2, 0, "f16", capacity=224)
+        for a, b in ((0, 1), (1, 31), (31, 70), (70, 200)):
+            tq.tq_append(t, X[:, a:b].contiguous(), app)
+        assert app.T == 200
+        torch.cuda.synchronize()
+        assert torch.equal(app.buf_codes, bulk.buf_codes)
+        assert torch.equal(app.buf_norm, bulk.buf_norm)
+        if role == tq.TQ_KEY:
+            assert torch.equal(app.buf_signs, bulk.buf_signs) and torch.equal(app.buf_rnorm, bulk.buf_rnorm)
+
+
+@pytest.mark.parametrize("bits,G,T,nd", [(2, 4, 777, "f16"), (3, 8, 2049, "f32"), (3, 1, 100, "f16")])
+def test_split_logits(bits, G, T, nd):
+    say("split logits", bits, G, T, nd)
+    B, Hkv = 1, 2
+    Hq = G * Hkv
+    X = (torch.randn((B * Hkv, T, D), device="cuda") * 2).to(torch.bfloat16).contiguous()
+    tk, pk = _keys(X, bits, nd)
+    q = torch.randn((B, Hq, D), device="cuda")
+    got = tq.tq_attn_logits(tk, q, pk, B, Hq, Hkv).cpu().numpy()
+    Pi, S, C, _ = oracle_split(M, bits)
+    idx, sg, n, rn = key_records(pk, bits)
+    qn = to64(q)
+    for h in range(Hq):
+        s = h // G
+        ref = oracle.key_logits(qn[0, h], idx[s], sg[s], n[s].astype(np.float64), rn[s].astype(np.float64),
+                                Pi, S, C)
+        ok, nbad, mx = logits_close(got[0, h], ref)
+        assert ok, (h, nbad, mx)
+
+
+@pytest.mark.parametrize("kbits,vbits,G,T", [(2, 3, 4, 1000), (3, 3, 8, 3000), (3, 2, 1, 77), (2, 2, 2, 9000)])
+def test_split_decode(kbits, vbits, G, T):
+    say("split decode", kbits, vbits, G, T)
+    B, Hkv = 2, 2
+    Hq = G * Hkv
+    g = torch.Generator().manual_seed(kbits * 10 + vbits)
+    K = (torch.randn((B * Hkv, T, D), generator=g) * 1.5).to(torch.bfloat16).cuda().contiguous()
+    V = torch.randn((B * Hkv, T, D), generator=g).to(torch.bfloat16).cuda().contiguous()
+    tk, pk = _keys(K, kbits, "f16")
+    tv, pv = _values(V, vbits, "f16")
+    q = torch.randn((B, Hq, D), generator=g).cuda()
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv).cpu().numpy()
+    Pi, S, Ck, _ = oracle_split(M, kbits)
+    _, _, Cv, _ = oracle_split(0, vbits)
+    kidx, ksg, kn, krn = key_records(pk, kbits)
+    vidx, vn = value_records(pv, vbits)
+    rs = lambda a: a.reshape(B, Hkv, *a.shape[1:])
+    f = lambda a: rs(a).astype(np.float64)
+    ref = oracle.decode(to64(q), rs(kidx), rs(ksg), f(kn), f(krn), rs(vidx), f(vn), Pi, S, Ck, Cv)
+    ok, rel = decode_close(got.reshape(-1, D), ref.reshape(-1, D))
+    assert ok, rel
