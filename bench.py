@@ -38,7 +38,7 @@ def _sha(path):
 def key_record_bytes(bits, d=128, m=128, norm_bytes=2, hi=0):
     """Bytes of one packed key: code planes (one more plane for the hi/32
     leading words of a split stream), sign words, two norms."""
-    return ((d // 32) * bits + hi // 32) * 4 + (m // 32) * 4 + 2 * norm_bytes
+    return (((d + 31) // 32) * bits + hi // 32) * 4 + ((m + 31) // 32) * 4 + 2 * norm_bytes
 
 
 def value_record_bytes(bits, d=128, norm_bytes=2, hi=0):

@@ -168,7 +168,8 @@ tq_status tq_codebook(int d, int bits, double *centroids64, double *bounds64,
  * Cites: a2a-mcp.org page, "How it works", Stage 1 (QR of a Gaussian matrix);
  * deepsignal-app.com page, QJL section (drawn once before inference, cached).
  * Setup helper; G is an input drawn by the caller (iid N(0,1)).
- *   d      2..128
+ *   d      2..1024 (up to 128 in LDS; past 128 in rot64, an L2-resident
+ *          working copy)
  *   G      in, d x d row-major doubles
  *   rot64  out, d x d row-major doubles (also used as working storage)
  *   rot32  out, d x d row-major floats (round to nearest), or NULL

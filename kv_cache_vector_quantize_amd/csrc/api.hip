@@ -11,8 +11,9 @@
 
 namespace {
 
-constexpr int kSupportedD = 128;
+constexpr int kSupportedD = 128;   // the matrix-core kernels
 constexpr int kSupportedM = 128;
+constexpr int kGenericMinD = 8, kGenericMax = 256;   // the vector-ALU kernels (generic.hip)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
@@ -27,8 +28,8 @@ size_t align256(size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); }
 tq_status check_tables(const tq_tables* t, bool key) {
   if (t == nullptr) return TQ_EINVAL;
   if (t->rot_kind != TQ_ROT_DENSE && t->rot_kind != TQ_ROT_HADAMARD) return TQ_EINVAL;
-  if (t->bits < 1 || t->bits > 4 || t->d <= 0 || t->d % 32 != 0) return TQ_EINVAL;
-  if (t->m < 0 || t->m % 32 != 0) return TQ_EINVAL;
+  if (t->bits < 1 || t->bits > 4 || t->d < 2) return TQ_EINVAL;
+  if (t->m < 0) return TQ_EINVAL;
   if (key ? t->m == 0 : t->m != 0) return TQ_EINVAL;
   if (!ok_ptr(t->rot) || !ok_ptr(t->centroids) || !ok_ptr(t->bounds)) return TQ_EINVAL;
   if (key ? !ok_ptr(t->sketch) : t->sketch != nullptr) return TQ_EINVAL;
@@ -39,13 +40,20 @@ tq_status check_tables(const tq_tables* t, bool key) {
   } else if (t->centroids_hi != nullptr || t->bounds_hi != nullptr) {
     return TQ_EINVAL;
   }
-  if (t->d != kSupportedD) return TQ_EUNSUPPORTED;
-  if (key && t->m != kSupportedM) return TQ_EUNSUPPORTED;
+  const bool mfma = t->d == kSupportedD && (key ? t->m == kSupportedM : true);
+  if (!mfma) {   // the generic kernels: any d and m up to 256, no split widths
+    if (t->d < kGenericMinD || t->d > kGenericMax || t->m > kGenericMax || t->hi_coords != 0)
+      return TQ_EUNSUPPORTED;
+  }
   if (t->hi_coords != 0 && t->hi_coords != t->d / 2) return TQ_EUNSUPPORTED;
   return TQ_OK;
 }
 
 bool split(const tq_tables* t) { return t->hi_coords != 0; }
+
+// head dimension / sketch size of the vector-ALU kernels (not the 128 of the
+// matrix-core ones)
+bool generic(const tq_tables* t) { return !(t->d == kSupportedD && (t->m == kSupportedM || t->m == 0)); }
 
 tq_status check_packed(const tq_packed* p, const tq_tables* t, int role) {
   if (p == nullptr) return TQ_EINVAL;
@@ -134,7 +142,7 @@ tq_status tq_codebook(int d, int bits, double* centroids64, double* bounds64, fl
 }
 
 tq_status tq_rotation(int d, const double* G, double* rot64, float* rot32, hipStream_t stream) {
-  if (d < 2 || d > 128 || !ok_ptr(G) || !ok_ptr(rot64) || !ok_opt(rot32)) return TQ_EINVAL;
+  if (d < 2 || d > 1024 || !ok_ptr(G) || !ok_ptr(rot64) || !ok_opt(rot32)) return TQ_EINVAL;
   return from_hip(tq::launch_rotation(d, G, rot64, rot32, stream));
 }
 
@@ -156,6 +164,7 @@ tq_status tq_quantize(const tq_tables* t, const void* x, int x_dtype, const tq_p
   if (split(t) && t->rot_kind != TQ_ROT_DENSE) return TQ_EUNSUPPORTED;
   if (out->nseq == 0 || out->T == 0) return TQ_OK;
   if (!ok_ptr(x)) return TQ_EINVAL;
+  if (generic(t)) return from_hip(tq::launch_quantize_generic(*t, x, x_dtype, *out, stream));
   return from_hip(tq::launch_quantize(*t, x, x_dtype, *out, 0, out->T, false, stream));
 }
 
@@ -170,6 +179,7 @@ tq_status tq_append(const tq_tables* t, const void* x, int x_dtype, int64_t n, c
   if (st != TQ_OK) return st;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
   if (split(t) && t->rot_kind != TQ_ROT_DENSE) return TQ_EUNSUPPORTED;
+  if (generic(t)) return TQ_EUNSUPPORTED;   // appends run on the d = 128 kernels
   // the new tokens must fit the stream's storage
   if (n < 0 || out->capacity == 0 || n > out->capacity - out->T) return TQ_EINVAL;
   if (out->nseq == 0 || n == 0) return TQ_OK;
@@ -204,6 +214,10 @@ tq_status tq_attn_logits(const tq_tables* tk, const void* q, int q_dtype, int B,
   float* qr = static_cast<float*>(ws);
   float* u = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                       align256(static_cast<size_t>(B) * Hq * tk->d * sizeof(float)));
+  if (generic(tk)) {
+    if (tq::launch_qprep_generic(*tk, q, q_dtype, B * Hq, qr, u, stream) != hipSuccess) return TQ_EHIP;
+    return from_hip(tq::launch_logits_generic(*tk, qr, u, B, Hq, Hkv, *k, logits, stream));
+  }
   hipError_t e = tq::launch_qprep(*tk, q, q_dtype, B * Hq, qr, u, stream);
   if (e != hipSuccess) return TQ_EHIP;
   if (Hq / Hkv <= 8)  // matrix-core tiles; 16 heads per KV head take the vector-ALU kernel
@@ -265,6 +279,7 @@ tq_status decode_args(const tq_tables* tk, const tq_tables* tv, const void* q, i
   if (k->T < 1 && B > 0) return TQ_EINVAL;
   if (k->nseq > 65535) return TQ_EUNSUPPORTED;  // one grid row per sequence
   if (k->T >= (static_cast<int64_t>(1) << 28)) return TQ_EUNSUPPORTED;  // 32-bit record offsets
+  if (generic(tk) || generic(tv)) return TQ_EUNSUPPORTED;   // decode runs at d = 128
   // split streams: both split, bits 2 or 3 each, float16 norms
   if (split(tk) || split(tv)) {
     if (!split(tk) || !split(tv) || tk->bits < 2 || tv->bits < 2 || k->norm_dtype != TQ_F16 ||

@@ -49,6 +49,15 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
 hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
                               int Hkv, const tq_packed& k, float* logits, hipStream_t stream);
 
+// Head dimensions other than 128 (d <= 256, m <= 256): vector-ALU quantize,
+// query preparation and logits (generic.hip).
+hipError_t launch_quantize_generic(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,
+                                   hipStream_t stream);
+hipError_t launch_qprep_generic(const tq_tables& tk, const void* q, int q_dtype, int nh, float* qr, float* u,
+                                hipStream_t stream);
+hipError_t launch_logits_generic(const tq_tables& tk, const float* qr, const float* u, int B, int Hq, int Hkv,
+                                 const tq_packed& k, float* logits, hipStream_t stream);
+
 // Top-k of each score row (k <= 32): chunk lists in ws, then one merge per row.
 int64_t topk_chunks(int64_t n);
 size_t topk_workspace(int64_t rows, int64_t n, int k);

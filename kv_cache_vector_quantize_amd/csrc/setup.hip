@@ -147,6 +147,7 @@ hipError_t launch_codebook(int d, int bits, double* c64, double* b64, float* c32
 
 constexpr int kRotMax = 128;
 constexpr int kRotThreads = 256;
+constexpr int kRotGMax = 1024;   // the global-memory factorization (d > kRotMax)
 
 __global__ __launch_bounds__(kRotThreads) void rotation_kernel(int d, const double* __restrict__ G,
                                                                double* __restrict__ Q,
@@ -204,8 +205,94 @@ __global__ __launch_bounds__(kRotThreads) void rotation_kernel(int d, const doub
   }
 }
 
+// The same factorization for head dimensions past what LDS holds: one
+// workgroup works in global memory (the output buffer, L2-resident), with the
+// matrix column-major, A[c * d + r].  The reflectors are reduced in place;
+// then Q is formed in place over them, last reflector first: when reflector
+// i is applied to columns i+1.. (rows i..), those columns already hold Q's
+// trailing block and the reflectors stored there are spent, and column i is
+// then replaced by H_i e_i (zeros above row i).  Finally the sign fix, the
+// transpose to row-major and the float32 copy.
+constexpr int kRotGThreads = 1024;
+
+__global__ __launch_bounds__(kRotGThreads) void rotation_global_kernel(int d, const double* __restrict__ G,
+                                                                       double* __restrict__ A,
+                                                                       float* __restrict__ Q32) {
+  __shared__ double rdiag[kRotGMax];
+  __shared__ double red[kRotGThreads];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < d * d; e += kRotGThreads) A[(e % d) * d + e / d] = G[e];   // column-major copy
+  __syncthreads();
+  for (int k = 0; k < d; ++k) {
+    double* ak = A + static_cast<int64_t>(k) * d;
+    double s = 0.0;
+    for (int i = k + tid; i < d; i += kRotGThreads) s += ak[i] * ak[i];
+    red[tid] = s;
+    __syncthreads();
+    for (int o = kRotGThreads / 2; o > 0; o >>= 1) {
+      if (tid < o) red[tid] += red[tid + o];
+      __syncthreads();
+    }
+    const double nrm = sqrt(red[0]);
+    const double x0 = ak[k];
+    const double alpha = (x0 >= 0.0) ? -nrm : nrm;
+    const double vn2 = 2.0 * nrm * (nrm + fabs(x0));
+    __syncthreads();
+    for (int i = k + tid; i < d; i += kRotGThreads) {
+      const double v = (i == k) ? (x0 - alpha) : ak[i];
+      ak[i] = (vn2 > 0.0) ? v / sqrt(vn2) : 0.0;
+    }
+    if (tid == 0) rdiag[k] = (vn2 > 0.0) ? alpha : 0.0;
+    __syncthreads();
+    for (int j = k + 1 + tid; j < d; j += kRotGThreads) {
+      double* aj = A + static_cast<int64_t>(j) * d;
+      double w = 0.0;
+      for (int i = k; i < d; ++i) w += ak[i] * aj[i];
+      w *= 2.0;
+      for (int i = k; i < d; ++i) aj[i] -= w * ak[i];
+    }
+    __syncthreads();
+  }
+  // Q = H_0 H_1 ... H_{d-1} I, formed in place
+  for (int i = d - 1; i >= 0; --i) {
+    const double* vi = A + static_cast<int64_t>(i) * d;   // reflector i, rows i..d-1
+    for (int c = i + 1 + tid; c < d; c += kRotGThreads) {
+      double* qc = A + static_cast<int64_t>(c) * d;
+      double w = 0.0;
+      for (int r = i; r < d; ++r) w += vi[r] * qc[r];
+      w *= 2.0;
+      for (int r = i; r < d; ++r) qc[r] -= w * vi[r];
+    }
+    __syncthreads();
+    const double a = vi[i];
+    __syncthreads();
+    double* qi = A + static_cast<int64_t>(i) * d;
+    for (int r = tid; r < d; r += kRotGThreads)
+      qi[r] = (r < i) ? 0.0 : (r == i ? 1.0 - 2.0 * a * a : -2.0 * a * qi[r]);
+    __syncthreads();
+  }
+  // Pi = Q diag(sign(diag R)), transposed in place to row-major
+  for (int e = tid; e < d * d; e += kRotGThreads) {
+    const int c = e / d, r = e % d;
+    if (rdiag[c] < 0.0) A[e] = -A[e];
+  }
+  __syncthreads();
+  for (int e = tid; e < d * d; e += kRotGThreads) {
+    const int c = e / d, r = e % d;
+    if (r < c) {
+      const double t = A[e];
+      A[e] = A[r * d + c];
+      A[r * d + c] = t;
+    }
+  }
+  __syncthreads();
+  if (Q32)
+    for (int e = tid; e < d * d; e += kRotGThreads) Q32[e] = static_cast<float>(A[e]);
+}
+
 hipError_t launch_rotation(int d, const double* G, double* Q, float* Q32, hipStream_t stream) {
-  hipLaunchKernelGGL(rotation_kernel, dim3(1), dim3(kRotThreads), 0, stream, d, G, Q, Q32);
+  if (d <= kRotMax) hipLaunchKernelGGL(rotation_kernel, dim3(1), dim3(kRotThreads), 0, stream, d, G, Q, Q32);
+  else hipLaunchKernelGGL(rotation_global_kernel, dim3(1), dim3(kRotGThreads), 0, stream, d, G, Q, Q32);
   return hipGetLastError();
 }
 

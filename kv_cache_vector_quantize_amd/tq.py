@@ -275,9 +275,9 @@ def alloc_packed(role, tables, nseq, T, norm_dtype="f16", device="cuda", capacit
     if role == TQ_KEY:
         if hi:   # split stream: one record of (d/32) bits + hi/32 words per token
             codes = torch.zeros((nseq, Tp, (d // 32) * bits + hi // 32), dtype=torch.int32, device=device)
-        else:
-            codes = torch.zeros((nseq, Tp, d // 32, bits), dtype=torch.int32, device=device)
-        signs = torch.zeros((nseq, Tp, m // 32), dtype=torch.int32, device=device)
+        else:   # coordinates padded to whole 32-bit words (bits of padding are 0)
+            codes = torch.zeros((nseq, Tp, (d + 31) // 32, bits), dtype=torch.int32, device=device)
+        signs = torch.zeros((nseq, Tp, (m + 31) // 32), dtype=torch.int32, device=device)
         rnorm = torch.zeros((nseq, Tp), dtype=tdt, device=device)
     else:
         if hi:   # split stream: one record of d bits + hi words per block

@@ -9,8 +9,10 @@ implementation's choice, fixed here so that GPU parity is byte-for-byte.
 All words are little-endian uint32; bit k of a word is (word >> k) & 1.
 
 Key stream (one record per token, coordinates along the word):
-  codes[s, t, w, p]  bit k = bit p of idx[s, t, 32*w + k]     shape [S, T, d/32, b]
-  signs[s, t, w]     bit k = sign bit of z[s, t, 32*w + k]    shape [S, T, m/32]
+  codes[s, t, w, p]  bit k = bit p of idx[s, t, 32*w + k]     shape [S, T, ceil(d/32), b]
+  signs[s, t, w]     bit k = sign bit of z[s, t, 32*w + k]    shape [S, T, ceil(m/32)]
+  (when d or m is not a multiple of 32 the last word is padded with 0 bits:
+  the search workload of the pages runs at d = 200)
 Value stream (blocks of 32 tokens; one record of b words per coordinate):
   codes[s, B, j, :]  the 32 b-bit indices idx[s, 32*B + k, j], k = 0..31,
                      packed in token order: index k occupies bits
@@ -26,11 +28,11 @@ import numpy as np
 
 
 def pack_key_codes(idx, bits):
+    """idx [..., d] -> words [..., ceil(d/32), bits]; the bits of the padding
+    coordinates d .. 32 ceil(d/32) - 1 are 0."""
     idx = np.asarray(idx, dtype=np.int64)
     *lead, d = idx.shape
-    if d % 32:
-        raise ValueError("d must be a multiple of 32")
-    words = np.zeros((*lead, d // 32, bits), dtype=np.uint64)
+    words = np.zeros((*lead, (d + 31) // 32, bits), dtype=np.uint64)
     for j in range(d):
         w, k = divmod(j, 32)
         for p in range(bits):
@@ -50,11 +52,10 @@ def unpack_key_codes(words, d):
 
 
 def pack_signs(signs):
+    """signs [..., m] -> words [..., ceil(m/32)]; padding rows' bits are 0."""
     signs = np.asarray(signs, dtype=bool)
     *lead, m = signs.shape
-    if m % 32:
-        raise ValueError("m must be a multiple of 32")
-    words = np.zeros((*lead, m // 32), dtype=np.uint64)
+    words = np.zeros((*lead, (m + 31) // 32), dtype=np.uint64)
     for i in range(m):
         w, k = divmod(i, 32)
         words[..., w] |= signs[..., i].astype(np.uint64) << np.uint64(k)

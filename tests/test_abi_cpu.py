@@ -85,7 +85,8 @@ def test_codebook_and_rotation_validation(L):
     assert L.tq_codebook(128, 0, None, None, vp(FAKE), vp(FAKE), None) == -1
     assert L.tq_codebook(128, 2, None, None, None, vp(FAKE), None) == -1        # null out
     assert L.tq_codebook(128, 2, None, None, vp(FAKE + 4), vp(FAKE), None) == -1  # misaligned
-    assert L.tq_rotation(129, vp(FAKE), vp(FAKE), None, None) == -1
+    assert L.tq_rotation(1025, vp(FAKE), vp(FAKE), None, None) == -1      # past the global-memory kernel
+    assert L.tq_rotation(1, vp(FAKE), vp(FAKE), None, None) == -1
     assert L.tq_rotation(128, None, vp(FAKE), None, None) == -1
     assert L.tq_hadamard_rotation(96, vp(FAKE), vp(FAKE), None) == -1     # not a power of two
     assert L.tq_hadamard_rotation(8192, vp(FAKE), vp(FAKE), None) == -1
@@ -101,8 +102,10 @@ def test_quantize_validation(L):
     cases = [
         (_tables(tq, rot_kind=2), _packed(tq), -1),            # unknown rotation kind
         (_tables(tq, bits=5), _packed(tq, bits=5), -1),
-        (_tables(tq, d=96), _packed(tq, d=96), -2),            # valid, unsupported d
-        (_tables(tq, m=64), _packed(tq, m=64), -2),            # unsupported sketch size
+        (_tables(tq, d=300), _packed(tq, d=300), -2),          # valid, past the generic kernels' 256
+        (_tables(tq, d=4), _packed(tq, d=4), -2),              # below the generic kernels' 8
+        (_tables(tq, m=512), _packed(tq, m=512), -2),          # sketch past the generic kernels' 256
+        (_tables(tq, d=200, hi=64), _packed(tq, d=200, hi=64), -2),  # split widths only at d = 128
         (_tables(tq), _packed(tq, bits=3), -1),                # bits mismatch
         (_tables(tq, m=0, sketch=False), _packed(tq, role=0, m=0), -1),  # key without sketch
         (_tables(tq, m=0, sketch=False), _packed(tq, role=1, m=0, nd=7), -1),  # bad norm dtype

@@ -61,10 +61,10 @@ def test_topk_many_rows_long():
     _check_topk(_scores(16, 1 << 20, seed=99), 10)
 
 
-def _search(w_bits, N, nq, k, seed, law="normal_outliers"):
-    w = inputs.Workload("search_test", 60 + seed, B=1, Hq=nq, Hkv=1, T=N, k_bits=w_bits, k_law=law)
+def _search(w_bits, N, nq, k, seed, law="normal_outliers", d=D, m=M):
+    w = inputs.Workload("search_test", 60 + seed, B=1, Hq=nq, Hkv=1, T=N, d=d, m=m, k_bits=w_bits, k_law=law)
     X = inputs.key_slice(w, 0, 0, device="cuda").unsqueeze(0).contiguous()
-    tabs = gpu_tables(D, M, w_bits)
+    tabs = gpu_tables(d, m, w_bits)
     p = tq.alloc_packed(tq.TQ_KEY, tabs, 1, N, "f16")
     tq.tq_quantize(tabs, X, p)
     q = inputs.queries(w, device="cuda")                      # [1, nq, d]
@@ -91,14 +91,15 @@ def _check_search(ref_scores_at, logits, idx, val, k, sample):
         assert np.all(ref_other <= kth + 2 * (1e-4 + 1e-3 * abs(kth))), r
 
 
-def test_search_small_against_oracle_scores():
+@pytest.mark.parametrize("d", [128, 200])
+def test_search_small_against_oracle_scores(d):
     """A 20000-key database, 8 queries, top 10: the oracle scores every key
     from the GPU's records; the GPU's top 10 must be a top 10 of them up to
-    the logits tolerance."""
-    say("search small")
+    the logits tolerance.  d = 200 (m = 200) is the pages' search dimension."""
+    say("search small", d)
     N, nq, k = 20000, 8, 10
-    w, p, q, logits, idx, val = _search(3, N, nq, k, seed=1)
-    Pi, S, c, _ = oracle_tables(D, M, 3)
+    w, p, q, logits, idx, val = _search(3, N, nq, k, seed=1, d=d, m=d)
+    Pi, S, c, _ = oracle_tables(d, d, 3)
     codes = p.codes[0].cpu().numpy().view(np.uint32)
     signs = p.signs[0].cpu().numpy().view(np.uint32)
     ridx, rval, rscores = oracle.search_from_records(to64(q)[0], codes, signs,
@@ -116,8 +117,8 @@ def test_search_full_size_sampled():
     of 20000 others."""
     w6 = inputs.WORKLOADS[6]
     say("search full size", w6.name)
-    X = inputs.keys(w6, device="cuda").reshape(1, w6.T, D)
-    tabs = gpu_tables(D, M, w6.k_bits)
+    X = inputs.keys(w6, device="cuda").reshape(1, w6.T, w6.d)
+    tabs = gpu_tables(w6.d, w6.m, w6.k_bits)
     p = tq.alloc_packed(tq.TQ_KEY, tabs, 1, w6.T, w6.norm_dtype)
     tq.tq_quantize(tabs, X, p)
     del X
@@ -128,7 +129,7 @@ def test_search_full_size_sampled():
     logits_h, idx, val = logits.cpu().numpy(), idx.cpu().numpy(), val.cpu().numpy()
     rng = np.random.default_rng(6)
     sample = np.unique(np.concatenate([rng.choice(w6.T, 20000, replace=False), idx.reshape(-1)]))
-    Pi, S, c, _ = oracle_tables(D, M, w6.k_bits)
+    Pi, S, c, _ = oracle_tables(w6.d, w6.m, w6.k_bits)
     codes = p.codes[0].cpu().numpy().view(np.uint32)[sample]
     signs = p.signs[0].cpu().numpy().view(np.uint32)[sample]
     kn = p.norm[0].cpu().numpy().astype(np.float64)[sample]

@@ -12,7 +12,7 @@ from gpu_common import say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("d", [8, 64, 128])
+@pytest.mark.parametrize("d", [8, 64, 128, 200])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_codebook_matches_oracle(d, bits):
     say("tq_codebook", d, bits)
@@ -26,8 +26,9 @@ def test_codebook_matches_oracle(d, bits):
     assert np.array_equal(b32.cpu().numpy(), b64.cpu().numpy().astype(np.float32))
 
 
-@pytest.mark.parametrize("d", [8, 32, 128])
+@pytest.mark.parametrize("d", [8, 32, 128, 129, 200, 256])
 def test_rotation_matches_oracle(d):
+    # up to 128 the factorization runs in LDS, past 128 in global memory
     say("tq_rotation", d)
     G, _ = inputs.table_gaussians(d, 0)
     r64, r32 = tq.tq_rotation(torch.as_tensor(G).cuda())
@@ -39,10 +40,10 @@ def test_rotation_matches_oracle(d):
     assert np.array_equal(r32.cpu().numpy(), P.astype(np.float32))
 
 
-def test_rotation_rank_deficient_column():
+@pytest.mark.parametrize("d", [16, 200])
+def test_rotation_rank_deficient_column(d):
     # a zero column leaves the reflector at the identity and a +1 sign
-    say("tq_rotation zero column")
-    d = 16
+    say("tq_rotation zero column", d)
     G, _ = inputs.table_gaussians(d, 0, seed=3)
     G[:, 5] = 0.0
     r64, _ = tq.tq_rotation(torch.as_tensor(G).cuda())

@@ -197,3 +197,18 @@ def test_bits_per_value_matches_llama_cpp_cache_types():
         bpv = nbytes * 8 / d
         assert bpv == fig[name]
         assert round(16 / bpv, 1) == fig["compression_vs_fp16"][name]
+
+
+def test_packing_pads_partial_words_with_zero_bits():
+    """d = 40 coordinates take two 32-bit words per plane: coordinates 32..39
+    sit at bits 0..7 of the second word and bits 8..31 stay 0 (the padded
+    layout of head dimensions that are not multiples of 32, e.g. the pages'
+    d = 200 search vectors).  All-ones 1-bit codes give 0xFFFFFFFF, 0x000000FF;
+    41 sketch rows of sign 1 give 0xFFFFFFFF, 0x000001FF."""
+    idx = np.ones((1, 40), dtype=np.int64)
+    w = oracle.pack_key_codes(idx, 1)
+    assert w.shape == (1, 2, 1) and w[0, :, 0].tolist() == [0xFFFFFFFF, 0x000000FF]
+    assert np.array_equal(oracle.unpack_key_codes(w, 40), idx)
+    sw = oracle.pack_signs(np.ones((1, 41), dtype=bool))
+    assert sw[0].tolist() == [0xFFFFFFFF, 0x000001FF]
+    assert np.array_equal(oracle.unpack_signs(sw, 41), np.ones((1, 41), dtype=bool))
