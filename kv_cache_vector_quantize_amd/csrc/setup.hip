@@ -273,8 +273,7 @@ __global__ __launch_bounds__(kRotGThreads) void rotation_global_kernel(int d, co
   }
   // Pi = Q diag(sign(diag R)), transposed in place to row-major
   for (int e = tid; e < d * d; e += kRotGThreads) {
-    const int c = e / d, r = e % d;
-    if (rdiag[c] < 0.0) A[e] = -A[e];
+    if (rdiag[e / d] < 0.0) A[e] = -A[e];
   }
   __syncthreads();
   for (int e = tid; e < d * d; e += kRotGThreads) {
