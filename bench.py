@@ -58,8 +58,8 @@ def traffic_from_profiles(kernel_src, kernel_name, workload):
         return None
     try:
         t = json.load(open(p))
-        e = t.get(kernel_name)
-        if e is None or e.get("workload") != workload or e.get("source_sha256") != _sha(kernel_src):
+        e = t.get(f"{kernel_name} @ {workload}")
+        if e is None or e.get("source_sha256") != _sha(kernel_src):
             return None
         return e["hbm_bytes_per_launch"]
     except Exception:
@@ -397,18 +397,32 @@ def main():
     # the key sketch R_hi S_hi + R_hi S_lo + R_lo S_hi; "mfma_flop_per_unit"
     # counts those executed d x d products.
     rot_products = (1 if had else 2) + (1 if w.x_dtype == "f32" else 0)
+    G_ = w.Hq // w.Hkv
+    generic_d = not (d == 128 and m in (0, 128))   # head dimensions other than 128: the VALU kernels
+    if generic_d:
+        kq_kernel = f"quantize_generic_kernel<{w.x_dtype}>"
+    elif hi:
+        kq_kernel = f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>"
+    else:
+        kq_kernel = f"quantize_keys_pipe_kernel<{w.x_dtype}, {w.k_bits}{rtag}>"
+    if generic_d:
+        lg_kernel = f"logits_generic_kernel<{G_}, {w.k_bits}>"
+    elif G_ <= 8:
+        lg_kernel = f"logits_mfma_kernel<{G_}, {w.k_bits}, {nb}>"
+    else:
+        lg_kernel = f"logits_kernel<{G_}>"
     stages = []
     if w.quantize_timed:
         stages.append({"name": "quantize_k", "bytes": nvec * (d * xb + kb), "units": nvec,
                        "fn": lambda: tq.tq_quantize(tk, K, pk),
-                       "kernel": (f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>" if hi
-                                  else f"quantize_keys_pipe_kernel<{w.x_dtype}, {w.k_bits}{rtag}>"),
+                       "kernel": kq_kernel,
                        "flop_per_unit": 2 * d * d + 2 * m * d,
                        "mfma_flop_per_unit": (rot_products + 3) * 2 * d * d})
         if w.v_bits:
             stages.append({"name": "quantize_v", "bytes": nvec * (d * xb + vb), "units": nvec,
                            "fn": lambda: tq.tq_quantize(tv, V, pv),
-                           "kernel": f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}{rtag}>",
+                           "kernel": (f"quantize_generic_kernel<{w.x_dtype}>" if generic_d
+                                      else f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}{rtag}>"),
                            "flop_per_unit": 2 * d * d,
                            "mfma_flop_per_unit": rot_products * 2 * d * d})
     else:
@@ -421,8 +435,7 @@ def main():
                           device=dev)
         stages.append({"name": "logits", "bytes": nvec * kb + w.B * w.Hq * w.T * 4 + qbytes,
                        "units": nvec,
-                       "kernel": (f"logits_mfma_kernel<{w.Hq // w.Hkv}, {w.k_bits}, {nb}>" if w.Hq // w.Hkv <= 8
-                                  else f"logits_kernel<{w.Hq // w.Hkv}>"),
+                       "kernel": lg_kernel,
                        "fn": lambda: tq.tq_attn_logits(tk, q, pk, w.B, w.Hq, w.Hkv, ws=lws, out=logits),
                        "flop_per_unit": 2 * (w.Hq // w.Hkv) * (d + m)})
     if w.topk:
@@ -439,7 +452,6 @@ def main():
         ws = torch.empty(tq.decode_workspace_bytes(w.B, w.Hq, w.Hkv, w.T, d, m), dtype=torch.uint8,
                          device=dev)
         out = torch.empty((w.B, w.Hq, d), dtype=torch.float32, device=dev)
-        G_ = w.Hq // w.Hkv
         stages.append({"name": "decode", "bytes": nvec * (kb + vb) + qbytes + w.B * w.Hq * d * 4,
                        "units": nvec, "kernel": f"decode_mfma_kernel<{G_}, {w.k_bits}, {w.v_bits}>",
                        "fn": lambda: tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv, ws=ws, out=out),
@@ -517,8 +529,8 @@ def main():
     # 32768, decode 102 B per (token, KV head) against 2G(2d+m) flop, so at
     # the fp16 matrix-core peak all of them are bandwidth-bound.
     dom = max(stages, key=lambda st: st["ms"])
-    generic_d = not (d == 128 and m in (0, 128))
-    src = {"quantize_k": "quantize.hip", "quantize_v": "quantize.hip",
+    src = {"quantize_k": "generic.hip" if generic_d else "quantize.hip",
+           "quantize_v": "generic.hip" if generic_d else "quantize.hip",
            "logits": "generic.hip" if generic_d else ("decode_kernels.h" if w.Hq // w.Hkv <= 8 else "attention.hip"),
            "decode": "decode_kernels.h", "topk": "topk.hip"}[dom["name"]]
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
