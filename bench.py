@@ -398,14 +398,18 @@ def main():
     # counts those executed d x d products.
     rot_products = (1 if had else 2) + (1 if w.x_dtype == "f32" else 0)
     G_ = w.Hq // w.Hkv
-    generic_d = not (d == 128 and m in (0, 128))   # head dimensions other than 128: the VALU kernels
+    # head dimensions other than 128: vector-ALU quantize, wide matrix-core
+    # logits (one or two passes of 4 coordinate words)
+    generic_d = not (d == 128 and m in (0, 128))
     if generic_d:
         kq_kernel = f"quantize_generic_kernel<{w.x_dtype}>"
     elif hi:
         kq_kernel = f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>"
     else:
         kq_kernel = f"quantize_keys_pipe_kernel<{w.x_dtype}, {w.k_bits}{rtag}>"
-    if generic_d:
+    if generic_d and G_ <= 8:
+        lg_kernel = f"logits_wide_kernel<{G_}, {w.k_bits}, {nb}, {1 if max(d, m) <= 128 else 2}>"
+    elif generic_d:
         lg_kernel = f"logits_generic_kernel<{G_}, {w.k_bits}>"
     elif G_ <= 8:
         lg_kernel = f"logits_mfma_kernel<{G_}, {w.k_bits}, {nb}>"
@@ -531,13 +535,14 @@ def main():
     dom = max(stages, key=lambda st: st["ms"])
     src = {"quantize_k": "generic.hip" if generic_d else "quantize.hip",
            "quantize_v": "generic.hip" if generic_d else "quantize.hip",
-           "logits": "generic.hip" if generic_d else ("decode_kernels.h" if w.Hq // w.Hkv <= 8 else "attention.hip"),
+           "logits": ("decode_kernels.h" if w.Hq // w.Hkv <= 8 else ("generic.hip" if generic_d else "attention.hip")),
            "decode": "decode_kernels.h", "topk": "topk.hip"}[dom["name"]]
     achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
     # the time divided into is the stage's event-timed call: for decode and
     # logits that call launches query preparation (and decode's combine) too
-    calls = {"decode": f"tq_attn_decode: qprep_kernel, {dom['kernel']}, decode_combine_kernel",
-             "logits": f"tq_attn_logits: qprep_kernel, {dom['kernel']}"}
+    qprep = "qprep_generic_kernel" if generic_d else "qprep_kernel"
+    calls = {"decode": f"tq_attn_decode: {qprep}, {dom['kernel']}, decode_combine_kernel",
+             "logits": f"tq_attn_logits: {qprep}, {dom['kernel']}"}
     roofline = {
         "kernel": dom["kernel"],
         "timed_call": calls.get(dom["name"], dom["kernel"]),

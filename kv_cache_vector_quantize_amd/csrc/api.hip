@@ -216,6 +216,9 @@ tq_status tq_attn_logits(const tq_tables* tk, const void* q, int q_dtype, int B,
                                       align256(static_cast<size_t>(B) * Hq * tk->d * sizeof(float)));
   if (generic(tk)) {
     if (tq::launch_qprep_generic(*tk, q, q_dtype, B * Hq, qr, u, stream) != hipSuccess) return TQ_EHIP;
+    // matrix-core tiles up to 8 heads per KV head; 16 take the vector-ALU kernel
+    if (Hq / Hkv <= 8 && tk->m > 0 && !split(tk))
+      return from_hip(tq::launch_logits_wide(*tk, qr, u, B, Hq, Hkv, *k, logits, stream));
     return from_hip(tq::launch_logits_generic(*tk, qr, u, B, Hq, Hkv, *k, logits, stream));
   }
   hipError_t e = tq::launch_qprep(*tk, q, q_dtype, B * Hq, qr, u, stream);

@@ -12,7 +12,10 @@ namespace tq {
                                  int nsplit, hipStream_t stream);                                  \
   hipError_t logits_launch_g##GV(const tq_tables& tk, const float* qr, const float* u,             \
                                  int64_t nseq, const tq_packed& k, int len, int nsplit,            \
-                                 float* out, hipStream_t stream);
+                                 float* out, hipStream_t stream);                                  \
+  hipError_t logits_wide_launch_g##GV(const tq_tables& tk, const float* qr, const float* u,        \
+                                      int64_t nseq, const tq_packed& k, int len, int nsplit,       \
+                                      float* out, hipStream_t stream);
 TQ_DECL_G(1)
 TQ_DECL_G(2)
 TQ_DECL_G(4)
@@ -148,6 +151,28 @@ hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float*
     case 2: return logits_launch_g2(tk, qr, u, nseq, k, len, nsplit, logits, stream);
     case 4: return logits_launch_g4(tk, qr, u, nseq, k, len, nsplit, logits, stream);
     case 8: return logits_launch_g8(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The wide logits kernel holds its query fragments for two passes in
+// registers (about 250 VGPRs: 2 workgroups per CU) and sets up for longer
+// than the d = 128 one: one round of the chip, up to 8192 tokens a split.
+constexpr int kWideTarget = 2 * kCus;
+constexpr int kWideMaxSplit = 8192;
+
+hipError_t launch_logits_wide(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
+                              int Hkv, const tq_packed& k, float* logits, hipStream_t stream) {
+  if (B == 0 || k.T == 0) return hipSuccess;
+  const int G = Hq / Hkv;
+  const int64_t nseq = static_cast<int64_t>(B) * Hkv;
+  const int len = split_length(nseq, k.T, kWideMaxSplit, kWideTarget);
+  const int nsplit = static_cast<int>((k.T + len - 1) / len);
+  switch (G) {
+    case 1: return logits_wide_launch_g1(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 2: return logits_wide_launch_g2(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 4: return logits_wide_launch_g4(tk, qr, u, nseq, k, len, nsplit, logits, stream);
+    case 8: return logits_wide_launch_g8(tk, qr, u, nseq, k, len, nsplit, logits, stream);
     default: return hipErrorInvalidValue;
   }
 }

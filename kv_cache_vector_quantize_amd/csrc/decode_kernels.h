@@ -209,11 +209,13 @@ __device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const c
 // word; tab: the LDS tables of build_tables.
 // MX (split streams): pw holds KB planes, the narrow words' top plane zero,
 // and ktab is the lane's own pair table (wide or narrow, generic layout).
+// tile_accumulate adds one group of 4 coordinate words to the two
+// accumulators (head dimensions above 128 take two groups), tile_finish
+// folds their hi and lo columns into cen and qj.
 template <int G, int KB, bool X2, bool MX = false>
-__device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
-                                            const half8 (&bu)[4], const char* tab, float (&cen)[4],
-                                            float (&qj)[4], const char* ktab = nullptr) {
-  floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void tile_accumulate(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
+                                                const half8 (&bu)[4], const char* tab, floatx4& accC,
+                                                floatx4& accS, const char* ktab = nullptr) {
   if constexpr (MX) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -262,12 +264,26 @@ __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, con
   accS = sign_kstep<1>(sw, sw << 4, tab + kSgnOff, bu[1], accS);
   accS = sign_kstep<2>(sw, sw << 4, tab + kSgnOff, bu[2], accS);
   accS = sign_kstep<3>(sw, sw << 4, tab + kSgnOff, bu[3], accS);
-  // the hi column n plus the lo column G + n
+}
+
+// the hi column n plus the lo column G + n of the two accumulators
+template <int G>
+__device__ __forceinline__ void tile_finish(const floatx4& accC, const floatx4& accS, float (&cen)[4],
+                                            float (&qj)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     cen[i] = accC[i] + row_shl<G>(accC[i]);
     qj[i] = accS[i] + row_shl<G>(accS[i]);
   }
+}
+
+template <int G, int KB, bool X2, bool MX = false>
+__device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
+                                            const half8 (&bu)[4], const char* tab, float (&cen)[4],
+                                            float (&qj)[4], const char* ktab = nullptr) {
+  floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
+  tile_accumulate<G, KB, X2, MX>(pw, sw, bq, bu, tab, accC, accS, ktab);
+  tile_finish<G>(accC, accS, cen, qj);
 }
 
 // This lane's query fragments for KV head s, built from the rotated queries
@@ -1127,6 +1143,254 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0, M
   }
 }
 
+// ------------------------------------------------------------ logits, d up to 256
+// The same logits at other head dimensions, up to d = 256 and m = 256 sketch
+// rows (the pages' search vectors have d = 200: a2a-mcp.org page,
+// "Benchmarks"): the records hold D = ceil(d/32) code-plane words and
+// Dm = ceil(m/32) sign words per key, whose padding bits are zero.  A tile
+// takes NP passes of 4 words (words 4p + g4 in lane group g4), each one
+// group of centroid and sign K-steps added into the same accumulators; the
+// query fragments are zero at coordinates >= d and sketch rows >= m, so the
+// padding and the words past D or Dm contribute nothing.
+//
+// Blocks stream through an LDS ring by LDS DMA as in decode, in stream
+// order (key records, sign words, the two norm rows: 4 D KB, 4 Dm and 2 NK
+// bytes per token).  A ring slot is sized for D = Dm = 8, so that every lane
+// of a fixed number of DMA loads per block lands inside it (the waits count
+// loads): lanes past the block's real bytes re-read its first 16 bytes into
+// the slot's unused end.  Per token a lane reads its KB words and sign word
+// at a stride of D KB and Dm words, which spreads the 16 rows of a tile over
+// the LDS banks (records are not a multiple of 16 bytes, so there is no
+// reordering).
+
+template <int KB, int NK>
+struct WidePacket {
+  static constexpr int kMaxBytes = 128 * 8 * KB + 128 * 8 + 64 * NK;
+  static constexpr int kInstr = (kMaxBytes / 16 + 63) / 64;   // DMA loads per block
+  static constexpr int kSlot = 1024 * kInstr;                 // bytes per wave and block
+  static constexpr int kTail = 64;                            // every lane of every load
+};
+
+template <typename P>
+struct WideStream {
+  const char* src[P::kInstr];
+  int step[P::kInstr];
+  uint32_t ring0;   // LDS address of this wave's slot 0
+  int kslot;        // bytes per ring slot (the 4 waves' packets)
+
+  template <int KB, int NK>
+  __device__ __forceinline__ void init(const uint32_t* kcodes, const uint32_t* ksigns, const void* knorm,
+                                       const void* krnorm, int D, int Dm, int64_t tok, int lane,
+                                       uint32_t ring_wave0, int slot_bytes) {
+    ring0 = ring_wave0;
+    kslot = slot_bytes;
+    const int ck = 8 * D * KB, cs = 8 * Dm;   // 16-byte chunks of keys and signs per block
+#pragma unroll
+    for (int i = 0; i < P::kInstr; ++i) {
+      const int c = 64 * i + lane;
+      const char* p = reinterpret_cast<const char*>(kcodes) + tok * 4 * D * KB;   // past the packet
+      int st = 0;
+      if (c < ck) {
+        p += 16 * c;
+        st = 4 * 32 * 4 * D * KB;
+      } else if (c < ck + cs) {
+        p = reinterpret_cast<const char*>(ksigns) + tok * 4 * Dm + 16 * (c - ck);
+        st = 4 * 32 * 4 * Dm;
+      } else if (c < ck + cs + 4 * NK) {
+        const int e = c - ck - cs, row = e / (2 * NK);
+        p = reinterpret_cast<const char*>(row == 0 ? knorm : krnorm) + tok * NK + 16 * (e - 2 * NK * row);
+        st = 4 * 32 * NK;
+      }
+      src[i] = p;
+      step[i] = st;
+    }
+  }
+
+  __device__ __forceinline__ void issue(int j, int slot) const {
+    const uint32_t l = ring0 + slot * kslot;
+#pragma unroll
+    for (int i = 0; i < P::kInstr; ++i) dma16(src[i] + static_cast<int64_t>(j) * step[i], l + 1024 * i);
+  }
+
+  __device__ __forceinline__ void advance(int j, int nbw, int slot) const {
+    if (j + kRing - 1 < nbw) {
+      issue(j + kRing - 1, slot == 0 ? kRing - 1 : slot - 1);
+      wait_vm<(kRing - 1) * P::kInstr>();
+    } else if (kRing > 2 && j + 2 < nbw) {
+      wait_vm<(kRing > 2 ? 2 : 0) * P::kInstr>();
+    } else if (j + 1 < nbw) {
+      wait_vm<P::kInstr>();
+    } else {
+      wait_vm<0>();
+    }
+  }
+};
+
+// This lane's fragments for pass p (coordinate words 4p .. 4p+3) of KV head
+// s, from rotated queries of d floats and sketched ones of m floats per row.
+template <int G>
+__device__ __forceinline__ void query_frags_wide(const float* __restrict__ qr, const float* __restrict__ u,
+                                                 int64_t s, int lane, float fu, int d, int m, int p,
+                                                 half8 (&bq)[8], half8 (&bu)[4]) {
+  const int n = lane & 15, g4 = lane >> 4;
+  const bool hi_col = n < G, lo_col = (n >= G) && (n < 2 * G);
+  const int g = hi_col ? n : (lo_col ? n - G : 0);
+  const float* qg = qr + (s * G + g) * d;
+  const float* ug = u + (s * G + g) * m;
+  const int w0 = 32 * (4 * p + g4);
+  auto part = [&](float x) -> _Float16 {
+    const _Float16 a = static_cast<_Float16>(x);
+    if (hi_col) return a;
+    if (lo_col) return static_cast<_Float16>(x - static_cast<float>(a));
+    return static_cast<_Float16>(0.f);
+  };
+  constexpr int kSlot[8] = {0, 1, 0, 1, 2, 3, 2, 3};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    _Float16 h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = w0 + 4 * c + kSlot[i];
+      h[i] = part(j < d ? qg[j] : 0.f);
+    }
+    bq[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    _Float16 h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = w0 + 8 * c + i;
+      h[i] = part(j < m ? fu * ug[j] : 0.f);
+    }
+    bu[c] = u4_to_h8(h2u(h[0], h[1]), h2u(h[2], h[3]), h2u(h[4], h[5]), h2u(h[6], h[7]));
+  }
+}
+
+template <int G, int KB, int NK, int NP>
+__global__ __launch_bounds__(kDecThreads, 2) void logits_wide_kernel(
+    const float* __restrict__ qr, const float* __restrict__ u, const float* __restrict__ ck, int d, int m,
+    int64_t T, int64_t TpK, int split_len, const uint32_t* __restrict__ kcodes,
+    const uint32_t* __restrict__ ksigns, const void* knorm, const void* krnorm, float fu,
+    float* __restrict__ out) {
+  using P = WidePacket<KB, NK>;
+  constexpr int kSlot = 4 * P::kSlot;   // one ring slot: the 4 waves' packets
+  __shared__ __align__(16) char lds[kTabBytes];
+  __shared__ __align__(16) char ring[kRing * kSlot];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g4 = lane >> 4;
+  const int split = blockIdx.x;
+  const int64_t s = blockIdx.y;
+  const int t0 = split * split_len;                  // T < 2^28 (checked on the host)
+  const int Ti = static_cast<int>(T);
+  const int t1 = (t0 + split_len < Ti) ? t0 + split_len : Ti;
+  const int nb_split = (t1 - t0 + 31) / 32;
+  const int nbw = (nb_split > wave) ? (nb_split - wave + 3) / 4 : 0;
+  const int D = (d + 31) >> 5, Dm = (m + 31) >> 5;   // <= 4 NP (checked on the host)
+
+  WideStream<P> st;
+  st.template init<KB, NK>(kcodes, ksigns, knorm, krnorm, D, Dm, s * TpK + t0 + 32 * wave, lane,
+                           lds_addr(ring) + wave * P::kSlot, kSlot);
+#pragma unroll
+  for (int jj = 0; jj + 1 < kRing; ++jj)
+    if (jj < nbw) st.issue(jj, jj);
+
+  build_tables<KB, 0, false>(ck, nullptr, lds, tid, kDecThreads);
+  half8 bq[NP][8], bu[NP][4];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) query_frags_wide<G>(qr, u, s, lane, fu, d, m, p, bq[p], bu[p]);
+  __syncthreads();
+
+  float* out_h = out + (s * G + (n < G ? n : 0)) * T;
+  const bool vec_ok = (Ti & 3) == 0;                  // 16-byte aligned output rows
+  // this lane's offsets within a packet: its tile-0 token's key words and
+  // sign word (tile 1: 4 tokens on), and its group's 8 tokens' norms.  Words
+  // past D or Dm read word 0 and are cleared.
+  const int trow = 8 * (n >> 2) + (n & 3);
+  uint32_t koff[NP], soff[NP];
+  bool kin[NP], sin[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int w = 4 * p + g4;
+    kin[p] = w < D;
+    sin[p] = w < Dm;
+    koff[p] = 4 * (trow * D * KB + (kin[p] ? w : 0) * KB);
+    soff[p] = 128 * D * KB + 4 * (trow * Dm + (sin[p] ? w : 0));
+  }
+  const uint32_t ktile = 16 * D * KB, stile = 16 * Dm;   // 4 tokens of records
+  const uint32_t nkoff = 128 * D * KB + 128 * Dm + 8 * NK * g4;
+  int slot = 0;
+  for (int j = 0; j < nbw; ++j) {
+    st.advance(j, nbw, slot);
+    const uint32_t pko = slot * kSlot + wave * P::kSlot;   // the block's packet in the ring
+    slot = (slot == kRing - 1) ? 0 : slot + 1;
+    const char* nkb = lds_at(ring, pko + nkoff);
+    const int tb = t0 + 32 * (wave + 4 * j);           // first token of the block
+    float lv[8];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint32_t* kp = reinterpret_cast<const uint32_t*>(lds_at(ring, pko + koff[p] + tau * ktile));
+        uint32_t kw[KB];
+#pragma unroll
+        for (int q = 0; q < KB; ++q) kw[q] = kin[p] ? kp[q] : 0u;
+        const uint32_t sw0 = *reinterpret_cast<const uint32_t*>(lds_at(ring, pko + soff[p] + tau * stile));
+        const uint32_t sw = sin[p] ? sw0 : 0u;
+        tile_accumulate<G, KB, false>(kw, sw, bq[p], bu[p], lds, accC, accS);
+      }
+      float cen[4], qj[4];
+      tile_finish<G>(accC, accS, cen, qj);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        lv[4 * tau + i] = fmaf(norm_at<NK>(nkb, 4 * tau + i), cen[i], norm_at<NK>(nkb + 32 * NK, 4 * tau + i) * qj[i]);
+    }
+    // lane (g4, n < G): tokens tb + 8*g4 .. tb + 8*g4 + 7 of head n
+    if (n < G) {
+      const int tt = tb + 8 * g4;
+      if (vec_ok && tt + 8 <= Ti) {
+        float4* o4 = reinterpret_cast<float4*>(out_h + tt);
+        o4[0] = make_float4(lv[0], lv[1], lv[2], lv[3]);
+        o4[1] = make_float4(lv[4], lv[5], lv[6], lv[7]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (tt + k < Ti) out_h[tt + k] = lv[k];
+      }
+    }
+  }
+}
+
+template <int G, int NP>
+static void launch_logits_wide_np(dim3 grid, hipStream_t stream, const tq_tables& tk, const float* qr,
+                                  const float* u, const tq_packed& k, int len, float fu, float* out) {
+#define TQ_LW(KBV, NKV)                                                                                 \
+  hipLaunchKernelGGL((logits_wide_kernel<G, KBV, NKV, NP>), grid, dim3(kDecThreads), 0, stream, qr, u,   \
+                     tk.centroids, tk.d, tk.m, k.T, stream_stride(k), len, k.codes, k.signs, k.norm,     \
+                     k.rnorm, fu, out)
+  const bool f16 = k.norm_dtype == TQ_F16;
+  switch (tk.bits) {
+    case 1: if (f16) TQ_LW(1, 2); else TQ_LW(1, 4); break;
+    case 2: if (f16) TQ_LW(2, 2); else TQ_LW(2, 4); break;
+    case 3: if (f16) TQ_LW(3, 2); else TQ_LW(3, 4); break;
+    default: if (f16) TQ_LW(4, 2); else TQ_LW(4, 4); break;
+  }
+#undef TQ_LW
+}
+
+template <int G>
+static hipError_t launch_logits_wide_g(const tq_tables& tk, const float* qr, const float* u, int64_t nseq,
+                                       const tq_packed& k, int len, int nsplit, float* out, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(nsplit), static_cast<unsigned>(nseq));
+  const float fu = 1.2533141373155003f / static_cast<float>(tk.m);   // sqrt(pi/2) / m
+  const int words = ((tk.d > tk.m ? tk.d : tk.m) + 31) / 32;
+  if (words <= 4) launch_logits_wide_np<G, 1>(grid, stream, tk, qr, u, k, len, fu, out);
+  else launch_logits_wide_np<G, 2>(grid, stream, tk, qr, u, k, len, fu, out);
+  return hipGetLastError();
+}
+
 template <int G, int KB, int VB>
 static void launch_norms(dim3 grid, hipStream_t stream, const tq_tables& tk, const tq_tables& tv,
                          const float* qr, const float* u, const tq_packed& k, const tq_packed& v,
@@ -1239,6 +1503,11 @@ static hipError_t launch_logits_g(const tq_tables& tk, const float* qr, const fl
                                  int64_t nseq, const tq_packed& k, int len, int nsplit,            \
                                  float* out, hipStream_t stream) {                                 \
     return launch_logits_g<GV>(tk, qr, u, nseq, k, len, nsplit, out, stream);                      \
+  }                                                                                                \
+  hipError_t logits_wide_launch_g##GV(const tq_tables& tk, const float* qr, const float* u,        \
+                                      int64_t nseq, const tq_packed& k, int len, int nsplit,       \
+                                      float* out, hipStream_t stream) {                            \
+    return launch_logits_wide_g<GV>(tk, qr, u, nseq, k, len, nsplit, out, stream);                 \
   }
 
 }  // namespace tq

@@ -1,17 +1,16 @@
-// Quantize, query preparation and logits at head dimensions other than the
-// matrix-core kernels' 128 (any d <= 256, sketch rows m <= 256): the vector
-// search workload of the pages runs at d = 200 (a2a-mcp.org page,
-// "Benchmarks": GloVe vectors, judged by the top-k recall of the estimated
-// inner products).
+// Quantize, query preparation and (16 query heads per KV head) logits at
+// head dimensions other than the matrix-core kernels' 128 (any d <= 256,
+// sketch rows m <= 256): the vector search workload of the pages runs at
+// d = 200 (a2a-mcp.org page, "Benchmarks": GloVe vectors, judged by the
+// top-k recall of the estimated inner products).  Logits for up to 8 query
+// heads per KV head run on the matrix-core tiles (logits_wide_kernel).
 //
 // Same method as the d = 128 kernels (a2a-mcp.org page, "How it works",
 // Stages 1 and 2): normalise, rotate, count the codebook boundaries at or
 // below each rotated coordinate, and for keys take the signs of the sketch
 // of the residual.  These run on the vector ALU with float64 accumulation
 // (products of float32 table entries and exact inputs): database
-// quantization is set-up for search, and the logits are bound by their
-// index arithmetic, not by a contraction worth the matrix cores' operand
-// shuffling at d = 200.
+// quantization is set-up for search.
 //
 // Layout as at d = 128 with d and m padded to whole 32-bit words: key
 // codes[s][Tp][ceil(d/32)][bits], signs[s][Tp][ceil(m/32)], value
@@ -174,7 +173,12 @@ __global__ __launch_bounds__(kGThreads) void quantize_generic_kernel(
   }
 }
 
-// q' = Pi q and u = S q' for one query head per workgroup (float64 sums).
+// q' = Pi q and u = S q' (float64 sums).  Workgroup (h, rb) computes the
+// whole q' of query head h and rows 32 rb .. 32 rb + 31 of its u: thread
+// (r, part) = (tid / 8, tid % 8) takes row r of a group of 32 rows and the
+// row's entries part, part + 8, ... (the 8 threads of a row read 32
+// consecutive bytes per load), three shuffles sum the eighths.  Workgroup
+// rb = 0 writes q'.
 template <typename QT>
 __global__ __launch_bounds__(kGThreads) void qprep_generic_kernel(int d, int m, const float* __restrict__ rot,
                                                                  const float* __restrict__ sketch,
@@ -182,21 +186,56 @@ __global__ __launch_bounds__(kGThreads) void qprep_generic_kernel(int d, int m, 
                                                                  float* __restrict__ u) {
   __shared__ double qs[kGMax], qrs[kGMax];
   const int64_t h = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int rb = blockIdx.y;
+  const int tid = threadIdx.x, r = tid >> 3, part = tid & 7;
   for (int k = tid; k < d; k += kGThreads) qs[k] = load_elem<QT>(q, h * d + k);
   __syncthreads();
-  for (int j = tid; j < d; j += kGThreads) {
+  // every load of a row's eighth is issued before the sums (at most 32 per
+  // thread), unconditionally from a clamped index and masked afterwards: a
+  // load under a condition becomes a branch that waits for it, and the L2
+  // latency would be paid once per product
+  auto load_part = [&](const float* row, float (&w)[32]) {
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int k = part + 8 * t;
+      const float x = row[k < d ? k : d - 1];
+      w[t] = k < d ? x : 0.f;
+    }
+  };
+  auto part_dot = [&](const float (&w)[32], const double* v) {
     double a = 0.0;
-    for (int k = 0; k < d; ++k) a = fma(static_cast<double>(rot[static_cast<int64_t>(j) * d + k]), qs[k], a);
-    qrs[j] = a;
-    qr[h * d + j] = static_cast<float>(a);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int k = part + 8 * t;
+      a = fma(static_cast<double>(w[t]), v[k < d ? k : 0], a);
+    }
+    a += __shfl_xor(a, 1, 8);
+    a += __shfl_xor(a, 2, 8);
+    a += __shfl_xor(a, 4, 8);
+    return a;
+  };
+  for (int j0 = 0; j0 < d; j0 += 64) {   // two groups of 32 rows in flight
+    const int ja = j0 + r, jb = j0 + 32 + r;
+    float wa[32], wb[32];
+    load_part(rot + static_cast<int64_t>(ja < d ? ja : 0) * d, wa);
+    load_part(rot + static_cast<int64_t>(jb < d ? jb : 0) * d, wb);
+    const double a = part_dot(wa, qs), b = part_dot(wb, qs);
+    if (part == 0 && ja < d) {
+      qrs[ja] = a;
+      if (rb == 0) qr[h * d + ja] = static_cast<float>(a);
+    }
+    if (part == 0 && jb < d) {
+      qrs[jb] = b;
+      if (rb == 0) qr[h * d + jb] = static_cast<float>(b);
+    }
   }
+  if (m == 0) return;   // no sketch (uniform)
   __syncthreads();
-  for (int i = tid; i < m; i += kGThreads) {
-    double a = 0.0;
-    for (int j = 0; j < d; ++j) a = fma(static_cast<double>(sketch[static_cast<int64_t>(i) * d + j]), qrs[j], a);
-    u[h * m + i] = static_cast<float>(a);
-  }
+  const int i = 32 * rb + r;
+  float wi[32];
+  load_part(sketch + static_cast<int64_t>(i < m ? i : 0) * d, wi);
+  const double a = part_dot(wi, qrs);
+  if (part == 0 && i < m) u[h * m + i] = static_cast<float>(a);
 }
 
 // Raw logits of the G query heads that share KV head s (blockIdx.y), one
@@ -280,11 +319,12 @@ hipError_t launch_quantize_generic(const tq_tables& t, const void* x, int x_dtyp
 hipError_t launch_qprep_generic(const tq_tables& tk, const void* q, int q_dtype, int nh, float* qr, float* u,
                                 hipStream_t stream) {
   if (nh == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(nh), static_cast<unsigned>(tk.m > 0 ? (tk.m + 31) / 32 : 1));
   if (q_dtype == TQ_BF16)
-    hipLaunchKernelGGL(qprep_generic_kernel<uint16_t>, dim3(nh), dim3(kGThreads), 0, stream, tk.d, tk.m, tk.rot,
+    hipLaunchKernelGGL(qprep_generic_kernel<uint16_t>, grid, dim3(kGThreads), 0, stream, tk.d, tk.m, tk.rot,
                        tk.sketch, static_cast<const uint16_t*>(q), qr, u);
   else
-    hipLaunchKernelGGL(qprep_generic_kernel<float>, dim3(nh), dim3(kGThreads), 0, stream, tk.d, tk.m, tk.rot,
+    hipLaunchKernelGGL(qprep_generic_kernel<float>, grid, dim3(kGThreads), 0, stream, tk.d, tk.m, tk.rot,
                        tk.sketch, static_cast<const float*>(q), qr, u);
   return hipGetLastError();
 }

@@ -49,6 +49,12 @@ hipError_t launch_decode(const tq_tables& tk, const tq_tables& tv, const float* 
 hipError_t launch_logits_mfma(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
                               int Hkv, const tq_packed& k, float* logits, hipStream_t stream);
 
+// Logits on the matrix cores at any d <= 256 and 1 <= m <= 256 from the
+// rotated queries of launch_qprep_generic (rows of d and m floats), for
+// G = Hq/Hkv in {1, 2, 4, 8} and keys of one width.
+hipError_t launch_logits_wide(const tq_tables& tk, const float* qr, const float* u, int B, int Hq,
+                              int Hkv, const tq_packed& k, float* logits, hipStream_t stream);
+
 // Head dimensions other than 128 (d <= 256, m <= 256): vector-ALU quantize,
 // query preparation and logits (generic.hip).
 hipError_t launch_quantize_generic(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,

@@ -1,8 +1,10 @@
-"""GPU parity at head dimensions other than 128 (the vector-ALU kernels):
-the pages' search vectors have d = 200 (a2a-mcp.org page, "Benchmarks"),
-quantized with m = 200 sketch rows; other sizes check the padding of
-partial 32-bit words.  Codes, signs and norms of every vector and every
-logit are compared with the oracle; decode and appends stay at d = 128."""
+"""GPU parity at head dimensions other than 128: the pages' search vectors
+have d = 200 (a2a-mcp.org page, "Benchmarks"), quantized with m = 200 sketch
+rows; other sizes check the padding of partial 32-bit words.  Quantize runs
+on the vector-ALU kernels, logits on the matrix-core tiles (one or two
+passes of 4 coordinate words) for up to 8 query heads per KV head and on the
+vector ALU for 16.  Codes, signs and norms of every vector and every logit
+are compared with the oracle; decode and appends stay at d = 128."""
 
 import ctypes
 
@@ -56,15 +58,20 @@ def test_generic_keys_and_values(d, m, bits, dtype):
     assert np.all(full[:, 333:] == 0) and not torch.any(pv.buf_norm[:, 333:])
 
 
-@pytest.mark.parametrize("G,bits,T", [(1, 3, 1000), (8, 3, 4097), (16, 2, 300), (4, 4, 64)])
-def test_generic_logits(G, bits, T):
-    say("generic logits", G, bits, T)
-    d = m = 200
+@pytest.mark.parametrize("d,m,G,bits,T,nd", [
+    (200, 200, 1, 3, 1000, "f16"), (200, 200, 8, 3, 4097, "f16"), (200, 200, 16, 2, 300, "f16"),
+    (200, 200, 4, 4, 64, "f16"), (200, 200, 2, 1, 777, "f32"), (200, 200, 8, 2, 2100, "f32"),
+    (256, 256, 8, 3, 515, "f16"),      # eight full words in both passes
+    (136, 32, 4, 2, 333, "f16"),       # five code words, one sign word
+    (96, 64, 8, 3, 1031, "f32"),       # one pass (three code words, two sign words)
+    (128, 64, 2, 4, 96, "f16")])       # d = 128 with a shorter sketch
+def test_generic_logits(d, m, G, bits, T, nd):
+    say("generic logits", d, m, G, bits, T, nd)
     B, Hkv = 2, 2
     Hq = G * Hkv
     X = (torch.randn((B * Hkv, T, d), device="cuda") * 2).to(torch.bfloat16).contiguous()
     tk = gpu_tables(d, m, bits)
-    pk = tq.alloc_packed(tq.TQ_KEY, tk, B * Hkv, T, "f16")
+    pk = tq.alloc_packed(tq.TQ_KEY, tk, B * Hkv, T, nd)
     tq.tq_quantize(tk, X, pk)
     q = torch.randn((B, Hq, d), device="cuda").to(torch.bfloat16)
     got = tq.tq_attn_logits(tk, q, pk, B, Hq, Hkv).cpu().numpy()
