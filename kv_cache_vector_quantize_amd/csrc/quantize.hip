@@ -155,41 +155,44 @@ __device__ __forceinline__ int value_index(float y, const QTab<BITS>& tab) {
   return (cnt ^ sgn) + half;  // half + cnt, or half - 1 - cnt
 }
 
-// The same index for keys in the transposed layout (one token per lane):
-// appends the index's plane bits, inverted, below the bits
-// already in pw[] -- pw[BITS-1] <- the sign bit of y (the sign plane is set
-// for y's sign bit clear), pw[p] <- the sign bit of y XOR that of a - t for
-// the boundary t the magnitude search tested for plane p (set for
-// [a >= t] XNOR [y's sign bit clear]).  a - t is never -0 or NaN for finite
-// inputs, so its sign bit is exactly a < t, the compare value_index makes.
-// Returns the signed centroid through C (y's sign, so -0.0 gives -mag).
+// The same index for keys in the transposed layout (one token per lane),
+// of y = x rt (x the rotation output, rt > 0 its token's scale, or 0 for a
+// zero vector, whose x is +0): appends the index's plane bits, inverted,
+// below the bits already in pw[] -- pw[BITS-1] <- the sign bit of x, which
+// is y's (the sign plane is set for it clear), pw[p] <- the sign bit of x
+// XOR that of a rt - t, a = |x|, for the boundary t the magnitude search
+// tested for plane p (set for [|y| >= t] XNOR [y's sign bit clear]).  Each
+// a rt - t is one fma, never -0 or NaN for finite inputs (the exact
+// difference is 0 or far above the smallest denormal), so its sign bit is
+// exactly |y| < t, the compare value_index makes.  Returns the signed
+// centroid through C (x's sign, so -0.0 gives -mag).
 template <int BITS>
-__device__ __forceinline__ void quant_append(float y, const QTab<BITS>& tab, uint32_t* pw, float& C) {
-  const uint32_t yb = __float_as_uint(y);
-  const float a = fabsf(y);
+__device__ __forceinline__ void quant_append(float x, float rt, const QTab<BITS>& tab, uint32_t* pw, float& C) {
+  const uint32_t yb = __float_as_uint(x);
+  const float a = fabsf(x);
   auto push = [&](int p, uint32_t bits) { pw[p] = __builtin_amdgcn_alignbit(pw[p], bits, 31); };
   push(BITS - 1, yb);
   float mag;
   if constexpr (BITS == 1) {
     mag = tab.cpos[0];
   } else if constexpr (BITS == 2) {
-    const float d1 = a - tab.tpos[0];
+    const float d1 = fmaf(a, rt, -tab.tpos[0]);
     push(0, yb ^ __float_as_uint(d1));
     mag = sel(d1 >= 0.f, tab.cpos[1], tab.cpos[0]);
   } else if constexpr (BITS == 3) {
-    const float d1 = a - tab.tpos[1];
+    const float d1 = fmaf(a, rt, -tab.tpos[1]);
     const bool m1 = d1 >= 0.f;
-    const float d2 = a - sel(m1, tab.tpos[2], tab.tpos[0]);
+    const float d2 = fmaf(a, rt, -sel(m1, tab.tpos[2], tab.tpos[0]));
     const bool m2 = d2 >= 0.f;
     push(1, yb ^ __float_as_uint(d1));
     push(0, yb ^ __float_as_uint(d2));
     mag = sel(m1, sel(m2, tab.cpos[3], tab.cpos[2]), sel(m2, tab.cpos[1], tab.cpos[0]));
   } else {
-    const float d1 = a - tab.tpos[3];
+    const float d1 = fmaf(a, rt, -tab.tpos[3]);
     const bool m1 = d1 >= 0.f;
-    const float d2 = a - sel(m1, tab.tpos[5], tab.tpos[1]);
+    const float d2 = fmaf(a, rt, -sel(m1, tab.tpos[5], tab.tpos[1]));
     const bool m2 = d2 >= 0.f;
-    const float d3 = a - sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0]));
+    const float d3 = fmaf(a, rt, -sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0])));
     const bool m3 = d3 >= 0.f;
     push(2, yb ^ __float_as_uint(d1));
     push(1, yb ^ __float_as_uint(d2));
@@ -198,7 +201,22 @@ __device__ __forceinline__ void quant_append(float y, const QTab<BITS>& tab, uin
     const float hi4 = sel(m2, sel(m3, tab.cpos[7], tab.cpos[6]), sel(m3, tab.cpos[5], tab.cpos[4]));
     mag = sel(m1, hi4, lo4);
   }
-  C = copysignf(mag, y);
+  C = copysignf(mag, x);
+}
+
+// y - C for y = x rt, one v_fma_f32 with the addend negated by a source
+// modifier (the compiler would otherwise negate C with a separate XOR to
+// use the accumulating form); the result is a value of its own, so that its
+// fp16 rounding is one v_cvt_pk_f16_f32 per pair rather than a fused
+// fma_mix per value
+__device__ __forceinline__ float residual(float x, float rt, float C) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  float r;
+  asm("v_fma_f32 %0, %1, %2, -%3" : "=v"(r) : "v"(x), "v"(rt), "v"(C));
+  return r;
+#else
+  return fmaf(x, rt, -C);
+#endif
 }
 
 template <typename XT>
@@ -532,17 +550,11 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
       float rodd = 0.f;
 #pragma unroll
       for (int v = 15; v >= 0; --v) {
-        const float y = acc[v] * rt;
         float C;
-        quant_append<WB>(y, tb, pw, C);
+        quant_append<WB>(acc[v], rt, tb, pw, C);
         // residual x256 (for a zero vector y = 0 and the residual is unused:
         // its signs and rnorm are fixed at the store)
-        float r = y - C;
-#if defined(__HIP_DEVICE_COMPILE__)
-        // keep r a value of its own, so that its fp16 rounding below is one
-        // v_cvt_pk_f16_f32 per pair rather than a fused fma_mix per value
-        asm("" : "+v"(r));
-#endif
+        const float r = residual(acc[v], rt, C);
         rr = fmaf(r, r, rr);
         if (v & 1) {
           rodd = r;
@@ -932,13 +944,9 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
 #pragma unroll
     for (int k = 0; k < 16; ++k) z[k] = 0.f;
     auto qstep = [&](int v) {
-      const float y = acc[v] * rt;
       float C;
-      quant_append<BITS>(y, tab, pw, C);
-      float r = y - C;
-#if defined(__HIP_DEVICE_COMPILE__)
-      asm("" : "+v"(r));
-#endif
+      quant_append<BITS>(acc[v], rt, tab, pw, C);
+      const float r = residual(acc[v], rt, C);
       rr = fmaf(r, r, rr);
       if (v & 1) {
         rodd = r;
