@@ -157,15 +157,16 @@ __device__ __forceinline__ int value_index(float y, const QTab<BITS>& tab) {
 
 // The same index for keys in the transposed layout (one token per lane),
 // of y = x rt (x the rotation output, rt > 0 its token's scale, or 0 for a
-// zero vector, whose x is +0): appends the index's plane bits, inverted,
-// below the bits already in pw[] -- pw[BITS-1] <- the sign bit of x, which
-// is y's (the sign plane is set for it clear), pw[p] <- the sign bit of x
-// XOR that of a rt - t, a = |x|, for the boundary t the magnitude search
-// tested for plane p (set for [|y| >= t] XNOR [y's sign bit clear]).  Each
-// a rt - t is one fma, never -0 or NaN for finite inputs (the exact
-// difference is 0 or far above the smallest denormal), so its sign bit is
-// exactly |y| < t, the compare value_index makes.  Returns the signed
-// centroid through C (x's sign, so -0.0 gives -mag).
+// zero vector, whose x is +0): appends one bit per plane below the bits
+// already in pw[] -- pw[BITS-1] <- the sign bit of x, which is y's (the
+// sign plane, inverted: set for y's sign bit clear), pw[p] <- the sign bit
+// of a rt - t, a = |x|, for the boundary t the magnitude search tested for
+// plane p.  The inverted plane bit is that XOR the sign bit of x (set for
+// [|y| >= t] XNOR [y's sign bit clear]); code_words applies the XOR to
+// whole words.  Each a rt - t is one fma, never -0 or NaN for finite inputs
+// (the exact difference is 0 or far above the smallest denormal), so its
+// sign bit is exactly |y| < t, the compare value_index makes.  Returns the
+// signed centroid through C (x's sign, so -0.0 gives -mag).
 template <int BITS>
 __device__ __forceinline__ void quant_append(float x, float rt, const QTab<BITS>& tab, uint32_t* pw, float& C) {
   const uint32_t yb = __float_as_uint(x);
@@ -177,15 +178,15 @@ __device__ __forceinline__ void quant_append(float x, float rt, const QTab<BITS>
     mag = tab.cpos[0];
   } else if constexpr (BITS == 2) {
     const float d1 = fmaf(a, rt, -tab.tpos[0]);
-    push(0, yb ^ __float_as_uint(d1));
+    push(0, __float_as_uint(d1));
     mag = sel(d1 >= 0.f, tab.cpos[1], tab.cpos[0]);
   } else if constexpr (BITS == 3) {
     const float d1 = fmaf(a, rt, -tab.tpos[1]);
     const bool m1 = d1 >= 0.f;
     const float d2 = fmaf(a, rt, -sel(m1, tab.tpos[2], tab.tpos[0]));
     const bool m2 = d2 >= 0.f;
-    push(1, yb ^ __float_as_uint(d1));
-    push(0, yb ^ __float_as_uint(d2));
+    push(1, __float_as_uint(d1));
+    push(0, __float_as_uint(d2));
     mag = sel(m1, sel(m2, tab.cpos[3], tab.cpos[2]), sel(m2, tab.cpos[1], tab.cpos[0]));
   } else {
     const float d1 = fmaf(a, rt, -tab.tpos[3]);
@@ -194,9 +195,9 @@ __device__ __forceinline__ void quant_append(float x, float rt, const QTab<BITS>
     const bool m2 = d2 >= 0.f;
     const float d3 = fmaf(a, rt, -sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0])));
     const bool m3 = d3 >= 0.f;
-    push(2, yb ^ __float_as_uint(d1));
-    push(1, yb ^ __float_as_uint(d2));
-    push(0, yb ^ __float_as_uint(d3));
+    push(2, __float_as_uint(d1));
+    push(1, __float_as_uint(d2));
+    push(0, __float_as_uint(d3));
     const float lo4 = sel(m2, sel(m3, tab.cpos[3], tab.cpos[2]), sel(m3, tab.cpos[1], tab.cpos[0]));
     const float hi4 = sel(m2, sel(m3, tab.cpos[7], tab.cpos[6]), sel(m3, tab.cpos[5], tab.cpos[4]));
     mag = sel(m1, hi4, lo4);
@@ -217,6 +218,19 @@ __device__ __forceinline__ float residual(float x, float rt, float C) {
 #else
   return fmaf(x, rt, -C);
 #endif
+}
+
+// The code-plane words of the lane's token from quant_append's bits (16
+// coordinates per lane half): each lower plane XOR the sign plane, lane half
+// 0 taking half 1's 16 bits on top, the inversion undone.
+template <int B>
+__device__ __forceinline__ void code_words(const uint32_t (&pw)[B], uint32_t (&cw)[B]) {
+#pragma unroll
+  for (int p = 0; p < B; ++p) {
+    const uint32_t w = p + 1 < B ? pw[p] ^ pw[B - 1] : pw[p];
+    const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(w), 32, 64));
+    cw[p] = ~((w & 0xFFFFu) | (o << 16));
+  }
 }
 
 template <typename XT>
@@ -573,13 +587,9 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
         dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
       }
-      // code words of token c32: lane half 0 takes half 1's 16 bits on top
+      // code words of token c32
       uint32_t cw[WB];
-#pragma unroll
-      for (int p = 0; p < WB; ++p) {
-        const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(pw[p]), 32, 64));
-        cw[p] = ~((pw[p] & 0xFFFFu) | (o << 16));
-      }
+      code_words<WB>(pw, cw);
       // ||r||^2 over this wave's 32 coordinates
       const float rr32 = rr + __shfl_xor(rr, 32, 64);
       if (h == 0) {
@@ -975,11 +985,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
       dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
     }
     uint32_t cw[BITS];
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) {
-      const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(pw[p]), 32, 64));
-      cw[p] = ~((pw[p] & 0xFFFFu) | (o << 16));
-    }
+    code_words<BITS>(pw, cw);
     const float rr32 = rr + __shfl_xor(rr, 32, 64);
     // codes and ||r||^2 share of unit i
     if (h == 0) {
