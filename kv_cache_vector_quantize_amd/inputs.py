@@ -81,8 +81,8 @@ WORKLOADS = {
                 quantize_timed=False),
     # Inner-product search (the pages' second workload: GloVe vectors, d = 200,
     # judged by top-k recall), as a synthetic stand-in at the pages' dimension:
-    # one database of 2^20 keys (3 bits: 2-bit codes + QJL with m = d = 200
-    # sketch rows), 8 queries per call, top 10.
+    # one database of 2^20 keys (3-bit codes + QJL with m = d = 200 sketch
+    # rows), 8 queries per call, top 10.
     6: Workload("search_d200_N1M_q8_top10", 6, B=1, Hq=8, Hkv=1, T=1048576, d=200, m=200, k_bits=3,
                 logits=True, quantize_timed=False, topk=10),
 }
