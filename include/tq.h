@@ -106,8 +106,10 @@ typedef enum {
 
 /* Data-independent tables of one stream (device memory, caller-owned). */
 typedef struct {
-  int32_t d;               /* head dimension; the hot-path kernels support 128   */
-  int32_t m;               /* sketch rows: 128 for keys, 0 for values             */
+  int32_t d;               /* head dimension: 128 on every path; 8..256 for      */
+                           /* quantize and logits (padded to 32-bit words)        */
+  int32_t m;               /* sketch rows of keys (128 at d = 128, <= 256 else);  */
+                           /* 0 for values                                         */
   int32_t bits;            /* code width, 1..4                                    */
   int32_t rot_kind;        /* tq_rotation_kind of rot                             */
   const float *rot;        /* Pi, d x d row-major; y = Pi x                       */
@@ -199,8 +201,9 @@ tq_status tq_hadamard_rotation(int d, const float *signs, float *rot32, hipStrea
  *   t      tables of the stream (t->m > 0 for keys, 0 for values)
  *   x      in, [out->nseq][out->T][d] of x_dtype (TQ_F32 or TQ_BF16)
  *   out    packed stream to write; role, bits, d, m, hi_coords must match t
- * Split streams (hi_coords = d/2) take bits 1..3 and a dense rotation
- * (TQ_EUNSUPPORTED otherwise).
+ * d = 128 with m = 128 (keys) runs on the matrix cores; other d in 8..256 and
+ * m <= 256 on the vector ALU.  Split streams (hi_coords = d/2) take d = 128,
+ * bits 1..3 and a dense rotation (TQ_EUNSUPPORTED otherwise).
  */
 tq_status tq_quantize(const tq_tables *t, const void *x, int x_dtype, const tq_packed *out,
                       hipStream_t stream);
@@ -223,6 +226,7 @@ tq_status tq_quantize(const tq_tables *t, const void *x, int x_dtype, const tq_p
  * place).  After the call the stream equals, bit for bit, tq_quantize of all
  * T+n tokens at the same capacity.  out->T is the caller's to advance: pass
  * T+n to later calls.  Calls that write one stream must not overlap.
+ * d = 128 (and m = 128 for keys) only (TQ_EUNSUPPORTED otherwise).
  */
 tq_status tq_append(const tq_tables *t, const void *x, int x_dtype, int64_t n, const tq_packed *out,
                     hipStream_t stream);
@@ -243,7 +247,9 @@ size_t tq_logits_workspace(int B, int Hq, int d, int m);
  *   ws       workspace of at least tq_logits_workspace(B, Hq, d, m) bytes
  * Hq/Hkv must be 1, 2, 4, 8 or 16 (else TQ_EUNSUPPORTED); T < 2^28 and
  * B*Hkv <= 65535 (else TQ_EUNSUPPORTED).  A split key stream (hi_coords =
- * d/2) takes bits 2 or 3 and Hq/Hkv <= 8.
+ * d/2) takes bits 2 or 3 and Hq/Hkv <= 8.  Head dimensions other than 128
+ * (d <= 256, m <= 256) run on the same matrix-core tiles in two passes of
+ * 128 coordinates for Hq/Hkv <= 8, on the vector ALU for 16.
  */
 tq_status tq_attn_logits(const tq_tables *tk, const void *q, int q_dtype, int B, int Hq, int Hkv,
                          const tq_packed *k, float *logits, void *ws, size_t ws_bytes,
@@ -266,8 +272,8 @@ size_t tq_decode_workspace(int B, int Hq, int Hkv, int64_t T, int d, int m);
  *   scale    softmax scale, > 0 (1/sqrt(d) for standard attention)
  *   out      out, [B][Hq][d] float32
  *   ws       workspace of at least tq_decode_workspace(B, Hq, Hkv, T, d, m) bytes
- * Hq/Hkv must be 1, 2, 4 or 8, T < 2^28 and B*Hkv <= 65535 (else
- * TQ_EUNSUPPORTED).  Key and value norms may be stored as float16 or float32
+ * d = 128 with m = 128, Hq/Hkv 1, 2, 4 or 8, T < 2^28 and B*Hkv <= 65535
+ * (else TQ_EUNSUPPORTED).  Key and value norms may be stored as float16 or float32
  * independently.  Split streams (hi_coords = d/2: 2.5 / 3.5-bit keys or
  * values) are decoded when both streams are split, with bits 2 or 3 each and
  * float16 norms (else TQ_EUNSUPPORTED).  Logits carry float32-grade accuracy (float16 hi/lo operand
