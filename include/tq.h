@@ -248,7 +248,7 @@ size_t tq_logits_workspace(int B, int Hq, int d, int m);
  * Hq/Hkv must be 1, 2, 4, 8 or 16 (else TQ_EUNSUPPORTED); T < 2^28 and
  * B*Hkv <= 65535 (else TQ_EUNSUPPORTED).  A split key stream (hi_coords =
  * d/2) takes bits 2 or 3 and Hq/Hkv <= 8.  Head dimensions other than 128
- * (d <= 256, m <= 256) run on the same matrix-core tiles in two passes of
+ * (d <= 256, m <= 256) run on the same matrix-core tiles in one or two passes of
  * 128 coordinates for Hq/Hkv <= 8, on the vector ALU for 16.
  */
 tq_status tq_attn_logits(const tq_tables *tk, const void *q, int q_dtype, int B, int Hq, int Hkv,
