@@ -192,6 +192,41 @@ __device__ __forceinline__ floatx4 key2x_kstep(uint32_t Ql, uint32_t Q2l, uint32
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x0, x1, x2, x3), b, acc, 0, 0, 0);
 }
 
+// byte K of x times 8, in one instruction (a byte-select operand shifted)
+template <int K>
+__device__ __forceinline__ uint32_t byte_shl3(uint32_t x) {
+  uint32_t r = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (K == 0)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "s"(3u), "v"(x));
+  else if constexpr (K == 1)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "s"(3u), "v"(x));
+  else if constexpr (K == 2)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "s"(3u), "v"(x));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "s"(3u), "v"(x));
+#else
+  r = ((x >> (8 * K)) & 0xFFu) << 3;
+#endif
+  return r;
+}
+
+// centroid K-step C of a 3- or 4-bit tile from the pair table (entry x:
+// uint2 at 8x): byte C/2 of E / O is the pair index of coordinates
+// (4C, 4C+1) / (4C+2, 4C+3) -- E and O are the words of the low nibbles for
+// even C, of the high nibbles for odd C (tile_accumulate)
+template <int C>
+__device__ __forceinline__ floatx4 key3_kstep(uint32_t E, uint32_t O, const char* tab, const half8& b,
+                                              floatx4 acc) {
+  const uint2 x = *reinterpret_cast<const uint2*>(tab + byte_shl3<C / 2>(E));
+  const uint2 y = *reinterpret_cast<const uint2*>(tab + byte_shl3<C / 2>(O));
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(u4_to_h8(x.x, x.y, y.x, y.y), b, acc, 0, 0, 0);
+}
+
 // sign K-step C: byte C of the sign word sw; sws = sw << 4
 template <int C>
 __device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const char* tab, const half8& b,
@@ -249,6 +284,45 @@ __device__ __forceinline__ void tile_accumulate(const uint32_t* pw, uint32_t sw,
     accC = key2_kstep<5>(Q, Q2, Qs, Q2s, tab, bq[5], accC);
     accC = key2_kstep<6>(Q, Q2, Qs, Q2s, tab, bq[6], accC);
     accC = key2_kstep<7>(Q, Q2, Qs, Q2s, tab, bq[7], accC);
+  } else if constexpr (KB == 4) {
+    // pair indices (8 bits: 2 per plane) one per byte: the nibbles of planes
+    // 0-1 (A, B) below those of planes 2-3 (C, D), as for 3-bit keys below
+    const uint32_t A = ((pw[1] << 2) & 0xCCCCCCCCu) | (pw[0] & 0x33333333u);
+    const uint32_t B = (pw[1] & 0xCCCCCCCCu) | ((pw[0] >> 2) & 0x33333333u);
+    const uint32_t C = ((pw[3] << 2) & 0xCCCCCCCCu) | (pw[2] & 0x33333333u);
+    const uint32_t D = (pw[3] & 0xCCCCCCCCu) | ((pw[2] >> 2) & 0x33333333u);
+    const uint32_t E0 = (A & 0x0F0F0F0Fu) | ((C << 4) & 0xF0F0F0F0u);
+    const uint32_t E1 = ((A >> 4) & 0x0F0F0F0Fu) | (C & 0xF0F0F0F0u);
+    const uint32_t O0 = (B & 0x0F0F0F0Fu) | ((D << 4) & 0xF0F0F0F0u);
+    const uint32_t O1 = ((B >> 4) & 0x0F0F0F0Fu) | (D & 0xF0F0F0F0u);
+    accC = key3_kstep<0>(E0, O0, tab, bq[0], accC);
+    accC = key3_kstep<1>(E1, O1, tab, bq[1], accC);
+    accC = key3_kstep<2>(E0, O0, tab, bq[2], accC);
+    accC = key3_kstep<3>(E1, O1, tab, bq[3], accC);
+    accC = key3_kstep<4>(E0, O0, tab, bq[4], accC);
+    accC = key3_kstep<5>(E1, O1, tab, bq[5], accC);
+    accC = key3_kstep<6>(E0, O0, tab, bq[6], accC);
+    accC = key3_kstep<7>(E1, O1, tab, bq[7], accC);
+  } else if constexpr (KB == 3) {
+    // pair indices (6 bits: 2 per plane) repacked one per byte.  Nibble c of
+    // A / B holds planes 0 and 1 of the pair (4c, 4c+1) / (4c+2, 4c+3) (as
+    // for 2-bit keys); the 4 words below put each pair's plane-2 bits above
+    // its nibble, so that byte K of E0 / E1 is the index of pair 4c (c = 2K /
+    // 2K+1) and byte K of O0 / O1 that of pair 4c+2.
+    const uint32_t A = ((pw[1] << 2) & 0xCCCCCCCCu) | (pw[0] & 0x33333333u);
+    const uint32_t B = (pw[1] & 0xCCCCCCCCu) | ((pw[0] >> 2) & 0x33333333u);
+    const uint32_t E0 = (A & 0x0F0F0F0Fu) | ((pw[2] << 4) & 0x30303030u);
+    const uint32_t E1 = ((A >> 4) & 0x0F0F0F0Fu) | (pw[2] & 0x30303030u);
+    const uint32_t O0 = (B & 0x0F0F0F0Fu) | ((pw[2] << 2) & 0x30303030u);
+    const uint32_t O1 = ((B >> 4) & 0x0F0F0F0Fu) | ((pw[2] >> 2) & 0x30303030u);
+    accC = key3_kstep<0>(E0, O0, tab, bq[0], accC);
+    accC = key3_kstep<1>(E1, O1, tab, bq[1], accC);
+    accC = key3_kstep<2>(E0, O0, tab, bq[2], accC);
+    accC = key3_kstep<3>(E1, O1, tab, bq[3], accC);
+    accC = key3_kstep<4>(E0, O0, tab, bq[4], accC);
+    accC = key3_kstep<5>(E1, O1, tab, bq[5], accC);
+    accC = key3_kstep<6>(E0, O0, tab, bq[6], accC);
+    accC = key3_kstep<7>(E1, O1, tab, bq[7], accC);
   } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
