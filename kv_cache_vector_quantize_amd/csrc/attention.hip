@@ -19,11 +19,20 @@ constexpr int kAM = 128;
 
 // ------------------------------------------------------------- query prep
 // One workgroup per query head: q' = Pi q, then (keys with a sketch) u = S q'.
-// Thread t owns half a row of each matrix (row t/2, columns 64 (t%2) ..
-// +63) in registers, loaded up front for both matrices so that the whole
-// kernel waits for memory once; the two halves of a row meet by a lane
-// shuffle.  The vectors are read from LDS as broadcasts.
+// Eight threads share a row: thread t takes rows t/8 + 32p (p = 0..3) and of
+// each the float4 columns t%8 + 8k (k = 0..3), so that the 8 lanes of a row
+// read 128 contiguous bytes per load and a wave touches 8 cache lines per
+// load.  All of both matrices' loads are issued up front (the kernel waits
+// for memory once); the vectors come from LDS, the same four float4 for
+// every row of a thread; three DPP adds sum a row's eighths.
 constexpr int kQThreadsP = 2 * kAD;
+
+__device__ __forceinline__ float sum_eighths(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));
+  return v;
+}
 
 template <typename QT>
 __global__ __launch_bounds__(kQThreadsP) void qprep_kernel(const float* __restrict__ rot,
@@ -31,41 +40,62 @@ __global__ __launch_bounds__(kQThreadsP) void qprep_kernel(const float* __restri
                                                            const QT* __restrict__ q,
                                                            float* __restrict__ qr,
                                                            float* __restrict__ u) {
-  __shared__ float xs[kAD], ys[kAD];
+  __shared__ __align__(16) float xs[kAD], ys[kAD];
   const int64_t h = blockIdx.x;
-  const int tid = threadIdx.x, row = tid >> 1, c0 = 64 * (tid & 1);
+  const int tid = threadIdx.x, r0 = tid >> 3, j = tid & 7;
   const bool sk = m > 0;                    // m is 0 or kAM (checked on the host)
-  float4 pr[16], sr[16];
-  const float4* prow = reinterpret_cast<const float4*>(rot + row * kAD + c0);
+  float4 pr[4][4], sr[4][4];                // [row p][float4 k]
 #pragma unroll
-  for (int i = 0; i < 16; ++i) pr[i] = prow[i];
+  for (int p = 0; p < 4; ++p) {
+    const float4* prow = reinterpret_cast<const float4*>(rot + (r0 + 32 * p) * kAD);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pr[p][k] = prow[j + 8 * k];
+  }
   if (sk) {
-    const float4* srow = reinterpret_cast<const float4*>(sketch + row * kAD + c0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sr[i] = srow[i];
+    for (int p = 0; p < 4; ++p) {
+      const float4* srow = reinterpret_cast<const float4*>(sketch + (r0 + 32 * p) * kAD);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sr[p][k] = srow[j + 8 * k];
+    }
   }
   if (tid < kAD) xs[tid] = load_elem(q, h * kAD + tid);
   __syncthreads();
-  auto dot64 = [&](const float4 (&w)[16], const float* v) {
-    float a = 0.f;
+  // rows r0 + 32p of W v, every lane of the row's eight holding the sum
+  auto dots = [&](const float4 (&w)[4][4], const float* v, float (&out)[4]) {
+    float4 vv[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      a = fmaf(w[i].x, v[c0 + 4 * i], a);
-      a = fmaf(w[i].y, v[c0 + 4 * i + 1], a);
-      a = fmaf(w[i].z, v[c0 + 4 * i + 2], a);
-      a = fmaf(w[i].w, v[c0 + 4 * i + 3], a);
+    for (int k = 0; k < 4; ++k) vv[k] = reinterpret_cast<const float4*>(v)[j + 8 * k];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float a = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a = fmaf(w[p][k].x, vv[k].x, a);
+        a = fmaf(w[p][k].y, vv[k].y, a);
+        a = fmaf(w[p][k].z, vv[k].z, a);
+        a = fmaf(w[p][k].w, vv[k].w, a);
+      }
+      out[p] = sum_eighths(a);
     }
-    return a + __shfl_xor(a, 1);
   };
-  const float y = dot64(pr, xs);
-  if ((tid & 1) == 0) {
-    ys[row] = y;
-    qr[h * kAD + row] = y;
+  float y[4];
+  dots(pr, xs, y);
+  if (j == 0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      ys[r0 + 32 * p] = y[p];
+      qr[h * kAD + r0 + 32 * p] = y[p];
+    }
   }
   if (sk) {
     __syncthreads();
-    const float z = dot64(sr, ys);
-    if ((tid & 1) == 0) u[h * kAM + row] = z;
+    float z[4];
+    dots(sr, ys, z);
+    if (j == 0) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) u[h * kAM + r0 + 32 * p] = z[p];
+    }
   }
 }
 

@@ -72,6 +72,30 @@ def test_logits_group_sizes_ragged(G):
     assert ok, (nbad, mx)
 
 
+@pytest.mark.parametrize("B,Hkv,G", [(1, 3, 1), (1, 5, 2), (3, 1, 2)])
+def test_odd_head_counts(B, Hkv, G):
+    """3, 10 and 6 query heads (counts that are not a power of two), 3 and 5
+    KV heads: logits and decode against the oracle."""
+    say("odd head counts", B, Hkv, G)
+    T = 300
+    Hq = G * Hkv
+    K = (torch.randn((B * Hkv, T, D), device="cuda") * 1.5).to(torch.bfloat16).contiguous()
+    V = torch.randn((B * Hkv, T, D), device="cuda").to(torch.bfloat16).contiguous()
+    tk, pk = _keys(K, 2, "f16")
+    tv, pv = _values(V, 3, "f16")
+    q = torch.randn((B, Hq, D), device="cuda")
+    got = tq.tq_attn_logits(tk, q, pk, B, Hq, Hkv)
+    torch.cuda.synchronize()
+    ref = _oracle_logits(to64(q), pk, 2, B, Hq, Hkv)
+    ok, nbad, mx = logits_close(got.cpu().numpy(), ref)
+    assert ok, (nbad, mx)
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv).cpu().numpy()
+    rows = [(b, h) for b in range(B) for h in range(Hq)]
+    ref = _oracle_decode_rows(to64(q), pk, pv, 2, 3, B, Hq, Hkv, rows)
+    ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
+    assert ok, rel
+
+
 @pytest.mark.parametrize("bits,T,nd", [(1, 100, "f16"), (2, 2049, "f16"), (4, 64, "f16"), (3, 333, "f32"),
                                        (2, 4096, "f32")])
 def test_logits_code_widths_and_splits(bits, T, nd):
