@@ -174,13 +174,16 @@ __global__ __launch_bounds__(kGThreads) void quantize_generic_kernel(
 }
 
 // q' = Pi q and u = S q' (float64 sums).  Workgroup (h, rb) computes the
-// whole q' of query head h and rows 32 rb .. 32 rb + 31 of its u: thread
-// (r, part) = (tid / 8, tid % 8) takes row r of a group of 32 rows and the
+// whole q' of query head h and rows 64 rb .. 64 rb + 63 of its u: thread
+// (r, part) = (tid / 8, tid % 8) takes row r of a group of 64 rows and the
 // row's entries part, part + 8, ... (the 8 threads of a row read 32
-// consecutive bytes per load), three shuffles sum the eighths.  Workgroup
+// consecutive bytes per load), three shuffles sum the eighths.  Two groups
+// of 64 rows are loaded per round (two rounds up to d = 256).  Workgroup
 // rb = 0 writes q'.
+constexpr int kQGThreads = 512;
+
 template <typename QT>
-__global__ __launch_bounds__(kGThreads) void qprep_generic_kernel(int d, int m, const float* __restrict__ rot,
+__global__ __launch_bounds__(kQGThreads) void qprep_generic_kernel(int d, int m, const float* __restrict__ rot,
                                                                  const float* __restrict__ sketch,
                                                                  const QT* __restrict__ q, float* __restrict__ qr,
                                                                  float* __restrict__ u) {
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kGThreads) void qprep_generic_kernel(int d, int m, 
   const int64_t h = blockIdx.x;
   const int rb = blockIdx.y;
   const int tid = threadIdx.x, r = tid >> 3, part = tid & 7;
-  for (int k = tid; k < d; k += kGThreads) qs[k] = load_elem<QT>(q, h * d + k);
+  for (int k = tid; k < d; k += kQGThreads) qs[k] = load_elem<QT>(q, h * d + k);
   __syncthreads();
   // every load of a row's eighth is issued before the sums (at most 32 per
   // thread), unconditionally from a clamped index and masked afterwards: a
@@ -214,8 +217,8 @@ __global__ __launch_bounds__(kGThreads) void qprep_generic_kernel(int d, int m, 
     a += __shfl_xor(a, 4, 8);
     return a;
   };
-  for (int j0 = 0; j0 < d; j0 += 64) {   // two groups of 32 rows in flight
-    const int ja = j0 + r, jb = j0 + 32 + r;
+  for (int j0 = 0; j0 < d; j0 += 128) {   // two groups of 64 rows in flight
+    const int ja = j0 + r, jb = j0 + 64 + r;
     float wa[32], wb[32];
     load_part(rot + static_cast<int64_t>(ja < d ? ja : 0) * d, wa);
     load_part(rot + static_cast<int64_t>(jb < d ? jb : 0) * d, wb);
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(kGThreads) void qprep_generic_kernel(int d, int m, 
   }
   if (m == 0) return;   // no sketch (uniform)
   __syncthreads();
-  const int i = 32 * rb + r;
+  const int i = 64 * rb + r;
   float wi[32];
   load_part(sketch + static_cast<int64_t>(i < m ? i : 0) * d, wi);
   const double a = part_dot(wi, qrs);
@@ -319,12 +322,12 @@ hipError_t launch_quantize_generic(const tq_tables& t, const void* x, int x_dtyp
 hipError_t launch_qprep_generic(const tq_tables& tk, const void* q, int q_dtype, int nh, float* qr, float* u,
                                 hipStream_t stream) {
   if (nh == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(nh), static_cast<unsigned>(tk.m > 0 ? (tk.m + 31) / 32 : 1));
+  const dim3 grid(static_cast<unsigned>(nh), static_cast<unsigned>(tk.m > 0 ? (tk.m + 63) / 64 : 1));
   if (q_dtype == TQ_BF16)
-    hipLaunchKernelGGL(qprep_generic_kernel<uint16_t>, grid, dim3(kGThreads), 0, stream, tk.d, tk.m, tk.rot,
+    hipLaunchKernelGGL(qprep_generic_kernel<uint16_t>, grid, dim3(kQGThreads), 0, stream, tk.d, tk.m, tk.rot,
                        tk.sketch, static_cast<const uint16_t*>(q), qr, u);
   else
-    hipLaunchKernelGGL(qprep_generic_kernel<float>, grid, dim3(kGThreads), 0, stream, tk.d, tk.m, tk.rot,
+    hipLaunchKernelGGL(qprep_generic_kernel<float>, grid, dim3(kQGThreads), 0, stream, tk.d, tk.m, tk.rot,
                        tk.sketch, static_cast<const float*>(q), qr, u);
   return hipGetLastError();
 }
