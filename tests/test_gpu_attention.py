@@ -163,6 +163,26 @@ def test_decode_small(G, T):
     assert ok, rel
 
 
+@pytest.mark.parametrize("T,G", [(16000, 1), (20000, 2)])
+def test_decode_many_splits(T, G):
+    """One KV head over a long context: 125 and 157 splits of 128 tokens,
+    merged by the log-sum-exp combine (four groups of splits of uneven
+    length)."""
+    say("decode many splits", T, G)
+    B, Hkv = 1, 1
+    Hq = G * Hkv
+    K = (torch.randn((B * Hkv, T, D), device="cuda") * 1.5).to(torch.bfloat16).contiguous()
+    V = torch.randn((B * Hkv, T, D), device="cuda").to(torch.bfloat16).contiguous()
+    tk, pk = _keys(K, 2, "f16")
+    tv, pv = _values(V, 3, "f16")
+    q = torch.randn((B, Hq, D), device="cuda").to(torch.bfloat16)
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, B, Hq, Hkv).cpu().numpy()
+    rows = [(b, h) for b in range(B) for h in range(Hq)]
+    ref = _oracle_decode_rows(to64(q), pk, pv, 2, 3, B, Hq, Hkv, rows)
+    ok, rel = decode_close(np.stack([got[b, h] for b, h in rows]), np.stack([ref[r] for r in rows]))
+    assert ok, rel
+
+
 @pytest.mark.parametrize("kbits,vbits,knd,vnd,G", [
     (1, 4, "f32", "f32", 4), (3, 1, "f16", "f32", 2), (4, 2, "f32", "f16", 8), (2, 3, "f32", "f16", 1)])
 def test_decode_code_widths_and_norm_dtypes(kbits, vbits, knd, vnd, G):
