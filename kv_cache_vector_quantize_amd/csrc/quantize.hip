@@ -48,6 +48,10 @@ constexpr int kUnit = 32;          // tokens per unit
 constexpr int kRowH = 136;         // LDS row stride in halves (272 B, a multiple of 16 B)
 constexpr float kPiScale = 16.f;   // Pi is held x16 so that its lo half stays normal
 constexpr float kResScale = 256.f; // rotated coordinates are handled x256 (exact)
+// Fourth word of a buffer resource for untyped dword loads (DATA_FORMAT 32,
+// bits 18:15 = 4): with stride 0 the unit checks each byte offset against
+// num_records and returns zeros at or past it.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ uint32_t h2u(qhalf2 h) { return __builtin_bit_cast(uint32_t, h); }
 
@@ -776,31 +780,29 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
 
   const uint32_t g0 = blockIdx.x, gstep = gridDim.x;
   const int n_units = static_cast<int>((units - g0 + gstep - 1) / gstep);   // >= 1 (grid <= units)
+  const uint32_t seq_bytes = static_cast<uint32_t>(T * kD * static_cast<int64_t>(sizeof(XT)));   // < 2^31 (host)
   // first token (sequence * Tp + token) of the workgroup's unit i
   auto unit_base = [&](int i) -> int64_t {
     const uint32_t g = g0 + static_cast<uint32_t>(i) * gstep;
     const uint32_t s = g / nblk, b = g - s * nblk;
     return static_cast<int64_t>(s) * Tp + static_cast<int64_t>(b) * kUnit;
   };
-  // loads of unit i's staging share.  Always issued (from token 0 of a valid
-  // unit for lanes past T or units past the workgroup's last), so that the
-  // waits count a fixed number of loads; `ok` marks the lanes whose data
-  // is real, the others are zeroed when the data is used.
-  auto load_unit = [&](int i, RawX<XT>& raw, bool& ok) {
+  // loads of unit i's staging share, through a buffer resource over the
+  // unit's sequence (T rows; none for a unit past the workgroup's last):
+  // the hardware returns zeros for the rows at or past T, the padding
+  // tokens, which then stage as zero vectors.  Every lane issues the same
+  // loads, so the waits count a fixed number of them.
+  auto load_unit = [&](int i, RawX<XT>& raw) {
     const bool unit_ok = i < n_units;
     const uint32_t g = g0 + static_cast<uint32_t>(unit_ok ? i : 0) * gstep;
     const uint32_t s = g / nblk, b = g - s * nblk;
-    const int64_t t = static_cast<int64_t>(b) * kUnit + sv;
-    ok = unit_ok && t < T;
-    const uint4* src =
-        reinterpret_cast<const uint4*>(x + ((static_cast<int64_t>(s) * T + (ok ? t : 0)) * kD + 16 * sq));
-#pragma unroll
-    for (int r = 0; r < RawX<XT>::kWords; ++r) raw.w[r] = src[r];
-  };
-  auto keep = [&](RawX<XT>& raw, bool ok) {
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<XT*>(x + static_cast<int64_t>(s) * T * kD), 0,
+        unit_ok ? static_cast<int>(seq_bytes) : 0, kBufferWord3);
+    const uint32_t voff = ((b * kUnit + sv) * kD + 16 * sq) * static_cast<uint32_t>(sizeof(XT));
 #pragma unroll
     for (int r = 0; r < RawX<XT>::kWords; ++r)
-      if (!ok) raw.w[r] = make_uint4(0u, 0u, 0u, 0u);
+      raw.w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16 * r, 0, 0));
   };
   constexpr float kRotScale = HAD ? 11.313708498984761f : kPiScale;   // sqrt(128) or 16
   static_assert(kD == 128, "sqrt(kD) above");
@@ -925,24 +927,21 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
 
   constexpr bool kTwoSets = !kSplitX;   // bf16: loads two units ahead
   RawX<XT> rawA, rawB;
-  bool okA, okB;
   // ---- prologue: stage units 0 and 1, loads of units 2 and 3 in flight,
   // rotation of unit 0
-  load_unit(0, rawA, okA);
-  load_unit(1, rawB, okB);
-  keep(rawA, okA);
+  load_unit(0, rawA);
+  load_unit(1, rawB);
   stage(rawA, 0, 0);
-  keep(rawB, okB);
   stage(rawB, 1, 1);
-  load_unit(2, rawA, okA);
-  if constexpr (kTwoSets) load_unit(3, rawB, okB);
+  load_unit(2, rawA);
+  if constexpr (kTwoSets) load_unit(3, rawB);
   __syncthreads();
   qfloatx16 acc, z;
   rotate(0, acc);
 #pragma unroll
   for (int k = 0; k < 16; ++k) z[k] = 0.f;
 
-  auto iteration = [&](int i, RawX<XT>& raw, bool& ok) {
+  auto iteration = [&](int i, RawX<XT>& raw) {
     const int pb = i & 1;
     // ---------------- phase 1: sketch of unit i-1 with the quantization of unit i
     const float rt = rinv_s[i & 3][c32];
@@ -1001,7 +1000,6 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
     for (int v = 15; v >= 0; --v) sw = __builtin_amdgcn_alignbit(sw, __float_as_uint(z[v]), 31);
     const uint32_t so = static_cast<uint32_t>(__shfl_xor(static_cast<int>(sw), 32, 64));
     rotate(pb ^ 1, acc);
-    keep(raw, ok);
     const bool rare = stage_common(raw, (i + 2) & 3, pb);
     if (__builtin_amdgcn_ballot_w64(rare) != 0) stage_general(raw, (i + 2) & 3, pb);
     if (i > 0) {
@@ -1012,23 +1010,23 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
       }
       store_norms(i - 1);
     }
-    if constexpr (kTwoSets) load_unit(i + 4, raw, ok);
-    else load_unit(i + 3, raw, ok);
+    if constexpr (kTwoSets) load_unit(i + 4, raw);
+    else load_unit(i + 3, raw);
     __syncthreads();
   };
 
   int i = 0;
   if constexpr (kTwoSets) {
     for (; i + 1 < n_units; i += 2) {
-      iteration(i, rawA, okA);
-      iteration(i + 1, rawB, okB);
+      iteration(i, rawA);
+      iteration(i + 1, rawB);
     }
     if (i < n_units) {
-      iteration(i, rawA, okA);
+      iteration(i, rawA);
       ++i;
     }
   } else {
-    for (; i < n_units; ++i) iteration(i, rawA, okA);
+    for (; i < n_units; ++i) iteration(i, rawA);
   }
   // ---- epilogue: sketch and signs of the last unit
   {
@@ -1126,8 +1124,11 @@ hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const
   const int64_t nblk = (pos + n + kUnit - 1) / kUnit - pos / kUnit;
   const int64_t units = out.nseq * nblk;
   if (units == 0) return hipSuccess;
-  if (!append && out.role == TQ_KEY && t.hi_coords == 0 && units < (static_cast<int64_t>(1) << 31)) {
-    // whole key streams: the software-pipelined kernel (2 workgroups per CU)
+  const int64_t seq_bytes = out.T * kD * (x_dtype == TQ_BF16 ? 2 : 4);
+  if (!append && out.role == TQ_KEY && t.hi_coords == 0 && units < (static_cast<int64_t>(1) << 31) &&
+      seq_bytes < (static_cast<int64_t>(1) << 31)) {
+    // whole key streams: the software-pipelined kernel (2 workgroups per CU;
+    // its buffer loads take sequences of less than 2^31 bytes)
     const int64_t cap = 2 * static_cast<int64_t>(device_cus());
     const unsigned grid = static_cast<unsigned>(units < cap ? units : cap);
     const bool had = t.rot_kind == TQ_ROT_HADAMARD;
