@@ -780,7 +780,6 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
 
   const uint32_t g0 = blockIdx.x, gstep = gridDim.x;
   const int n_units = static_cast<int>((units - g0 + gstep - 1) / gstep);   // >= 1 (grid <= units)
-  const uint32_t seq_bytes = static_cast<uint32_t>(T * kD * static_cast<int64_t>(sizeof(XT)));   // < 2^31 (host)
   // first token (sequence * Tp + token) of the workgroup's unit i
   auto unit_base = [&](int i) -> int64_t {
     const uint32_t g = g0 + static_cast<uint32_t>(i) * gstep;
@@ -788,18 +787,20 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
     return static_cast<int64_t>(s) * Tp + static_cast<int64_t>(b) * kUnit;
   };
   // loads of unit i's staging share, through a buffer resource over the
-  // unit's sequence (T rows; none for a unit past the workgroup's last):
-  // the hardware returns zeros for the rows at or past T, the padding
-  // tokens, which then stage as zero vectors.  Every lane issues the same
-  // loads, so the waits count a fixed number of them.
+  // unit's rows that exist (none for a unit past the workgroup's last): the
+  // hardware returns zeros for the rows at or past T, the padding tokens,
+  // which then stage as zero vectors.  Every lane issues the same loads, so
+  // the waits count a fixed number of them.
   auto load_unit = [&](int i, RawX<XT>& raw) {
     const bool unit_ok = i < n_units;
     const uint32_t g = g0 + static_cast<uint32_t>(unit_ok ? i : 0) * gstep;
     const uint32_t s = g / nblk, b = g - s * nblk;
+    const int64_t r0 = static_cast<int64_t>(b) * kUnit;
+    const int nrows = !unit_ok ? 0 : (T - r0 < kUnit ? static_cast<int>(T - r0) : kUnit);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<XT*>(x + static_cast<int64_t>(s) * T * kD), 0,
-        unit_ok ? static_cast<int>(seq_bytes) : 0, kBufferWord3);
-    const uint32_t voff = ((b * kUnit + sv) * kD + 16 * sq) * static_cast<uint32_t>(sizeof(XT));
+        const_cast<XT*>(x + (static_cast<int64_t>(s) * T + r0) * kD), 0,
+        nrows * kD * static_cast<int>(sizeof(XT)), kBufferWord3);
+    const uint32_t voff = static_cast<uint32_t>((sv * kD + 16 * sq) * static_cast<int>(sizeof(XT)));
 #pragma unroll
     for (int r = 0; r < RawX<XT>::kWords; ++r)
       raw.w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16 * r, 0, 0));
@@ -1124,11 +1125,8 @@ hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const
   const int64_t nblk = (pos + n + kUnit - 1) / kUnit - pos / kUnit;
   const int64_t units = out.nseq * nblk;
   if (units == 0) return hipSuccess;
-  const int64_t seq_bytes = out.T * kD * (x_dtype == TQ_BF16 ? 2 : 4);
-  if (!append && out.role == TQ_KEY && t.hi_coords == 0 && units < (static_cast<int64_t>(1) << 31) &&
-      seq_bytes < (static_cast<int64_t>(1) << 31)) {
-    // whole key streams: the software-pipelined kernel (2 workgroups per CU;
-    // its buffer loads take sequences of less than 2^31 bytes)
+  if (!append && out.role == TQ_KEY && t.hi_coords == 0 && units < (static_cast<int64_t>(1) << 31)) {
+    // whole key streams: the software-pipelined kernel (2 workgroups per CU)
     const int64_t cap = 2 * static_cast<int64_t>(device_cus());
     const unsigned grid = static_cast<unsigned>(units < cap ? units : cap);
     const bool had = t.rot_kind == TQ_ROT_HADAMARD;
