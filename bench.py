@@ -326,8 +326,8 @@ def _cpu_model():
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3,
                     help="workload number 1-5 (default 3: batched quantize + decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
