@@ -738,13 +738,19 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
 // per-token scales ring over 4 units, so one barrier per unit orders every
 // LDS reuse.  Stores and the (rare) out-of-range rescaling happen between
 // the phases, so that each phase is one straight block of code.
-template <typename XT, int BITS, bool HAD>
+// MIX: a split stream, as in quantize_mfma_kernel: waves 0 and 1
+// (coordinates 0..63) quantize with BITS + 1 planes from the second
+// codebook, and every word keeps its own width in the record.
+template <typename XT, int BITS, bool HAD, bool MIX = false>
 __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
     const float* __restrict__ rot, const float* __restrict__ sketch,
     const float* __restrict__ cent, const float* __restrict__ bnd, const XT* __restrict__ x,
     uint32_t nblk, uint32_t units, int64_t T, int64_t Tp, uint32_t* __restrict__ codes,
     uint32_t* __restrict__ signs, void* __restrict__ norm, void* __restrict__ rnorm,
-    int norm_dtype) {
+    int norm_dtype, const float* __restrict__ cent_hi = nullptr, const float* __restrict__ bnd_hi = nullptr) {
+  static_assert(!MIX || (BITS + 1 <= 4 && !HAD), "split streams: dense rotation, BITS + 1 up to 4");
+  constexpr int BW = MIX ? BITS + 1 : BITS;   // width of the leading coordinates' words
+  constexpr int kKeyRec = MIX ? 4 * BITS + 2 : 4 * BITS;   // record words per token
   constexpr bool kSplitX = sizeof(XT) == 4;
   constexpr int kXP = kSplitX ? 2 : 1;
   __shared__ __align__(16) _Float16 xs[2][kXP][kUnit][kRowH];   // staged input, by unit parity
@@ -764,6 +770,15 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
 #pragma unroll
   for (int i = 0; i + 1 < kHalf; ++i) tab.tpos[i] = bnd[kHalf + i] * kResScale;
   if constexpr (BITS == 1) tab.tpos[0] = 0.f;
+  QTab<BW> tabw;   // the leading coordinates' table (MIX only)
+  if constexpr (MIX) {
+    constexpr int kHalfW = (1 << BW) / 2;
+#pragma unroll
+    for (int i = 0; i < kHalfW; ++i) tabw.cpos[i] = cent_hi[kHalfW + i] * kResScale;
+#pragma unroll
+    for (int i = 0; i + 1 < kHalfW; ++i) tabw.tpos[i] = bnd_hi[kHalfW + i] * kResScale;
+  }
+  const int woff = wave * BITS + (MIX ? (wave < 2 ? wave : 2) : 0);   // this wave's word in a record
 
   // A = Pi rows / S rows, permuted as in quantize_mfma_kernel (keys)
   const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
@@ -946,16 +961,18 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
     const int pb = i & 1;
     // ---------------- phase 1: sketch of unit i-1 with the quantization of unit i
     const float rt = rinv_s[i & 3][c32];
-    uint32_t pw[BITS];
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) pw[p] = 0u;
-    uint32_t hw[8], lw[8];
-    float rr = 0.f, rodd = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) z[k] = 0.f;
+    auto phase1 = [&](auto wc, const auto& tb) {
+    constexpr int WB = decltype(wc)::value;
+    uint32_t pw[WB];
+#pragma unroll
+    for (int p = 0; p < WB; ++p) pw[p] = 0u;
+    uint32_t hw[8], lw[8];
+    float rr = 0.f, rodd = 0.f;
     auto qstep = [&](int v) {
       float C;
-      quant_append<BITS>(acc[v], rt, tab, pw, C);
+      quant_append<WB>(acc[v], rt, tb, pw, C);
       const float r = residual(acc[v], rt, C);
       rr = fmaf(r, r, rr);
       if (v & 1) {
@@ -984,15 +1001,22 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
       dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
     }
-    uint32_t cw[BITS];
-    code_words<BITS>(pw, cw);
+    uint32_t cw[WB];
+    code_words<WB>(pw, cw);
     const float rr32 = rr + __shfl_xor(rr, 32, 64);
     // codes and ||r||^2 share of unit i
     if (h == 0) {
       rho_s[pb][wave][c32] = rr32;
-      uint32_t* dst = codes + ((unit_base(i) + c32) * 4 + wave) * BITS;
+      uint32_t* dst = codes + (unit_base(i) + c32) * kKeyRec + woff;
 #pragma unroll
-      for (int p = 0; p < BITS; ++p) dst[p] = cw[p];
+      for (int p = 0; p < WB; ++p) dst[p] = cw[p];
+    }
+    };
+    if constexpr (MIX) {
+      if (wave < 2) phase1(Width<BW>{}, tabw);   // uniform
+      else phase1(Width<BITS>{}, tab);
+    } else {
+      phase1(Width<BITS>{}, tab);
     }
     // ---------------- phase 2: rotation of unit i+1 with the sign bits of
     // unit i-1 and the staging of unit i+2
@@ -1106,16 +1130,26 @@ static void launch_dtypes(dim3 grid, hipStream_t stream, const tq_tables& t, con
 template <typename XT, bool HAD>
 static void launch_keys_pipe(unsigned grid, hipStream_t stream, const tq_tables& t, const void* x,
                              const tq_packed& out, uint32_t nblk, uint32_t units) {
-#define TQ_QK(B)                                                                                     \
-  hipLaunchKernelGGL((quantize_keys_pipe_kernel<XT, B, HAD>), dim3(grid), dim3(kQThreads), 0, stream, \
-                     t.rot, t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), nblk, units,  \
-                     out.T, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,           \
-                     out.norm_dtype)
+#define TQ_QK(B, MX)                                                                                     \
+  hipLaunchKernelGGL((quantize_keys_pipe_kernel<XT, B, HAD, MX>), dim3(grid), dim3(kQThreads), 0, stream, \
+                     t.rot, t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), nblk, units,      \
+                     out.T, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,               \
+                     out.norm_dtype, t.centroids_hi, t.bounds_hi)
+  if (t.hi_coords != 0) {   // split stream (validated: d/2 leading coordinates, bits 1..3, dense)
+    if constexpr (!HAD) {
+      switch (t.bits) {
+        case 1: TQ_QK(1, true); break;
+        case 2: TQ_QK(2, true); break;
+        default: TQ_QK(3, true); break;
+      }
+    }
+    return;
+  }
   switch (t.bits) {
-    case 1: TQ_QK(1); break;
-    case 2: TQ_QK(2); break;
-    case 3: TQ_QK(3); break;
-    default: TQ_QK(4); break;
+    case 1: TQ_QK(1, false); break;
+    case 2: TQ_QK(2, false); break;
+    case 3: TQ_QK(3, false); break;
+    default: TQ_QK(4, false); break;
   }
 #undef TQ_QK
 }
@@ -1125,7 +1159,7 @@ hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const
   const int64_t nblk = (pos + n + kUnit - 1) / kUnit - pos / kUnit;
   const int64_t units = out.nseq * nblk;
   if (units == 0) return hipSuccess;
-  if (!append && out.role == TQ_KEY && t.hi_coords == 0 && units < (static_cast<int64_t>(1) << 31)) {
+  if (!append && out.role == TQ_KEY && units < (static_cast<int64_t>(1) << 31)) {
     // whole key streams: the software-pipelined kernel (2 workgroups per CU)
     const int64_t cap = 2 * static_cast<int64_t>(device_cus());
     const unsigned grid = static_cast<unsigned>(units < cap ? units : cap);
