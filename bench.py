@@ -403,8 +403,6 @@ def main():
     generic_d = not (d == 128 and m in (0, 128))
     if generic_d:
         kq_kernel = f"quantize_generic_kernel<{w.x_dtype}>"
-    elif hi:
-        kq_kernel = f"quantize_mfma_kernel<{w.x_dtype}, key, {w.k_bits}{rtag}>"
     else:
         kq_kernel = f"quantize_keys_pipe_kernel<{w.x_dtype}, {w.k_bits}{rtag}>"
     if generic_d and G_ <= 8:
@@ -457,7 +455,8 @@ def main():
                          device=dev)
         out = torch.empty((w.B, w.Hq, d), dtype=torch.float32, device=dev)
         stages.append({"name": "decode", "bytes": nvec * (kb + vb) + qbytes + w.B * w.Hq * d * 4,
-                       "units": nvec, "kernel": f"decode_mfma_kernel<{G_}, {w.k_bits}, {w.v_bits}>",
+                       "units": nvec,
+                       "kernel": f"decode_mfma_kernel<{G_}, {w.k_bits}, {w.v_bits}>" + (" (split)" if hi else ""),
                        "fn": lambda: tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv, ws=ws, out=out),
                        "flop_per_unit": 2 * G_ * (2 * d + m)})
     torch.cuda.synchronize()
