@@ -159,3 +159,44 @@ def test_split_decode(kbits, vbits, G, T):
     ref = oracle.decode(to64(q), rs(kidx), rs(ksg), f(kn), f(krn), rs(vidx), f(vn), Pi, S, Ck, Cv)
     ok, rel = decode_close(got.reshape(-1, D), ref.reshape(-1, D))
     assert ok, rel
+
+
+def test_split_full_size_sampled():
+    """The batched workload's shapes (16 x 8 KV heads x 131072 tokens, bf16,
+    2.5-bit keys, 3.5-bit values, fp16 norms), each stream quantized by one
+    tq_quantize as the benchmark's split variant does; three whole sequences
+    of keys and values against the oracle, and the decode rows of their KV
+    heads against the oracle's decode of the GPU's records."""
+    w = inputs.WORKLOADS[3]
+    say("split full size", w.name)
+    kb, vb, nd = w.k_bits, w.v_bits, w.norm_dtype
+    K = inputs.keys(w, device="cuda").reshape(w.nseq, w.T, D)
+    tk, pk = _keys(K, kb, nd)
+    V = inputs.values(w, device="cuda").reshape(w.nseq, w.T, D)
+    tv, pv = _values(V, vb, nd)
+    q = inputs.queries(w, device="cuda").contiguous()
+    got = tq.tq_attn_decode(tk, tv, q, pk, pv, w.B, w.Hq, w.Hkv).cpu().numpy()
+    torch.cuda.synchronize()
+    Pi, S, Ck, Bk = oracle_split(M, kb)
+    Piv, _, Cv, Bv = oracle_split(0, vb)
+    G = w.Hq // w.Hkv
+    qn = to64(q)
+    for s in (0, w.nseq // 2 + 3, w.nseq - 1):
+        say("  sequence", s)
+        kidx = oracle.unpack_key_codes_split(pk.codes[s].cpu().numpy().view(np.uint32), D,
+                                             oracle.split_widths(D, kb, HI)[::32])
+        ksg = oracle.unpack_signs(pk.signs[s].cpu().numpy().view(np.uint32), M)
+        kn, krn = pk.norm[s].cpu().numpy(), pk.rnorm[s].cpu().numpy()
+        rep = check_key_stream(to64(K[s]), kidx, ksg, kn, krn, Pi, S, Ck, Bk, nd)
+        assert rep["ok"], (s, rep)
+        vidx = oracle.unpack_value_codes_split(pv.codes[s:s + 1].cpu().numpy().view(np.uint32), w.T,
+                                               oracle.split_widths(D, vb, HI))
+        vn = pv.norm[s].cpu().numpy()
+        rep = check_value_stream(to64(V[s]), vidx[0], vn, Piv, Cv, Bv, nd)
+        assert rep["ok"], (s, rep)
+        b, kv = divmod(s, w.Hkv)
+        f = lambda a: a.astype(np.float64)[None, None]
+        ref = oracle.decode(qn[b:b + 1, kv * G:(kv + 1) * G], kidx[None, None], ksg[None, None], f(kn), f(krn),
+                            vidx[None], f(vn), Pi, S, Ck, Cv)
+        ok, rel = decode_close(got[b, kv * G:(kv + 1) * G], ref[0])
+        assert ok, (s, rel)
