@@ -243,7 +243,11 @@ __device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const c
 // pw: the tile token's KB plane words of coordinate word g4; sw: its sign
 // word; tab: the LDS tables of build_tables.
 // MX (split streams): pw holds KB planes, the narrow words' top plane zero,
-// and ktab is the lane's own pair table (wide or narrow, generic layout).
+// and ktab is the lane's own pair table (wide or narrow).  Both tables
+// index a pair exactly as the 3- and 4-bit table does (entry x at 8x, the
+// coordinates' plane-p bits at bits 2p and 2p + 1 of x), so 3 and 4 planes
+// take the repacked byte indices below; a narrow lane's zero top plane
+// leaves its indices inside the narrow table.
 // tile_accumulate adds one group of 4 coordinate words to the two
 // accumulators (head dimensions above 128 take two groups), tile_finish
 // folds their hi and lo columns into cen and qj.
@@ -251,7 +255,8 @@ template <int G, int KB, bool X2, bool MX = false>
 __device__ __forceinline__ void tile_accumulate(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
                                                 const half8 (&bu)[4], const char* tab, floatx4& accC,
                                                 floatx4& accS, const char* ktab = nullptr) {
-  if constexpr (MX) {
+  const char* kt = MX ? ktab : tab;   // the key pair table of this lane
+  if constexpr (MX && KB == 2) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint2 x = *reinterpret_cast<const uint2*>(ktab + (pair_index<KB>(pw, 2 * c) << 3));
@@ -295,14 +300,14 @@ __device__ __forceinline__ void tile_accumulate(const uint32_t* pw, uint32_t sw,
     const uint32_t E1 = ((A >> 4) & 0x0F0F0F0Fu) | (C & 0xF0F0F0F0u);
     const uint32_t O0 = (B & 0x0F0F0F0Fu) | ((D << 4) & 0xF0F0F0F0u);
     const uint32_t O1 = ((B >> 4) & 0x0F0F0F0Fu) | (D & 0xF0F0F0F0u);
-    accC = key3_kstep<0>(E0, O0, tab, bq[0], accC);
-    accC = key3_kstep<1>(E1, O1, tab, bq[1], accC);
-    accC = key3_kstep<2>(E0, O0, tab, bq[2], accC);
-    accC = key3_kstep<3>(E1, O1, tab, bq[3], accC);
-    accC = key3_kstep<4>(E0, O0, tab, bq[4], accC);
-    accC = key3_kstep<5>(E1, O1, tab, bq[5], accC);
-    accC = key3_kstep<6>(E0, O0, tab, bq[6], accC);
-    accC = key3_kstep<7>(E1, O1, tab, bq[7], accC);
+    accC = key3_kstep<0>(E0, O0, kt, bq[0], accC);
+    accC = key3_kstep<1>(E1, O1, kt, bq[1], accC);
+    accC = key3_kstep<2>(E0, O0, kt, bq[2], accC);
+    accC = key3_kstep<3>(E1, O1, kt, bq[3], accC);
+    accC = key3_kstep<4>(E0, O0, kt, bq[4], accC);
+    accC = key3_kstep<5>(E1, O1, kt, bq[5], accC);
+    accC = key3_kstep<6>(E0, O0, kt, bq[6], accC);
+    accC = key3_kstep<7>(E1, O1, kt, bq[7], accC);
   } else if constexpr (KB == 3) {
     // pair indices (6 bits: 2 per plane) repacked one per byte.  Nibble c of
     // A / B holds planes 0 and 1 of the pair (4c, 4c+1) / (4c+2, 4c+3) (as
@@ -315,14 +320,14 @@ __device__ __forceinline__ void tile_accumulate(const uint32_t* pw, uint32_t sw,
     const uint32_t E1 = ((A >> 4) & 0x0F0F0F0Fu) | (pw[2] & 0x30303030u);
     const uint32_t O0 = (B & 0x0F0F0F0Fu) | ((pw[2] << 2) & 0x30303030u);
     const uint32_t O1 = ((B >> 4) & 0x0F0F0F0Fu) | ((pw[2] >> 2) & 0x30303030u);
-    accC = key3_kstep<0>(E0, O0, tab, bq[0], accC);
-    accC = key3_kstep<1>(E1, O1, tab, bq[1], accC);
-    accC = key3_kstep<2>(E0, O0, tab, bq[2], accC);
-    accC = key3_kstep<3>(E1, O1, tab, bq[3], accC);
-    accC = key3_kstep<4>(E0, O0, tab, bq[4], accC);
-    accC = key3_kstep<5>(E1, O1, tab, bq[5], accC);
-    accC = key3_kstep<6>(E0, O0, tab, bq[6], accC);
-    accC = key3_kstep<7>(E1, O1, tab, bq[7], accC);
+    accC = key3_kstep<0>(E0, O0, kt, bq[0], accC);
+    accC = key3_kstep<1>(E1, O1, kt, bq[1], accC);
+    accC = key3_kstep<2>(E0, O0, kt, bq[2], accC);
+    accC = key3_kstep<3>(E1, O1, kt, bq[3], accC);
+    accC = key3_kstep<4>(E0, O0, kt, bq[4], accC);
+    accC = key3_kstep<5>(E1, O1, kt, bq[5], accC);
+    accC = key3_kstep<6>(E0, O0, kt, bq[6], accC);
+    accC = key3_kstep<7>(E1, O1, kt, bq[7], accC);
   } else {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
