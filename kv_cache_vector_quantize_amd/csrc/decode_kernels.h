@@ -60,10 +60,18 @@ constexpr float kTau = 8.0f;      // raise the reference max when a block exceed
 constexpr int kSgnOff = 2048, kVluOff = 4096, kTabBytes = kVluOff + 1024;
 // Split streams (MX, fractional widths): coordinates 0..63 take one bit more
 // than 64..127.  The wide key pair table sits at 0 and the wide value table
-// at kVluOff as above; the narrow ones follow the sign table and the wide
-// value table.
+// at kVluOff as above; the narrow ones follow the sign table (keys; right
+// after the wide table for 3-plane wide words, below) and the wide value
+// table.
 constexpr int kNarrowKeyOff = kSgnOff + 256, kNarrowVluOff = kVluOff + 1024;
 constexpr int kTabBytesMix = kNarrowVluOff + 256;
+// With 3-plane wide words (2.5-bit keys) the wide table is 64 entries and
+// the narrow one sits right after it, at entry 64: a narrow lane sets bit 6
+// of its byte indices (kNarrowIndexBit per byte) and reads from the common
+// base, so no lookup adds a per-lane table address.
+template <int KBW>
+constexpr int narrow_key_off() { return KBW == 3 ? 64 * 8 : kNarrowKeyOff; }
+constexpr uint32_t kNarrowIndexBit = 0x40404040u;
 template <bool MX>
 constexpr int tab_bytes() { return MX ? kTabBytesMix : kTabBytes; }
 
@@ -254,8 +262,11 @@ __device__ __forceinline__ floatx4 sign_kstep(uint32_t sw, uint32_t sws, const c
 template <int G, int KB, bool X2, bool MX = false>
 __device__ __forceinline__ void tile_accumulate(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
                                                 const half8 (&bu)[4], const char* tab, floatx4& accC,
-                                                floatx4& accS, const char* ktab = nullptr) {
-  const char* kt = MX ? ktab : tab;   // the key pair table of this lane
+                                                floatx4& accS, const char* ktab = nullptr,
+                                                uint32_t kbias = 0u) {
+  // the key pair table of this lane: 3-plane split keys index both tables
+  // from tab (the narrow lanes' kbias sets bit 6 of each byte index)
+  const char* kt = (MX && KB != 3) ? ktab : tab;
   if constexpr (MX && KB == 2) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -316,10 +327,10 @@ __device__ __forceinline__ void tile_accumulate(const uint32_t* pw, uint32_t sw,
     // 2K+1) and byte K of O0 / O1 that of pair 4c+2.
     const uint32_t A = ((pw[1] << 2) & 0xCCCCCCCCu) | (pw[0] & 0x33333333u);
     const uint32_t B = (pw[1] & 0xCCCCCCCCu) | ((pw[0] >> 2) & 0x33333333u);
-    const uint32_t E0 = (A & 0x0F0F0F0Fu) | ((pw[2] << 4) & 0x30303030u);
-    const uint32_t E1 = ((A >> 4) & 0x0F0F0F0Fu) | (pw[2] & 0x30303030u);
-    const uint32_t O0 = (B & 0x0F0F0F0Fu) | ((pw[2] << 2) & 0x30303030u);
-    const uint32_t O1 = ((B >> 4) & 0x0F0F0F0Fu) | ((pw[2] >> 2) & 0x30303030u);
+    const uint32_t E0 = (A & 0x0F0F0F0Fu) | ((pw[2] << 4) & 0x30303030u) | kbias;
+    const uint32_t E1 = ((A >> 4) & 0x0F0F0F0Fu) | (pw[2] & 0x30303030u) | kbias;
+    const uint32_t O0 = (B & 0x0F0F0F0Fu) | ((pw[2] << 2) & 0x30303030u) | kbias;
+    const uint32_t O1 = ((B >> 4) & 0x0F0F0F0Fu) | ((pw[2] >> 2) & 0x30303030u) | kbias;
     accC = key3_kstep<0>(E0, O0, kt, bq[0], accC);
     accC = key3_kstep<1>(E1, O1, kt, bq[1], accC);
     accC = key3_kstep<2>(E0, O0, kt, bq[2], accC);
@@ -359,9 +370,9 @@ __device__ __forceinline__ void tile_finish(const floatx4& accC, const floatx4& 
 template <int G, int KB, bool X2, bool MX = false>
 __device__ __forceinline__ void tile_logits(const uint32_t* pw, uint32_t sw, const half8 (&bq)[8],
                                             const half8 (&bu)[4], const char* tab, float (&cen)[4],
-                                            float (&qj)[4], const char* ktab = nullptr) {
+                                            float (&qj)[4], const char* ktab = nullptr, uint32_t kbias = 0u) {
   floatx4 accC = {0.f, 0.f, 0.f, 0.f}, accS = {0.f, 0.f, 0.f, 0.f};
-  tile_accumulate<G, KB, X2, MX>(pw, sw, bq, bu, tab, accC, accS, ktab);
+  tile_accumulate<G, KB, X2, MX>(pw, sw, bq, bu, tab, accC, accS, ktab, kbias);
   tile_finish<G>(accC, accS, cen, qj);
 }
 
@@ -514,7 +525,7 @@ __device__ __forceinline__ void build_value_table(const float* __restrict__ cv, 
 }
 
 // Tables of split streams: key pair tables (KB + 1 bits at 0, KB bits at
-// kNarrowKeyOff; the lanes of words 0 and 1 index the first, of words 2 and
+// narrow_key_off<KB + 1>(); the lanes of words 0 and 1 index the first, of words 2 and
 // 3 the second, with a zero top plane), the sign table, and value tables
 // (VB + 1 bits at kVluOff, VB bits at kNarrowVluOff).
 template <int KB, int VB>
@@ -522,7 +533,7 @@ __device__ __forceinline__ void build_tables_mix(const float* __restrict__ ck, c
                                                  const float* __restrict__ cv, const float* __restrict__ cv_hi,
                                                  char* tab, int tid, int nthreads) {
   build_pair_table(ck_hi, KB + 1, tab, tid, nthreads);
-  build_pair_table(ck, KB, tab + kNarrowKeyOff, tid, nthreads);
+  build_pair_table(ck, KB, tab + narrow_key_off<KB + 1>(), tid, nthreads);
   for (int x = tid; x < 16; x += nthreads) {
     auto pm = [&](int i) { return static_cast<_Float16>(((x >> i) & 1) ? 1.f : -1.f); };
     *reinterpret_cast<uint2*>(tab + kSgnOff + 16 * x) = make_uint2(h2u(pm(0), pm(1)), h2u(pm(2), pm(3)));
@@ -917,7 +928,8 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV,
   const uint32_t voff = P::kVC + 4 * (n * VB + vwlo);
   // split streams: lane's key table, and the value record words / shifts of
   // the wide coordinates (0..63, VB + 1 bits) and the narrow ones (VB bits)
-  const char* ktab = lds + ((MX && g4 >= 2) ? kNarrowKeyOff : 0);
+  const char* ktab = lds + ((MX && g4 >= 2) ? narrow_key_off<KB + 1>() : 0);
+  const uint32_t kbias = (MX && KB + 1 == 3 && g4 >= 2) ? kNarrowIndexBit : 0u;   // 2.5-bit keys
   constexpr int VW = MX ? VB + 1 : VB;
   const int vbitW = 8 * VW * g4;
   const uint32_t voffW = P::kVC + 4 * (n * VW + (vbitW >> 5));
@@ -949,7 +961,7 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, VB, NK, NV,
         for (int q = 0; q <= KB; ++q) kw[q] = kp[q];
         if (g4 >= 2) kw[KB] = 0u;
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + 256 * tile);
-        tile_logits<G, KB + 1, false, true>(kw, sw, bq, bu, lds, cen, qj, ktab);
+        tile_logits<G, KB + 1, false, true>(kw, sw, bq, bu, lds, cen, qj, ktab, kbias);
       } else {
         uint32_t kw[KB], sw;
         ring_key_words<KB>(kb, sb, tile, kw, sw);
@@ -1164,7 +1176,8 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0, M
 
   if constexpr (MX) build_tables_mix<KB, 0>(ck, ck_hi, nullptr, nullptr, lds, tid, kDecThreads);
   else build_tables<KB, 0, false>(ck, nullptr, lds, tid, kDecThreads);
-  const char* ktab = lds + ((MX && g4 >= 2) ? kNarrowKeyOff : 0);
+  const char* ktab = lds + ((MX && g4 >= 2) ? narrow_key_off<KB + 1>() : 0);
+  const uint32_t kbias = (MX && KB + 1 == 3 && g4 >= 2) ? kNarrowIndexBit : 0u;   // 2.5-bit keys
   half8 bq[8], bu[4];
   query_frags<G, false>(qr, u, s, lane, 1.f, fu, bq, bu);
   __syncthreads();
@@ -1195,7 +1208,7 @@ __global__ __launch_bounds__(kDecThreads, (ring_occupancy<Packet<KB, 0, NK, 0, M
         for (int q = 0; q <= KB; ++q) kw[q] = kp[q];
         if (g4 >= 2) kw[KB] = 0u;
         const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + 256 * tile);
-        tile_logits<G, KB + 1, false, true>(kw, sw, bq, bu, lds, cen, qj, ktab);
+        tile_logits<G, KB + 1, false, true>(kw, sw, bq, bu, lds, cen, qj, ktab, kbias);
       } else {
         uint32_t kw[KB], sw;
         ring_key_words<KB>(kb, sb, tile, kw, sw);
