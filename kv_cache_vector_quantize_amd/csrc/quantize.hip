@@ -130,33 +130,63 @@ struct QTab {
 // an address and keep the table out of registers)
 __device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
 
-// Index of y (x256 scale) = number of boundaries <= y, for values: the sign
-// of y picks the upper or lower half (its sign bit, so a -0.0, only from a
-// negative product that underflowed, counts as negative like the value it
-// rounds) and a binary search over the positive boundaries the magnitude
-// cell, complemented for y < 0.
+// Index of y (x256 scale) = number of boundaries <= y.  With the codebook
+// symmetric about 0, the index of a y with its sign bit clear is L/2 + m and
+// of one with it set L/2 - 1 - m, m the cell of |y| among the positive
+// boundaries: in bits, the top bit is the inverted sign bit and the lower
+// bits are m, each XOR the sign bit.  (A -0.0, only from a negative product
+// that underflowed, counts as negative like the value it rounds.)
+//
+// Values: appends the raw bits of one token's field below the bits already
+// in w, top bit first -- the sign bit of x, then for each step of the
+// magnitude search the sign bit of a rt - t, a = |x|, t the boundary the
+// step tests (set for |y| < t: the inverted bit of m).  value_fields turns
+// whole words of raw fields into indices.  As in quant_append below, each
+// a rt - t is one fma whose sign bit is exactly the compare.
 template <int BITS>
-__device__ __forceinline__ int value_index(float y, const QTab<BITS>& tab) {
-  const int sgn = static_cast<int>(__float_as_uint(y)) >> 31;   // 0, or -1 for a set sign bit
-  const float a = fabsf(y);
-  int cnt;
-  if constexpr (BITS == 1) {
-    cnt = 0;
-  } else if constexpr (BITS == 2) {
-    cnt = a >= tab.tpos[0] ? 1 : 0;
+__device__ __forceinline__ void value_append(float x, float rt, const QTab<BITS>& tab, uint32_t& w) {
+  auto push = [&](float v) { w = __builtin_amdgcn_alignbit(w, __float_as_uint(v), 31); };
+  const float a = fabsf(x);
+  push(x);
+  if constexpr (BITS == 2) {
+    push(fmaf(a, rt, -tab.tpos[0]));
   } else if constexpr (BITS == 3) {
-    const bool m1 = a >= tab.tpos[1];
-    const bool m2 = a >= sel(m1, tab.tpos[2], tab.tpos[0]);
-    cnt = (m1 ? 2 : 0) + (m2 ? 1 : 0);
-  } else {
-    const bool m1 = a >= tab.tpos[3];
-    const bool m2 = a >= sel(m1, tab.tpos[5], tab.tpos[1]);
-    const float t3 = sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0]));
-    const bool m3 = a >= t3;
-    cnt = (m1 ? 4 : 0) + (m2 ? 2 : 0) + (m3 ? 1 : 0);
+    const float d1 = fmaf(a, rt, -tab.tpos[1]);
+    const float d2 = fmaf(a, rt, -sel(d1 >= 0.f, tab.tpos[2], tab.tpos[0]));
+    push(d1);
+    push(d2);
+  } else if constexpr (BITS == 4) {
+    const float d1 = fmaf(a, rt, -tab.tpos[3]);
+    const bool m1 = d1 >= 0.f;
+    const float d2 = fmaf(a, rt, -sel(m1, tab.tpos[5], tab.tpos[1]));
+    const bool m2 = d2 >= 0.f;
+    const float d3 = fmaf(a, rt, -sel(m1, sel(m2, tab.tpos[6], tab.tpos[4]), sel(m2, tab.tpos[2], tab.tpos[0])));
+    push(d1);
+    push(d2);
+    push(d3);
   }
-  constexpr int half = 1 << (BITS - 1);
-  return (cnt ^ sgn) + half;  // half + cnt, or half - 1 - cnt
+}
+
+// the top bit of each of n fields of `bits` bits
+constexpr uint32_t field_tops(int bits, int n) {
+  uint32_t m = 0u;
+  for (int f = 0; f < n; ++f) m |= 1u << (bits * f + bits - 1);
+  return m;
+}
+
+// Indices from N raw fields of BITS bits at the bottom of r: each field's
+// lower bits XOR its top bit (t - (t >> (BITS-1)) copies every top bit of t
+// into the bits below it in its field), then every field bit inverted.
+template <int BITS, int N>
+__device__ __forceinline__ uint32_t value_fields(uint32_t r) {
+  static_assert(BITS * N <= 32, "one word");
+  constexpr uint32_t kValid = BITS * N == 32 ? 0xFFFFFFFFu : (1u << (BITS * N % 32)) - 1u;
+  if constexpr (BITS == 1) {
+    return r ^ kValid;
+  } else {
+    const uint32_t t = r & field_tops(BITS, N);
+    return r ^ (t - (t >> (BITS - 1))) ^ kValid;
+  }
 }
 
 // The same index for keys in the transposed layout (one token per lane),
@@ -406,8 +436,25 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
   const int64_t step_s = gridDim.x / nblk, step_b = gridDim.x % nblk;
   int64_t s = blockIdx.x / nblk, blk = blockIdx.x % nblk;
 
+  const uint32_t voff = static_cast<uint32_t>((sv * kD + 16 * sq) * static_cast<int>(sizeof(XT)));
   auto load_raw = [&](int64_t us, int64_t ub, RawX<XT>& raw) {
-    const int64_t t = (blk0 + ub) * kUnit + sv;
+    const int64_t tb = (blk0 + ub) * kUnit;
+    if (us < nseq && tb >= pos && tb + kUnit <= T) {
+      // the whole unit is input (the condition is the same for every thread):
+      // buffer loads from one resource for the workgroup (a form of their
+      // own, which keeps the per-thread checks and zero fill below off this
+      // path)
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<XT*>(x + (us * nx + tb - pos) * kD), 0, kUnit * kD * static_cast<int>(sizeof(XT)),
+          kBufferWord3);
+#pragma unroll
+      for (int r = 0; r < RawX<XT>::kWords; ++r)
+        raw.w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16 * r, 0, 0));
+      return;
+    }
+    // a unit at the ends of the input: each thread loads its own token if
+    // it is input, else zeros
+    const int64_t t = tb + sv;
     if (us < nseq && t >= pos && t < T) {
       const uint4* src = reinterpret_cast<const uint4*>(x + ((us * nx + t - pos) * kD + 16 * sq));
 #pragma unroll
@@ -451,8 +498,12 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     }
   };
 
-  int par = 0;
-  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x, par ^= 1) {
+  // One unit of work.  par, the unit's parity (a constant per call), picks
+  // the LDS buffers; cur holds the unit's input.  The loop below takes two
+  // units per iteration, so that with two units of input in flight the two
+  // register buffers trade roles rather than being copied.
+  auto unit_step = [&](auto pc, RawX<XT>& cur) {
+    constexpr int par = decltype(pc)::value;
     const int xb = KEY ? 0 : par;
     const int64_t t0 = (blk0 + blk) * kUnit;
     const int nvalid = static_cast<int>((T - t0 < kUnit) ? T - t0 : kUnit);
@@ -461,8 +512,8 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     // ---------------- stage: norms, power-of-two range scale, fp16 copy
     {
       float xv[16];
-      unpack_raw<XT>(raw, xv);
-      float ss = sum8(sumsq16<XT>(raw, xv));
+      unpack_raw<XT>(cur, xv);
+      float ss = sum8(sumsq16<XT>(cur, xv));
       int sh;
       if (ss >= 1.f && ss < 0x1p28f) {
         // ||x|| in [1, 2^14): every element is below 2^14 and those that are
@@ -523,12 +574,10 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     }
     __syncthreads();
     if constexpr (KEY) store_key_norms(par ^ 1);  // the previous unit's
-    if constexpr (kAhead2) {
-      raw = raw_next;
-      load_raw(s2, b2, raw_next);  // the unit after next, in flight during two units' compute
-    } else {
-      load_raw(s1, b1, raw);  // the next unit, in flight during this unit's compute
-    }
+    // cur is free once staged: it takes the unit after next (bf16: in flight
+    // during two units' compute) or the next unit (fp32: during this one's)
+    if constexpr (kAhead2) load_raw(s2, b2, cur);
+    else load_raw(s1, b1, cur);
 
     // ---------------- rotation (x kPiScale, inputs scaled).  Values:
     // acc = X Pi^T, acc[v] = token 16h + v of coordinate 32*wave + c32.
@@ -639,27 +688,31 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     } else {
       // ---------------- quantize (values): acc[v] is token 16h + v of
       // coordinate 32*wave + c32
-      float rv[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 r4 = *reinterpret_cast<const float4*>(&rinv_s[par][16 * h + 4 * q]);
-        rv[4 * q] = r4.x;
-        rv[4 * q + 1] = r4.y;
-        rv[4 * q + 2] = r4.z;
-        rv[4 * q + 3] = r4.w;
-      }
       // the record of coordinate j = 32*wave + c32: WB words, after the
       // records of the coordinates before it
       auto quantize_value_coord = [&](auto wc, const auto& tb) {
       constexpr int WB = decltype(wc)::value;
-      uint32_t vlo = 0, vhi = 0;  // value fields of tokens 16h .. 16h+15 (bits WB*v ..)
+      // value fields of tokens 16h .. 16h+15 at bits WB*v of (vhi:vlo).  The
+      // raw fields are appended top token first, so token v ends at bit WB*v
+      // of its word: one word for WB <= 2; tokens 0..9 and 10..15 for WB = 3
+      // (the word boundary splits token 10), 0..7 and 8..15 for WB = 4.
+      constexpr int kLo = WB <= 2 ? 16 : (WB == 3 ? 10 : 8);
+      // (the tokens' scales are read four at a time as they are needed)
+      uint32_t wl = 0u, wh = 0u;
+      float4 r4;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float y = acc[v] * rv[v];
-        const int sh = WB * v;
-        const uint32_t u = static_cast<uint32_t>(value_index<WB>(y, tb));
-        if (sh < 32) vlo |= u << sh;
-        if (sh + WB > 32) vhi |= (sh < 32) ? (u >> (32 - sh)) : (u << (sh - 32));
+      for (int v = 15; v >= 0; --v) {
+        if (v % 4 == 3) r4 = *reinterpret_cast<const float4*>(&rinv_s[par][16 * h + v - 3]);
+        const float rt = v % 4 == 0 ? r4.x : v % 4 == 1 ? r4.y : v % 4 == 2 ? r4.z : r4.w;
+        value_append<WB>(acc[v], rt, tb, v >= kLo ? wh : wl);
+      }
+      uint32_t vlo = value_fields<WB, kLo>(wl), vhi = 0u;
+      if constexpr (WB == 3) {
+        wh = value_fields<WB, 16 - kLo>(wh);
+        vlo |= wh << 30;
+        vhi = wh >> 2;
+      } else if constexpr (WB == 4) {
+        vhi = value_fields<WB, 16 - kLo>(wh);
       }
       // mask off the fields of padded tokens (zero vectors past the end of T)
       const int nv = nvalid - 16 * h;  // valid tokens of this lane half
@@ -716,10 +769,20 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
     s1 = s2;
     b1 = b2;
     advance(s2, b2);
+  };
+
+  RawX<XT>& raw_odd = kAhead2 ? raw_next : raw;
+  int last = 1;  // parity of the last unit taken (none: 1, whose norms are pending for no token)
+  for (int64_t unit = blockIdx.x; unit < units; unit += 2 * static_cast<int64_t>(gridDim.x)) {
+    unit_step(Width<0>{}, raw);
+    last = 0;
+    if (unit + gridDim.x >= units) break;
+    unit_step(Width<1>{}, raw_odd);
+    last = 1;
   }
   if constexpr (KEY) {
     __syncthreads();
-    store_key_norms(par ^ 1);
+    store_key_norms(last);
   }
 }
 
