@@ -787,6 +787,110 @@ __global__ __launch_bounds__(kQThreads, KEY ? 2 : 3) void quantize_mfma_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Staging of the pipelined kernels: the 8 threads of a token each take 16
+// of its elements (raw), write the fp16 copy (fp32 input: hi and lo) to
+// LDS rows xh / xl at their elements, and the token's norm and rotation
+// scale to n_dst / rinv_dst (every thread of the token writes the same
+// values, so that no branch splits the block).
+//
+// Common path (||x|| in [1, 2^14): no rescaling): returns whether the token
+// needs rescaling.
+template <typename XT, bool HAD>
+__device__ __forceinline__ bool stage_share_common(const RawX<XT>& raw, _Float16* xh, _Float16* xl,
+                                                   float* n_dst, float* rinv_dst) {
+  constexpr bool kSplitX = sizeof(XT) == 4;
+  static_assert(kD == 128, "sqrt(kD) below");
+  constexpr float kRotScale = HAD ? 11.313708498984761f : kPiScale;   // sqrt(128) or 16
+  float xv[16];
+  unpack_raw<XT>(raw, xv);
+  const float ss = sum8(sumsq16<XT>(raw, xv));
+  const float nr = hw_sqrt(ss);
+  *n_dst = nr;
+  *rinv_dst = (ss > 0.f) ? (kResScale / kRotScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
+  uint32_t wh[8], wl[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const qhalf2 hh = {static_cast<_Float16>(xv[2 * e]), static_cast<_Float16>(xv[2 * e + 1])};
+    wh[e] = h2u(hh);
+    if constexpr (kSplitX) {
+      const qhalf2 ll = {static_cast<_Float16>(xv[2 * e] - static_cast<float>(hh[0])),
+                         static_cast<_Float16>(xv[2 * e + 1] - static_cast<float>(hh[1]))};
+      wl[e] = h2u(ll);
+    }
+  }
+  uint4* dh = reinterpret_cast<uint4*>(xh);
+  dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+  dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+  if constexpr (kSplitX) {
+    uint4* dl = reinterpret_cast<uint4*>(xl);
+    dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+  }
+  return !(ss >= 1.f && ss < 0x1p28f);
+}
+
+// Staging of a unit with at least one token outside that range: the general
+// path of quantize_mfma_kernel, for every token (the tokens in range take
+// sh = 0 and rewrite what stage_share_common wrote).
+template <typename XT, bool HAD>
+__device__ __forceinline__ void stage_share_general(const RawX<XT>& raw, _Float16* xh, _Float16* xl,
+                                                    float* n_dst, float* rinv_dst) {
+  constexpr bool kSplitX = sizeof(XT) == 4;
+  constexpr float kRotScale = HAD ? 11.313708498984761f : kPiScale;
+  float xv[16];
+  unpack_raw<XT>(raw, xv);
+  float ss = sum8(sumsq16<XT>(raw, xv));
+  int sh;
+  if (ss >= 1.f && ss < 0x1p28f) {
+    sh = 0;
+  } else if (ss >= 0x1p-100f && ss <= 0x1p100f) {
+    int e;
+    (void)frexpf(ss, &e);
+    sh = 15 - ((e + 1) >> 1);
+    const float f = pow2f(sh);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xv[i] *= f;
+    ss *= f * f;
+  } else {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(xv[i]));
+    mx = max8(mx);
+    int e = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e);
+    sh = 11 - e;
+    ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      xv[i] = ldexpf(xv[i], sh);
+      ss = fmaf(xv[i], xv[i], ss);
+    }
+    ss = sum8(ss);
+  }
+  const float nr = hw_sqrt(ss);
+  *n_dst = ldexpf(nr, -sh);
+  *rinv_dst = (ss > 0.f) ? (kResScale / kRotScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
+  uint32_t wh[8], wl[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const qhalf2 hh = {static_cast<_Float16>(xv[2 * e]), static_cast<_Float16>(xv[2 * e + 1])};
+    wh[e] = h2u(hh);
+    if constexpr (kSplitX) {
+      const qhalf2 ll = {static_cast<_Float16>(xv[2 * e] - static_cast<float>(hh[0])),
+                         static_cast<_Float16>(xv[2 * e + 1] - static_cast<float>(hh[1]))};
+      wl[e] = h2u(ll);
+    }
+  }
+  uint4* dh = reinterpret_cast<uint4*>(xh);
+  dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+  dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+  if constexpr (kSplitX) {
+    uint4* dl = reinterpret_cast<uint4*>(xl);
+    dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+  }
+}
+
 // Keys, whole stream: the same arithmetic as quantize_mfma_kernel, arranged
 // as a software pipeline so that each wave issues matrix-core and vector
 // work of different units side by side.  Iteration i of a workgroup, one
@@ -883,95 +987,13 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
     for (int r = 0; r < RawX<XT>::kWords; ++r)
       raw.w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16 * r, 0, 0));
   };
-  constexpr float kRotScale = HAD ? 11.313708498984761f : kPiScale;   // sqrt(128) or 16
-  static_assert(kD == 128, "sqrt(kD) above");
-  // staging, common path (||x|| in [1, 2^14): no rescaling).  Every lane of
-  // a token writes the token's norm and scale (the same values), so that no
-  // branch splits the block; returns whether the token needs rescaling.
   auto stage_common = [&](const RawX<XT>& raw, int slot, int buf) -> bool {
-    float xv[16];
-    unpack_raw<XT>(raw, xv);
-    const float ss = sum8(sumsq16<XT>(raw, xv));
-    const float nr = hw_sqrt(ss);
-    n_s[slot][sv] = nr;
-    rinv_s[slot][sv] = (ss > 0.f) ? (kResScale / kRotScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
-    uint32_t wh[8], wl[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const qhalf2 hh = {static_cast<_Float16>(xv[2 * e]), static_cast<_Float16>(xv[2 * e + 1])};
-      wh[e] = h2u(hh);
-      if constexpr (kSplitX) {
-        const qhalf2 ll = {static_cast<_Float16>(xv[2 * e] - static_cast<float>(hh[0])),
-                           static_cast<_Float16>(xv[2 * e + 1] - static_cast<float>(hh[1]))};
-        wl[e] = h2u(ll);
-      }
-    }
-    uint4* dh = reinterpret_cast<uint4*>(&xs[buf][0][sv][16 * sq]);
-    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
-    if constexpr (kSplitX) {
-      uint4* dl = reinterpret_cast<uint4*>(&xs[buf][kXP - 1][sv][16 * sq]);
-      dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-      dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
-    }
-    return !(ss >= 1.f && ss < 0x1p28f);
+    return stage_share_common<XT, HAD>(raw, &xs[buf][0][sv][16 * sq], &xs[buf][kXP - 1][sv][16 * sq],
+                                       &n_s[slot][sv], &rinv_s[slot][sv]);
   };
-  // staging of a unit with at least one token outside that range: the
-  // general path of quantize_mfma_kernel, for every token (the tokens in
-  // range take sh = 0 and rewrite what stage_common wrote)
   auto stage_general = [&](const RawX<XT>& raw, int slot, int buf) {
-    float xv[16];
-    unpack_raw<XT>(raw, xv);
-    float ss = sum8(sumsq16<XT>(raw, xv));
-    int sh;
-    if (ss >= 1.f && ss < 0x1p28f) {
-      sh = 0;
-    } else if (ss >= 0x1p-100f && ss <= 0x1p100f) {
-      int e;
-      (void)frexpf(ss, &e);
-      sh = 15 - ((e + 1) >> 1);
-      const float f = pow2f(sh);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xv[i] *= f;
-      ss *= f * f;
-    } else {
-      float mx = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(xv[i]));
-      mx = max8(mx);
-      int e = 0;
-      if (mx > 0.f) (void)frexpf(mx, &e);
-      sh = 11 - e;
-      ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        xv[i] = ldexpf(xv[i], sh);
-        ss = fmaf(xv[i], xv[i], ss);
-      }
-      ss = sum8(ss);
-    }
-    const float nr = hw_sqrt(ss);
-    n_s[slot][sv] = ldexpf(nr, -sh);
-    rinv_s[slot][sv] = (ss > 0.f) ? (kResScale / kRotScale) * __builtin_amdgcn_rcpf(nr) : 0.f;
-    uint32_t wh[8], wl[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const qhalf2 hh = {static_cast<_Float16>(xv[2 * e]), static_cast<_Float16>(xv[2 * e + 1])};
-      wh[e] = h2u(hh);
-      if constexpr (kSplitX) {
-        const qhalf2 ll = {static_cast<_Float16>(xv[2 * e] - static_cast<float>(hh[0])),
-                           static_cast<_Float16>(xv[2 * e + 1] - static_cast<float>(hh[1]))};
-        wl[e] = h2u(ll);
-      }
-    }
-    uint4* dh = reinterpret_cast<uint4*>(&xs[buf][0][sv][16 * sq]);
-    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
-    if constexpr (kSplitX) {
-      uint4* dl = reinterpret_cast<uint4*>(&xs[buf][kXP - 1][sv][16 * sq]);
-      dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-      dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
-    }
+    stage_share_general<XT, HAD>(raw, &xs[buf][0][sv][16 * sq], &xs[buf][kXP - 1][sv][16 * sq],
+                                 &n_s[slot][sv], &rinv_s[slot][sv]);
   };
   auto stage = [&](const RawX<XT>& raw, int slot, int buf) {
     const bool rare = stage_common(raw, slot, buf);
@@ -1017,6 +1039,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
   __syncthreads();
   qfloatx16 acc, z;
   rotate(0, acc);
+  __syncthreads();   // iteration 0 stages unit 2 into the buffer just read
 #pragma unroll
   for (int k = 0; k < 16; ++k) z[k] = 0.f;
 
@@ -1142,6 +1165,204 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
   }
 }
 
+// Values, whole stream: the arithmetic of quantize_mfma_kernel (values) as a
+// software pipeline, in the manner of quantize_keys_pipe_kernel.  Iteration
+// i of a workgroup, one barrier at its end, is one straight block of code:
+// the rotation of unit i+1 (16 MFMAs on its staged input; 8 with the
+// Walsh-Hadamard rotation, 24 for fp32 input) beside the quantization of
+// unit i (the vector ALU on the rotation computed in iteration i-1) and the
+// staging of unit i+2; then the unit's stores, the (rare) out-of-range
+// rescaling and the loads of unit i+4 (fp32: i+3).  Staging is
+// double-buffered by unit parity and the per-token scales ring over 4
+// units, so that one barrier per unit orders every LDS reuse.  It takes
+// about 160 VGPRs: 3 workgroups per CU.  (A split stream keeps the
+// unit-by-unit kernel: with two widths in one workgroup this one would
+// exceed that budget.)
+template <typename XT, int BITS, bool HAD>
+__global__ __launch_bounds__(kQThreads, 3) void quantize_values_pipe_kernel(
+    const float* __restrict__ rot, const float* __restrict__ bnd, const XT* __restrict__ x,
+    uint32_t nblk, uint32_t units, int64_t T, int64_t Tp, uint32_t* __restrict__ codes,
+    void* __restrict__ norm, int norm_dtype) {
+  constexpr int kValRec = kD * BITS;   // record words per block
+  constexpr bool kSplitX = sizeof(XT) == 4;
+  constexpr int kXP = kSplitX ? 2 : 1;
+  __shared__ __align__(16) _Float16 xs[2][kXP][kUnit][kRowH];   // staged input, by unit parity
+  __shared__ __align__(16) float rinv_s[4][kUnit];              // per-token scale, ring of 4 units
+  __shared__ float n_s[4][kUnit];                               // ||x||, ring of 4 units
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c32 = lane & 31, h = lane >> 5;
+  const int sv = tid >> 3, sq = tid & 7;   // staging role: token sv, elements 16 sq ..
+
+  // decision boundaries (x256 scale); values use no centroids
+  QTab<BITS> tab;
+  constexpr int kHalf = (1 << BITS) / 2;
+#pragma unroll
+  for (int i = 0; i + 1 < kHalf; ++i) tab.tpos[i] = bnd[kHalf + i] * kResScale;
+  if constexpr (BITS == 1) tab.tpos[0] = 0.f;
+
+  // acc = X Pi^T: the A rows are tokens, permuted so that output register v
+  // of lane half h is token 16h + v; B = Pi^T, column c32 = coordinate
+  // j = 32*wave + c32, as fp16 hi + lo (or the exact +-1 signs of Pi_H)
+  const int atok = 16 * ((c32 >> 2) & 1) + 4 * (c32 >> 3) + (c32 & 3);
+  const int j = 32 * wave + c32;
+  qhalf8 bph[8], bpl[HAD ? 1 : 8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if constexpr (HAD) sign_frag(rot + j * kD + 16 * c + 8 * h, bph[c]);
+    else split_frag(rot + j * kD + 16 * c + 8 * h, kPiScale, bph[c], bpl[c]);
+  }
+  const int joff = j * BITS;   // the record of coordinate j, after those of the coordinates before it
+
+  const uint32_t g0 = blockIdx.x, gstep = gridDim.x;
+  const int n_units = static_cast<int>((units - g0 + gstep - 1) / gstep);   // >= 1 (grid <= units)
+  // sequence and block of the workgroup's unit i
+  auto unit_sb = [&](int i, uint32_t& s, uint32_t& b) {
+    const uint32_t g = g0 + static_cast<uint32_t>(i) * gstep;
+    s = g / nblk;
+    b = g - s * nblk;
+  };
+  // loads of unit i's staging share through a buffer resource over the
+  // unit's rows that exist (none past the workgroup's last unit): the rows
+  // at or past T read as zeros and stage as zero vectors
+  const uint32_t voff = static_cast<uint32_t>((sv * kD + 16 * sq) * static_cast<int>(sizeof(XT)));
+  auto load_unit = [&](int i, RawX<XT>& raw) {
+    const bool unit_ok = i < n_units;
+    uint32_t s, b;
+    unit_sb(unit_ok ? i : 0, s, b);
+    const int64_t r0 = static_cast<int64_t>(b) * kUnit;
+    const int nrows = !unit_ok ? 0 : (T - r0 < kUnit ? static_cast<int>(T - r0) : kUnit);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<XT*>(x + (static_cast<int64_t>(s) * T + r0) * kD), 0,
+        nrows * kD * static_cast<int>(sizeof(XT)), kBufferWord3);
+#pragma unroll
+    for (int r = 0; r < RawX<XT>::kWords; ++r)
+      raw.w[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16 * r, 0, 0));
+  };
+  auto stage_common = [&](const RawX<XT>& raw, int slot, int buf) -> bool {
+    return stage_share_common<XT, HAD>(raw, &xs[buf][0][sv][16 * sq], &xs[buf][kXP - 1][sv][16 * sq],
+                                       &n_s[slot][sv], &rinv_s[slot][sv]);
+  };
+  auto stage_general = [&](const RawX<XT>& raw, int slot, int buf) {
+    stage_share_general<XT, HAD>(raw, &xs[buf][0][sv][16 * sq], &xs[buf][kXP - 1][sv][16 * sq],
+                                 &n_s[slot][sv], &rinv_s[slot][sv]);
+  };
+  // rotation of the unit staged in xs[buf], with hook(c) after K-step c
+  auto rotate = [&](int buf, qfloatx16& acc, auto&& hook) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const qhalf8 xh = *reinterpret_cast<const qhalf8*>(&xs[buf][0][atok][16 * c + 8 * h]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, bph[c], acc, 0, 0, 0);
+      if constexpr (!HAD) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xh, bpl[c], acc, 0, 0, 0);
+      if constexpr (kSplitX) {
+        const qhalf8 xl = *reinterpret_cast<const qhalf8*>(&xs[buf][kXP - 1][atok][16 * c + 8 * h]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(xl, bph[c], acc, 0, 0, 0);
+      }
+      hook(c);
+    }
+  };
+
+  constexpr bool kTwoSets = !kSplitX;   // bf16: loads two units ahead
+  RawX<XT> rawA, rawB;
+  // ---- prologue: stage units 0 and 1, loads of units 2 and 3 in flight,
+  // rotation of unit 0
+  load_unit(0, rawA);
+  load_unit(1, rawB);
+  if (stage_common(rawA, 0, 0)) stage_general(rawA, 0, 0);
+  if (stage_common(rawB, 1, 1)) stage_general(rawB, 1, 1);
+  load_unit(2, rawA);
+  if constexpr (kTwoSets) load_unit(3, rawB);
+  __syncthreads();
+  qfloatx16 accA, accB;
+  rotate(0, accA, [](int) {});
+  __syncthreads();   // iteration 0 stages unit 2 into the buffer just read
+
+  // iteration i: quantize unit i from accq, rotate unit i+1 into accr
+  auto iteration = [&](int i, RawX<XT>& raw, const qfloatx16& accq, qfloatx16& accr) {
+    const int pb = i & 1, slot = i & 3;
+    bool rare = false;
+    auto block = [&](auto wc, const auto& tb, uint32_t& vlo, uint32_t& vhi) {
+      constexpr int WB = decltype(wc)::value;
+      // fields of tokens 16h .. 16h+15 at bits WB*v of (vhi:vlo), appended
+      // top token first: one word for WB <= 2; tokens 0..9 and 10..15 for
+      // WB = 3 (the word boundary splits token 10), 0..7 and 8..15 for WB = 4
+      constexpr int kLo = WB <= 2 ? 16 : (WB == 3 ? 10 : 8);
+      uint32_t wl = 0u, wh = 0u;
+      float4 r4;
+      auto qtoken = [&](int v) {
+        if (v % 4 == 3) r4 = *reinterpret_cast<const float4*>(&rinv_s[slot][16 * h + v - 3]);
+        const float rt = v % 4 == 0 ? r4.x : v % 4 == 1 ? r4.y : v % 4 == 2 ? r4.z : r4.w;
+        value_append<WB>(accq[v], rt, tb, v >= kLo ? wh : wl);
+      };
+      rotate(pb ^ 1, accr, [&](int c) {
+        qtoken(15 - 2 * c);
+        qtoken(14 - 2 * c);
+      });
+      rare = stage_common(raw, (i + 2) & 3, pb);
+      vlo = value_fields<WB, kLo>(wl);
+      vhi = 0u;
+      if constexpr (WB == 3) {
+        wh = value_fields<WB, 16 - kLo>(wh);
+        vlo |= wh << 30;
+        vhi = wh >> 2;
+      } else if constexpr (WB == 4) {
+        vhi = value_fields<WB, 16 - kLo>(wh);
+      }
+    };
+    uint32_t vlo, vhi;
+    block(Width<BITS>{}, tab, vlo, vhi);
+    // stores of unit i: the record words of coordinate j (lane half h holds
+    // record bits [16*WB*h, 16*WB*(h+1))) and the tokens' norms
+    uint32_t s, b;
+    unit_sb(i, s, b);
+    const int64_t r0 = static_cast<int64_t>(b) * kUnit;
+    const int nv = (T - r0 < kUnit ? static_cast<int>(T - r0) : kUnit) - 16 * h;   // valid tokens of the half
+    auto put = [&](auto wc) {
+      constexpr int WB = decltype(wc)::value;
+      if (nv < 16) {   // padding past T: zero fields
+        const int nbits = nv > 0 ? WB * nv : 0;
+        vlo &= nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u);
+        vhi &= nbits <= 32 ? 0u : ((1u << (nbits - 32)) - 1u);
+      }
+      uint32_t* dst = codes + (static_cast<int64_t>(s) * (Tp / kUnit) + b) * kValRec + joff;
+      if constexpr (WB == 1) {
+        const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
+        if (h == 0) dst[0] = vlo | (other << 16);
+      } else if constexpr (WB == 2) {
+        dst[h] = vlo;
+      } else if constexpr (WB == 3) {
+        const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(vlo), 32, 64));
+        if (h == 0) {
+          dst[0] = vlo;
+          dst[1] = vhi | (other << 16);
+        } else {
+          dst[2] = (vlo >> 16) | (vhi << 16);
+        }
+      } else {
+        dst[2 * h] = vlo;
+        dst[2 * h + 1] = vhi;
+      }
+    };
+    put(Width<BITS>{});
+    if (tid < kUnit) store_norm(norm, norm_dtype, static_cast<int64_t>(s) * Tp + r0 + tid, n_s[slot][tid]);
+    if (__builtin_amdgcn_ballot_w64(rare) != 0) stage_general(raw, (i + 2) & 3, pb);
+    if constexpr (kTwoSets) load_unit(i + 4, raw);
+    else load_unit(i + 3, raw);
+    __syncthreads();
+  };
+
+  // two units per loop iteration: the accumulators (and, bf16, the input
+  // buffers) trade roles
+  int i = 0;
+  for (; i + 1 < n_units; i += 2) {
+    iteration(i, rawA, accA, accB);
+    iteration(i + 1, kTwoSets ? rawB : rawA, accB, accA);
+  }
+  if (i < n_units) iteration(i, rawA, accA, accB);
+}
+
 static int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -1217,6 +1438,22 @@ static void launch_keys_pipe(unsigned grid, hipStream_t stream, const tq_tables&
 #undef TQ_QK
 }
 
+template <typename XT, bool HAD>
+static void launch_values_pipe(unsigned grid, hipStream_t stream, const tq_tables& t, const void* x,
+                               const tq_packed& out, uint32_t nblk, uint32_t units) {
+#define TQ_QV(B)                                                                                        \
+  hipLaunchKernelGGL((quantize_values_pipe_kernel<XT, B, HAD>), dim3(grid), dim3(kQThreads), 0, stream,  \
+                     t.rot, t.bounds, static_cast<const XT*>(x), nblk, units, out.T, stream_stride(out), \
+                     out.codes, out.norm, out.norm_dtype)
+  switch (t.bits) {
+    case 1: TQ_QV(1); break;
+    case 2: TQ_QV(2); break;
+    case 3: TQ_QV(3); break;
+    default: TQ_QV(4); break;
+  }
+#undef TQ_QV
+}
+
 hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const tq_packed& out,
                            int64_t pos, int64_t n, bool append, hipStream_t stream) {
   const int64_t nblk = (pos + n + kUnit - 1) / kUnit - pos / kUnit;
@@ -1234,6 +1471,21 @@ hipError_t launch_quantize(const tq_tables& t, const void* x, int x_dtype, const
     } else {
       if (had) launch_keys_pipe<float, true>(grid, stream, t, x, out, nb, nu);
       else launch_keys_pipe<float, false>(grid, stream, t, x, out, nb, nu);
+    }
+    return hipGetLastError();
+  }
+  if (!append && out.role == TQ_VALUE && t.hi_coords == 0 && units < (static_cast<int64_t>(1) << 31)) {
+    // whole value streams of one width: the software-pipelined kernel (3 workgroups per CU)
+    const int64_t cap = 3 * static_cast<int64_t>(device_cus());
+    const unsigned grid = static_cast<unsigned>(units < cap ? units : cap);
+    const bool had = t.rot_kind == TQ_ROT_HADAMARD;
+    const uint32_t nb = static_cast<uint32_t>(nblk), nu = static_cast<uint32_t>(units);
+    if (x_dtype == TQ_BF16) {
+      if (had) launch_values_pipe<uint16_t, true>(grid, stream, t, x, out, nb, nu);
+      else launch_values_pipe<uint16_t, false>(grid, stream, t, x, out, nb, nu);
+    } else {
+      if (had) launch_values_pipe<float, true>(grid, stream, t, x, out, nb, nu);
+      else launch_values_pipe<float, false>(grid, stream, t, x, out, nb, nu);
     }
     return hipGetLastError();
   }
