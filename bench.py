@@ -424,7 +424,8 @@ def main():
             stages.append({"name": "quantize_v", "bytes": nvec * (d * xb + vb), "units": nvec,
                            "fn": lambda: tq.tq_quantize(tv, V, pv),
                            "kernel": (f"quantize_generic_kernel<{w.x_dtype}>" if generic_d
-                                      else f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}{rtag}>"),
+                                      else f"quantize_mfma_kernel<{w.x_dtype}, value, {w.v_bits}{rtag}>" if hi
+                                      else f"quantize_values_pipe_kernel<{w.x_dtype}, {w.v_bits}{rtag}>"),
                            "flop_per_unit": 2 * d * d,
                            "mfma_flop_per_unit": rot_products * 2 * d * d})
     else:
