@@ -394,9 +394,11 @@ def main():
     # quantize kernels reach fp32-grade products on the fp16 matrix cores
     # with hi + lo splits: the rotation takes X Pi_hi + X Pi_lo (one product
     # for the +-1 Walsh-Hadamard matrix), plus x_lo Pi_hi for fp32 input, and
-    # the key sketch R_hi S_hi + R_hi S_lo + R_lo S_hi; "mfma_flop_per_unit"
-    # counts those executed d x d products.
+    # the key sketch R_hi S_hi + R_hi S_lo + R_lo S_hi (R_hi S + R_lo S for a
+    # sketch exact in float16, the tables' flag); "mfma_flop_per_unit" counts
+    # those executed d x d products.
     rot_products = (1 if had else 2) + (1 if w.x_dtype == "f32" else 0)
+    sketch_products = 2 if tk.sketch_f16 else 3
     G_ = w.Hq // w.Hkv
     # head dimensions other than 128: vector-ALU quantize, wide matrix-core
     # logits (one or two passes of 4 coordinate words)
@@ -419,7 +421,7 @@ def main():
                        "fn": lambda: tq.tq_quantize(tk, K, pk),
                        "kernel": kq_kernel,
                        "flop_per_unit": 2 * d * d + 2 * m * d,
-                       "mfma_flop_per_unit": (rot_products + 3) * 2 * d * d})
+                       "mfma_flop_per_unit": (rot_products + sketch_products) * 2 * d * d})
         if w.v_bits:
             stages.append({"name": "quantize_v", "bytes": nvec * (d * xb + vb), "units": nvec,
                            "fn": lambda: tq.tq_quantize(tv, V, pv),

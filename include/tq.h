@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 5
+#define TQ_ABI_VERSION 6
 
 typedef enum {
   TQ_OK = 0,
@@ -120,6 +120,10 @@ typedef struct {
                            /* coordinate at bits) or d/2 (bits + 1/2 per coord)   */
   const float *centroids_hi; /* 2^(bits+1) centroids, NULL when hi_coords == 0    */
   const float *bounds_hi;  /* 2^(bits+1) - 1 boundaries, NULL when hi_coords == 0 */
+  int32_t sketch_f16;      /* 1: the caller promises that every entry of sketch */
+                           /* is exact in float16, and whole key streams then   */
+                           /* compute S r as R_hi S + R_lo S (a lo half of S    */
+                           /* would be ignored); 0: any float32 S.  0 for values */
 } tq_tables;
 
 /* A packed key or value stream of nseq sequences of T tokens (caller-owned). */

@@ -33,6 +33,7 @@ tq_status check_tables(const tq_tables* t, bool key) {
   if (key ? t->m == 0 : t->m != 0) return TQ_EINVAL;
   if (!ok_ptr(t->rot) || !ok_ptr(t->centroids) || !ok_ptr(t->bounds)) return TQ_EINVAL;
   if (key ? !ok_ptr(t->sketch) : t->sketch != nullptr) return TQ_EINVAL;
+  if (t->sketch_f16 != 0 && (t->sketch_f16 != 1 || !key)) return TQ_EINVAL;
   // split (fractional) widths: the leading hi_coords coordinates at bits + 1
   if (t->hi_coords < 0 || t->hi_coords > t->d || t->hi_coords % 32 != 0) return TQ_EINVAL;
   if (t->hi_coords > 0) {

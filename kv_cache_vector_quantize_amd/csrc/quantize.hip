@@ -908,7 +908,7 @@ __device__ __forceinline__ void stage_share_general(const RawX<XT>& raw, _Float1
 // MIX: a split stream, as in quantize_mfma_kernel: waves 0 and 1
 // (coordinates 0..63) quantize with BITS + 1 planes from the second
 // codebook, and every word keeps its own width in the record.
-template <typename XT, int BITS, bool HAD, bool MIX = false>
+template <typename XT, int BITS, bool HAD, bool MIX = false, bool SLO = true>
 __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
     const float* __restrict__ rot, const float* __restrict__ sketch,
     const float* __restrict__ cent, const float* __restrict__ bnd, const XT* __restrict__ x,
@@ -1075,7 +1075,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
       const qhalf8 rl = *reinterpret_cast<const qhalf8*>(&rs[pb ^ 1][1][c32][16 * c + 8 * h]);
       z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rh, z, 0, 0, 0);
       qstep(15 - 2 * c);
-      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsl[c], rh, z, 0, 0, 0);
+      if constexpr (SLO) z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsl[c], rh, z, 0, 0, 0);
       qstep(14 - 2 * c);
       z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rl, z, 0, 0, 0);
     }
@@ -1149,7 +1149,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quantize_keys_pipe_kernel(
       const qhalf8 rh = *reinterpret_cast<const qhalf8*>(&rs[pb][0][c32][16 * c + 8 * h]);
       const qhalf8 rl = *reinterpret_cast<const qhalf8*>(&rs[pb][1][c32][16 * c + 8 * h]);
       z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rh, z, 0, 0, 0);
-      z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsl[c], rh, z, 0, 0, 0);
+      if constexpr (SLO) z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsl[c], rh, z, 0, 0, 0);
       z = __builtin_amdgcn_mfma_f32_32x32x16_f16(bsh[c], rl, z, 0, 0, 0);
     }
     uint32_t sw = 0u;
@@ -1414,11 +1414,19 @@ static void launch_dtypes(dim3 grid, hipStream_t stream, const tq_tables& t, con
 template <typename XT, bool HAD>
 static void launch_keys_pipe(unsigned grid, hipStream_t stream, const tq_tables& t, const void* x,
                              const tq_packed& out, uint32_t nblk, uint32_t units) {
-#define TQ_QK(B, MX)                                                                                     \
-  hipLaunchKernelGGL((quantize_keys_pipe_kernel<XT, B, HAD, MX>), dim3(grid), dim3(kQThreads), 0, stream, \
-                     t.rot, t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), nblk, units,      \
-                     out.T, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,               \
+#define TQ_QK_S(B, MX, SL)                                                                                   \
+  hipLaunchKernelGGL((quantize_keys_pipe_kernel<XT, B, HAD, MX, SL>), dim3(grid), dim3(kQThreads), 0, stream, \
+                     t.rot, t.sketch, t.centroids, t.bounds, static_cast<const XT*>(x), nblk, units,          \
+                     out.T, stream_stride(out), out.codes, out.signs, out.norm, out.rnorm,                   \
                      out.norm_dtype, t.centroids_hi, t.bounds_hi)
+  // a sketch exact in float16 (the caller's promise) drops the S lo product
+#define TQ_QK(B, MX)                \
+  do {                              \
+    if (t.sketch_f16)               \
+      TQ_QK_S(B, MX, false);        \
+    else                            \
+      TQ_QK_S(B, MX, true);         \
+  } while (0)
   if (t.hi_coords != 0) {   // split stream (validated: d/2 leading coordinates, bits 1..3, dense)
     if constexpr (!HAD) {
       switch (t.bits) {
@@ -1436,6 +1444,7 @@ static void launch_keys_pipe(unsigned grid, hipStream_t stream, const tq_tables&
     default: TQ_QK(4, false); break;
   }
 #undef TQ_QK
+#undef TQ_QK_S
 }
 
 template <typename XT, bool HAD>

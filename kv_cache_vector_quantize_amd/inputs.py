@@ -24,10 +24,13 @@ TABLE_SEED = 42
 
 def table_gaussians(d=128, m=128, seed=TABLE_SEED):
     """G (d x d) for the rotation, then S (m x d) for the sketch, drawn in
-    that order from one numpy PCG64 stream; float64."""
+    that order from one numpy PCG64 stream; float64.  The sketch matrix is
+    stored at float16 precision: its draw is rounded once to float16 (a
+    relative change of at most 2^-11 per entry), so that both sides use a
+    matrix that is exact in float16."""
     rng = np.random.default_rng(seed)
     G = rng.standard_normal((d, d))
-    S = rng.standard_normal((m, d)) if m > 0 else None
+    S = rng.standard_normal((m, d)).astype(np.float16).astype(np.float64) if m > 0 else None
     return G, S
 
 

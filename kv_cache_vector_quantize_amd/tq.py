@@ -33,7 +33,8 @@ class Tables(ctypes.Structure):
                 ("rot_kind", ctypes.c_int32), ("rot", ctypes.c_void_p),
                 ("sketch", ctypes.c_void_p), ("centroids", ctypes.c_void_p),
                 ("bounds", ctypes.c_void_p), ("hi_coords", ctypes.c_int32),
-                ("centroids_hi", ctypes.c_void_p), ("bounds_hi", ctypes.c_void_p)]
+                ("centroids_hi", ctypes.c_void_p), ("bounds_hi", ctypes.c_void_p),
+                ("sketch_f16", ctypes.c_int32)]
 
 
 class Packed(ctypes.Structure):
@@ -169,25 +170,28 @@ class StreamTables:
     hi_coords: int = 0
     centroids_hi: Optional[torch.Tensor] = None
     bounds_hi: Optional[torch.Tensor] = None
+    sketch_f16: int = 0
 
     def c_struct(self):
         return Tables(self.d, self.m, self.bits, self.rot_kind, self.rot.data_ptr(),
                       None if self.sketch is None else self.sketch.data_ptr(),
                       self.centroids.data_ptr(), self.bounds.data_ptr(), self.hi_coords,
-                      _dp(self.centroids_hi), _dp(self.bounds_hi))
+                      _dp(self.centroids_hi), _dp(self.bounds_hi), self.sketch_f16)
 
     def coord_bits(self):
         """Bits of every coordinate (bits + 1 for the leading hi_coords)."""
         return [self.bits + 1 if j < self.hi_coords else self.bits for j in range(self.d)]
 
 
-def make_tables(G, S, bits, device="cuda", hadamard_signs=None, hi_coords=0):
+def make_tables(G, S, bits, device="cuda", hadamard_signs=None, hi_coords=0, sketch_f16=None):
     """Rotation from the Gaussian G (numpy/torch float64 [d, d]) -- or, given
     hadamard_signs (d values +-1), the randomized Walsh-Hadamard rotation
     from them (G is then unused) -- sketch S (float64 [m, d] or None) and the
     Lloyd-Max codebook, all built on the device by the library.  hi_coords
     > 0 makes a split (fractional-width) stream: the leading hi_coords
-    rotated coordinates take the (bits+1)-bit codebook, built here too."""
+    rotated coordinates take the (bits+1)-bit codebook, built here too.
+    sketch_f16 (the tables' flag) is, by default, whether every entry of S
+    is exact in float16; False forces the general sketch products."""
     if hadamard_signs is not None:
         sg = torch.as_tensor(hadamard_signs, dtype=torch.float32).to(device)
         rot32, kind = tq_hadamard_rotation(sg), TQ_ROT_HADAMARD
@@ -195,7 +199,10 @@ def make_tables(G, S, bits, device="cuda", hadamard_signs=None, hi_coords=0):
         _, rot32 = tq_rotation(torch.as_tensor(G, dtype=torch.float64).to(device))
         kind = TQ_ROT_DENSE
     d = rot32.shape[0]
-    sk = None if S is None else torch.as_tensor(S, dtype=torch.float64).to(device).float().contiguous()
+    s64 = None if S is None else torch.as_tensor(S, dtype=torch.float64)
+    exact = s64 is not None and bool(torch.equal(s64, s64.to(torch.float16).to(torch.float64)))
+    f16 = exact if sketch_f16 is None else (bool(sketch_f16) and exact)
+    sk = None if s64 is None else s64.to(device).float().contiguous()
     _, _, c32, b32 = tq_codebook(d, bits, device)
     b32 = b32.clone() if b32.numel() else torch.zeros(1, dtype=torch.float32, device=device)
     ch, bh = None, None
@@ -203,7 +210,7 @@ def make_tables(G, S, bits, device="cuda", hadamard_signs=None, hi_coords=0):
         _, _, ch, bh = tq_codebook(d, bits + 1, device)
         bh = bh.clone()
     return StreamTables(d, 0 if sk is None else sk.shape[0], bits, rot32, sk, c32, b32, kind,
-                        hi_coords, ch, bh)
+                        hi_coords, ch, bh, int(f16))
 
 
 @dataclass

@@ -33,7 +33,7 @@ def test_exports_every_declared_function(L):
     assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
-    assert L.tq_abi_version() == 5
+    assert L.tq_abi_version() == 6
 
 
 def test_status_strings(L):
@@ -66,9 +66,9 @@ needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
                                   reason="fake device pointers are only used without a GPU")
 
 
-def _tables(tq, d=128, m=128, bits=2, rot_kind=0, sketch=True, hi=0):
+def _tables(tq, d=128, m=128, bits=2, rot_kind=0, sketch=True, hi=0, sketch_f16=0):
     return tq.Tables(d, m, bits, rot_kind, FAKE, FAKE if sketch else None, FAKE, FAKE, hi,
-                     FAKE if hi else None, FAKE if hi else None)
+                     FAKE if hi else None, FAKE if hi else None, sketch_f16)
 
 
 def _packed(tq, role=0, bits=2, d=128, m=128, nseq=1, T=4, nd=2, cap=0, hi=0):
@@ -114,6 +114,8 @@ def test_quantize_validation(L):
         (_tables(tq), _packed(tq, T=4, cap=48), -1),           # capacity not a multiple of 32
         (_tables(tq), _packed(tq, T=70, cap=64), -1),          # capacity below T
         (_tables(tq), _packed(tq, T=4, cap=-32), -1),
+        (_tables(tq, sketch_f16=2), _packed(tq), -1),          # the float16-sketch flag is 0 or 1
+        (_tables(tq, m=0, sketch=False, sketch_f16=1), _packed(tq, role=1, m=0), -1),  # values have no sketch
     ]
     for t, p, want in cases:
         assert L.tq_quantize(by(t), x, 1, by(p), None) == want, (want,)

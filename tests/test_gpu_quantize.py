@@ -77,6 +77,51 @@ def test_bf16_keys_student_t_ragged(bits):
     assert not torch.any(p.buf_norm[:, 500:]) and not torch.any(p.buf_rnorm[:, 500:])
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+def test_keys_general_sketch(bits):
+    """A sketch that is not exact in float16 takes the three-product sketch
+    (R_hi S_hi + R_hi S_lo + R_lo S_hi): parity with the oracle on that S."""
+    say("quantize keys, sketch not exact in float16", bits)
+    G, _ = inputs.table_gaussians(D, M)
+    S = np.random.default_rng(7).standard_normal((M, D))
+    tabs = tq.make_tables(G, S, bits)
+    assert tabs.sketch_f16 == 0
+    w = inputs.WORKLOADS[2]
+    X = inputs.key_slice(w, 0, 1, device="cuda", T=2000).reshape(2, 1000, D).contiguous()
+    p = tq.alloc_packed(tq.TQ_KEY, tabs, 2, 1000, "f16")
+    tq.tq_quantize(tabs, X, p)
+    torch.cuda.synchronize()
+    Pi = oracle.rotation_from_gaussian(G)
+    c, t = oracle.lloyd_max(D, bits)
+    idx, sg, n, rn = key_records(p)
+    rep = check_key_stream(to64(X).reshape(-1, D), idx.reshape(-1, D), sg.reshape(-1, M), n.reshape(-1),
+                           rn.reshape(-1), Pi, S, c, t, "f16")
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("x_dtype", [torch.bfloat16, torch.float32])
+def test_float16_sketch_flag_gives_the_same_records(x_dtype):
+    """With a sketch exact in float16, the two-product path (tables flag set)
+    writes the records of the three-product one bit for bit: the dropped
+    product only adds zeros."""
+    say("quantize keys, float16 sketch flag on / off", x_dtype)
+    G, S = inputs.table_gaussians(D, M)
+    t16 = tq.make_tables(G, S, 2)
+    t32 = tq.make_tables(G, S, 2, sketch_f16=False)
+    assert t16.sketch_f16 == 1 and t32.sketch_f16 == 0
+    w = inputs.WORKLOADS[3]
+    X = inputs.key_slice(w, 1, 2, device="cuda", T=4000).to(x_dtype).reshape(4, 1000, D).contiguous()
+    out = []
+    for tabs in (t16, t32):
+        p = tq.alloc_packed(tq.TQ_KEY, tabs, 4, 1000, "f16")
+        tq.tq_quantize(tabs, X, p)
+        out.append(p)
+    torch.cuda.synchronize()
+    a, b = out
+    for f in ("buf_codes", "buf_signs", "buf_norm", "buf_rnorm"):
+        assert torch.equal(getattr(a, f).view(torch.uint8), getattr(b, f).view(torch.uint8)), f
+
+
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_bf16_values_ragged_blocks(bits):
     w = inputs.WORKLOADS[4]
