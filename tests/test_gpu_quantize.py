@@ -86,9 +86,11 @@ def test_keys_general_sketch(bits):
     S = np.random.default_rng(7).standard_normal((M, D))
     tabs = tq.make_tables(G, S, bits)
     assert tabs.sketch_f16 == 0
+    # 2 x 16000 tokens: 1000 units, so that workgroups of the pipelined kernel
+    # take several units (its loop body, not only its prologue and epilogue)
     w = inputs.WORKLOADS[2]
-    X = inputs.key_slice(w, 0, 1, device="cuda", T=2000).reshape(2, 1000, D).contiguous()
-    p = tq.alloc_packed(tq.TQ_KEY, tabs, 2, 1000, "f16")
+    X = inputs.key_slice(w, 0, 1, device="cuda", T=32000).reshape(2, 16000, D).contiguous()
+    p = tq.alloc_packed(tq.TQ_KEY, tabs, 2, 16000, "f16")
     tq.tq_quantize(tabs, X, p)
     torch.cuda.synchronize()
     Pi = oracle.rotation_from_gaussian(G)
@@ -110,10 +112,10 @@ def test_float16_sketch_flag_gives_the_same_records(x_dtype):
     t32 = tq.make_tables(G, S, 2, sketch_f16=False)
     assert t16.sketch_f16 == 1 and t32.sketch_f16 == 0
     w = inputs.WORKLOADS[3]
-    X = inputs.key_slice(w, 1, 2, device="cuda", T=4000).to(x_dtype).reshape(4, 1000, D).contiguous()
+    X = inputs.key_slice(w, 1, 2, device="cuda", T=40000).to(x_dtype).reshape(4, 10000, D).contiguous()
     out = []
     for tabs in (t16, t32):
-        p = tq.alloc_packed(tq.TQ_KEY, tabs, 4, 1000, "f16")
+        p = tq.alloc_packed(tq.TQ_KEY, tabs, 4, 10000, "f16")
         tq.tq_quantize(tabs, X, p)
         out.append(p)
     torch.cuda.synchronize()
@@ -147,6 +149,25 @@ def test_fp32_values_ragged():
     for bits in (2, 4):
         p = _quantize_values(X, bits, "f32")
         _check_values(X, p, bits, "f32")
+
+
+@pytest.mark.parametrize("role", ["key", "value"])
+def test_fp32_streams_several_units_per_workgroup(role):
+    """fp32 input keeps one unit of input in flight in the pipelined kernels
+    (one register buffer for every unit): streams of more units than
+    workgroups run their loop body, with a ragged last block."""
+    w = inputs.WORKLOADS[1]
+    say("quantize fp32 stream of many units", role)
+    T = 3 * 10000 + 17
+    if role == "key":
+        X = inputs.key_slice(w, 0, 0, device="cuda", T=T).reshape(1, T, D).contiguous()
+        p = _quantize_keys(X, 2, "f32")
+        _check_keys(X, p, 2, "f32")
+    else:
+        X = inputs.value_slice(w, 0, 0, device="cuda", T=T).reshape(1, T, D).contiguous()
+        p = _quantize_values(X, 3, "f32")
+        _check_values(X, p, 3, "f32")
+    assert X.dtype == torch.float32
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
