@@ -151,6 +151,19 @@ def test_fp32_values_ragged():
         _check_values(X, p, bits, "f32")
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_bf16_streams_several_units_per_workgroup(bits):
+    """Keys and values of every width through the pipelined kernels' loop
+    body: 32000 + 9 tokens, about 1000 units, more than the workgroups."""
+    w = inputs.WORKLOADS[4]
+    say("quantize bf16 streams of many units", bits)
+    T = 32009
+    K = inputs.key_slice(w, 0, 2, device="cuda", T=T).reshape(1, T, D).contiguous()
+    _check_keys(K, _quantize_keys(K, bits, "f16"), bits, "f16")
+    V = inputs.value_slice(w, 0, 2, device="cuda", T=T).reshape(1, T, D).contiguous()
+    _check_values(V, _quantize_values(V, bits, "f16"), bits, "f16")
+
+
 @pytest.mark.parametrize("role", ["key", "value"])
 def test_fp32_streams_several_units_per_workgroup(role):
     """fp32 input keeps one unit of input in flight in the pipelined kernels
