@@ -26,7 +26,13 @@
 //    so each lane builds its token's code-plane and sign words itself, one
 //    v_alignbit per bit from float sign bits, and sums its residual squares
 //    for ||r||^2.  The residual (x256, fp16 hi + lo) goes through LDS, one
-//    row per token; the sketch has three products (hi*hi, hi*lo, lo*hi).
+//    row per token; the sketch has three products (hi*hi, hi*lo, lo*hi), or
+//    two (R_hi S + R_lo S) when S is exact in fp16 (the tables' flag).
+//  * kernels: quantize_keys_pipe_kernel and quantize_values_pipe_kernel take
+//    whole streams as software pipelines (the vector work of one unit beside
+//    the matrix work of another); quantize_mfma_kernel takes appends and
+//    split-width value streams unit by unit, with the same arithmetic, so
+//    that appended records equal the bulk ones bit for bit.
 #include <math.h>
 
 #include <type_traits>
@@ -199,7 +205,7 @@ __device__ __forceinline__ uint32_t value_fields(uint32_t r) {
 // [|y| >= t] XNOR [y's sign bit clear]); code_words applies the XOR to
 // whole words.  Each a rt - t is one fma, never -0 or NaN for finite inputs
 // (the exact difference is 0 or far above the smallest denormal), so its
-// sign bit is exactly |y| < t, the compare value_index makes.  Returns the
+// sign bit is exactly |y| < t, the compare the index is defined by.  Returns the
 // signed centroid through C (x's sign, so -0.0 gives -mag).
 template <int BITS>
 __device__ __forceinline__ void quant_append(float x, float rt, const QTab<BITS>& tab, uint32_t* pw, float& C) {
@@ -895,9 +901,10 @@ __device__ __forceinline__ void stage_share_general(const RawX<XT>& raw, _Float1
 // as a software pipeline so that each wave issues matrix-core and vector
 // work of different units side by side.  Iteration i of a workgroup, one
 // barrier at its end:
-//   phase 1: sketch of unit i-1 (24 MFMAs on the residual staged in LDS)
-//            with the quantization of unit i (the vector ALU on the rotation
-//            computed in iteration i-1: plane bits, residual into LDS);
+//   phase 1: sketch of unit i-1 (24 MFMAs on the residual staged in LDS; 16
+//            when S is exact in fp16, SLO = false) with the quantization of
+//            unit i (the vector ALU on the rotation computed in iteration
+//            i-1: plane bits, residual into LDS);
 //   phase 2: rotation of unit i+1 (16 MFMAs on its staged input) with the
 //            sign bits of unit i-1 and the staging of unit i+2 (norm, range
 //            test, float16 copy into LDS).
@@ -1268,10 +1275,14 @@ __global__ __launch_bounds__(kQThreads, 3) void quantize_values_pipe_kernel(
   RawX<XT> rawA, rawB;
   // ---- prologue: stage units 0 and 1, loads of units 2 and 3 in flight,
   // rotation of unit 0
+  auto stage = [&](const RawX<XT>& raw, int slot, int buf) {
+    const bool rare = stage_common(raw, slot, buf);
+    if (__builtin_amdgcn_ballot_w64(rare) != 0) stage_general(raw, slot, buf);
+  };
   load_unit(0, rawA);
   load_unit(1, rawB);
-  if (stage_common(rawA, 0, 0)) stage_general(rawA, 0, 0);
-  if (stage_common(rawB, 1, 1)) stage_general(rawB, 1, 1);
+  stage(rawA, 0, 0);
+  stage(rawB, 1, 1);
   load_unit(2, rawA);
   if constexpr (kTwoSets) load_unit(3, rawB);
   __syncthreads();
