@@ -101,17 +101,22 @@ def test_keys_general_sketch(bits):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("x_dtype", [torch.bfloat16, torch.float32])
-def test_float16_sketch_flag_gives_the_same_records(x_dtype):
+@pytest.mark.parametrize("x_dtype,rotation,hi", [
+    (torch.bfloat16, "dense", 0), (torch.float32, "dense", 0), (torch.bfloat16, "hadamard", 0),
+    (torch.float32, "hadamard", 0), (torch.bfloat16, "dense", D // 2), (torch.float32, "dense", D // 2)])
+def test_float16_sketch_flag_gives_the_same_records(x_dtype, rotation, hi):
     """With a sketch exact in float16, the two-product path (tables flag set)
-    writes the records of the three-product one bit for bit: the dropped
-    product only adds zeros."""
-    say("quantize keys, float16 sketch flag on / off", x_dtype)
+    writes the records of the three-product one bit for bit -- the dropped
+    product only adds zeros -- for every instance of the whole-stream key
+    kernel: both input types, both rotations, uniform and split widths."""
+    say("quantize keys, float16 sketch flag on / off", x_dtype, rotation, hi)
     G, S = inputs.table_gaussians(D, M)
-    t16 = tq.make_tables(G, S, 2)
-    t32 = tq.make_tables(G, S, 2, sketch_f16=False)
+    hs = inputs.hadamard_signs(D) if rotation == "hadamard" else None
+    t16 = tq.make_tables(G, S, 2, hadamard_signs=hs, hi_coords=hi)
+    t32 = tq.make_tables(G, S, 2, hadamard_signs=hs, hi_coords=hi, sketch_f16=False)
     assert t16.sketch_f16 == 1 and t32.sketch_f16 == 0
     w = inputs.WORKLOADS[3]
+    # 4 x 10000 tokens: 1252 units, several per workgroup
     X = inputs.key_slice(w, 1, 2, device="cuda", T=40000).to(x_dtype).reshape(4, 10000, D).contiguous()
     out = []
     for tabs in (t16, t32):
