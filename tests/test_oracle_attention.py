@@ -40,6 +40,32 @@ def test_qjl_estimate_is_unbiased_over_sketch_seeds():
     assert abs(ests.var(ddof=1) - var) < 0.05 * var
 
 
+def test_qjl_estimate_with_float16_sketch_stays_unbiased():
+    # The sketch is held at float16 precision (each Gaussian entry rounded
+    # once): the estimate over sketch draws keeps its mean at <q, k> and its
+    # closed-form variance, as with exact Gaussian rows.
+    d, m, bits = 128, 128, 2
+    Pi, _, c, t = _setup(d, m, bits)
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal(d)
+    k = rng.standard_normal(d) * (1 + 5 * (np.arange(d) % 17 == 0))
+    base = oracle.quantize_values(k[None, :], Pi, c, t)
+    n, idx = base["norm"], base["idx"]
+    ests = []
+    for s in range(6000):
+        S = np.random.default_rng(30_000 + s).standard_normal((m, d)).astype(np.float16).astype(np.float64)
+        r = oracle.residual_and_sketch(base["yhat"], idx, c, S, n)
+        ests.append(oracle.key_logits(q, idx, r["signs"], n, r["rnorm"], Pi, S, c)[0])
+    ests = np.array(ests)
+    true = float(q @ k)
+    sigma = ests.std(ddof=1) / math.sqrt(len(ests))
+    assert abs(ests.mean() - true) < 3 * sigma, (ests.mean(), true, sigma)
+    qr = Pi @ q
+    rr = n[0] * oracle.residual_and_sketch(base["yhat"], idx, c, np.eye(d), n)["rhat"][0]
+    var = ((math.pi / 2) * (qr @ qr) * (rr @ rr) - (qr @ rr) ** 2) / m
+    assert abs(ests.var(ddof=1) - var) < 0.06 * var
+
+
 def test_mse_only_estimate_is_biased_by_one_minus_dD():
     # Negative control: without the sketch, the estimate averaged over Haar
     # rotations shrinks <q,k> by (1 - d D_b) -- the bias the QJL stage removes.
