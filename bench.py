@@ -591,8 +591,10 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16 hi/lo, f32 acc", "data": "synthetic",
         "precision": ("matrix products on fp16 hi/lo operand pairs with fp32 accumulation (fp32-grade "
-                      "rotation, sketch and logits; the sketch matrix is held in fp16, so the sketch "
-                      "takes R_hi S + R_lo S); decode's value contraction takes fp16 weights "
+                      "rotation, sketch and logits" +
+                      ("; the sketch matrix is exact in fp16, so the sketch takes R_hi S + R_lo S"
+                       if tk.sketch_f16 else "") +
+                      "); decode's value contraction takes fp16 weights "
                       "and fp16 centroids; norms and softmax in fp32"),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "d": d,
                    "k_bits": w.k_bits + (0.5 if hi else 0), "qjl_m": m,
